@@ -1,0 +1,46 @@
+"""Helpers shared by the GPU parity tests (inputs, conversions, comparisons)."""
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 image of a device or host tensor."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def bf16_dev(a, device=DEV) -> torch.Tensor:
+    return torch.as_tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).to(device)
+
+
+def randn_bf16(rng: np.random.Generator, shape, std=1.0, device=DEV) -> torch.Tensor:
+    return bf16_dev(rng.standard_normal(shape) * std, device)
+
+
+def rel_l2(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def assert_close(got, ref, rel=1e-2, elem=3e-2, what=""):
+    """rel-L2 <= rel, and every element within elem * (|ref| + rms(ref))."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    r = rel_l2(got, ref)
+    assert r <= rel, f"{what}: rel-L2 {r:.3e} > {rel:.1e}"
+    rms = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
+    bound = elem * (np.abs(ref) + rms)
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements outside bound, worst "
+                           f"{float(np.max(np.abs(got - ref) - bound)):.3e}")
+    return r
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bytes of a tensor for bit-identity checks."""
+    return t.detach().to("cpu").contiguous().view(torch.uint8).numpy()

@@ -1,0 +1,168 @@
+"""The C-ABI library loads, exports every symbol include/h3dit.h declares, and its host
+integer logic equals the oracle's bit for bit.  No device work is launched here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import host
+from tests.conftest import ROOT
+from video_diffusion_transformer_fwd_amd import binding as B
+from video_diffusion_transformer_fwd_amd import synthetic as S
+
+HEADER = os.path.join(ROOT, "include", "h3dit.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from video_diffusion_transformer_fwd_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 25
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for s in syms:
+        assert hasattr(raw, s), f"{s} declared in h3dit.h but not exported"
+    assert set(syms) == set(B.SIGNATURES), "binding signatures out of sync with the header"
+    assert lib.h3_abi_version() == 100
+
+
+def test_align_frames_matches_oracle(lib):
+    for req in range(1, 1200):
+        assert B.h3_align_frames(req) == host.align_frames(req)
+    with pytest.raises(B.H3Error) as e:
+        B.h3_align_frames(0)
+    assert e.value.code == B.H3_EINVAL
+
+
+def test_seconds_and_latent_frames_match_oracle(lib):
+    for s in [0.04, 0.5, 0.917, 1.0, 2.333, 4.458, 10.0, 10.125, 15.083, 15.0]:
+        assert B.h3_frames_for_seconds(s) == host.frames_for_seconds(s)
+    for f in range(1, 400):
+        assert B.h3_latent_frames(f) == host.latent_frames(f)
+    with pytest.raises(B.H3Error):
+        B.h3_frames_for_seconds(-1.0)
+
+
+def test_token_grid_matches_oracle(lib):
+    for w in range(0, 1500, 16):
+        for h in (0, 16, 32, 256, 512, 768, 800, 1344):
+            for ref in (False, True):
+                try:
+                    want = host.token_grid(w, h, ref)
+                except ValueError:
+                    with pytest.raises(B.H3Error):
+                        B.h3_token_grid(w, h, ref)
+                    continue
+                assert B.h3_token_grid(w, h, ref) == want
+
+
+def test_schedule_matches_oracle_bit_exact(lib):
+    for steps in (1, 2, 3, 4, 7, 20, 29, 50):
+        for reuse in (1, 2, 3, 5):
+            sig, fresh, nf = B.h3_schedule(steps, reuse, 1)
+            osig, ofresh = host.schedule(steps, reuse)
+            np.testing.assert_array_equal(sig.view(np.uint32), osig.view(np.uint32))
+            np.testing.assert_array_equal(fresh, ofresh)
+            assert nf == int(ofresh.sum())
+    with pytest.raises(B.H3Error) as e:
+        B.h3_schedule(20, 2, 4)
+    assert e.value.code == B.H3_EINVAL
+    with pytest.raises(B.H3Error) as e:
+        B.h3_schedule(20, 1, 4)
+    assert e.value.code == B.H3_EUNSUPPORTED
+
+
+def test_select_layers_matches_oracle_on_synthetic_tables(lib):
+    for nb, d, seed in [(50, 3072, 0), (2, 512, 0), (50, 512, 3), (7, 64, 1)]:
+        t = S.normal("global.mod_table", (nb, 6, d), 0.02, seed=seed)
+        bits = t.view(torch.int16).numpy().view(np.uint16)
+        vals = t.to(torch.float64).numpy()
+        for L in sorted({2, nb // 2 + 1, max(2, nb - 5), nb}):
+            assert B.h3_select_layers(bits, L) == host.select_layers(vals, L)
+    # ties: identical tables drop the higher index first
+    t = torch.ones((6, 6, 8), dtype=torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    assert B.h3_select_layers(bits, 4) == host.select_layers(t.double().numpy(), 4) == [0, 1, 2, 5]
+
+
+def test_token_plan_matches_oracle(lib):
+    for f, gh, gw in [(2, 8, 8), (6, 16, 16), (1, 15, 27), (3, 2, 5), (61, 24, 42)]:
+        for ev in (0, 9, 10, 17):
+            for na in (4, 20, 30, 45, 50):
+                got = B.h3_token_plan(f, gh, gw, ev, na)
+                want = host.token_plan(f, gh, gw, ev, na)
+                assert got["merge_after"] == want["merge_after"]
+                assert got["restore_before"] == want["restore_before"]
+                assert got["n_reduced"] == want["n_reduced"]
+                np.testing.assert_array_equal(got["pairs"], want["pairs"])
+    with pytest.raises(B.H3Error):
+        B.h3_token_plan(2, 8, 8, 0, 3)
+
+
+def test_geometry_validation(lib):
+    assert B.h3_geom_tokens(B.make_geom(6, 16, 16, 1.0)) == 1536
+    assert B.h3_geom_tokens(B.make_geom(6, 16, 16, 1.0, 1)) == 768
+    assert B.h3_geom_tokens(B.make_geom(61, 24, 42, 1.0)) == 61488
+    assert B.h3_geom_tokens(B.make_geom(1, 15, 27, 1.0, 1)) == 15 * 14
+    for bad in [B.make_geom(0, 8, 8, 1.0), B.make_geom(2, 8, 8, 0.3), B.make_geom(2, 8, 8, 1.0, 2)]:
+        with pytest.raises(B.H3Error):
+            B.h3_geom_tokens(bad)
+
+
+def test_model_create_validates_before_any_launch(lib):
+    dims = B.h3_dims(512, 8, 2048, 32, 128, 2)
+    g = B.h3_global_weights(*[1 + i for i in range(len(B.GLOBAL_FIELDS))])  # never dereferenced
+    blk = B.h3_block_weights(*([64] * 15 + [None, None]))
+    m = B.h3_model_create(dims, g, [blk, blk])
+    assert m.value
+    opts = B.make_opts()
+    # workspace size is host arithmetic; errors come back as codes
+    assert B.h3_workspace_size(m, 128, opts) > 0
+    with pytest.raises(B.H3Error) as e:
+        B.h3_workspace_size(m, 0, opts)
+    assert e.value.code == B.H3_ESHAPE
+    bad_opts = B.make_opts(fc2_mode=7)
+    with pytest.raises(B.H3Error):
+        B.h3_workspace_size(m, 128, bad_opts)
+    B.h3_model_destroy(m)
+    for bad_dims in [B.h3_dims(500, 8, 2048, 32, 128, 2), B.h3_dims(512, 3, 2048, 32, 128, 2),
+                     B.h3_dims(512, 8, 2000, 32, 128, 2), B.h3_dims(512, 2, 2048, 32, 128, 2),
+                     B.h3_dims(512, 8, 2048, 0, 128, 2)]:
+        with pytest.raises(B.H3Error) as e:
+            B.h3_model_create(bad_dims, g, [blk, blk])
+        assert e.value.code == B.H3_ESHAPE
+    blk_null = B.h3_block_weights(*([64] * 14 + [None, None, None]))
+    with pytest.raises(B.H3Error) as e:
+        B.h3_model_create(dims, g, [blk, blk_null])
+    assert e.value.code == B.H3_EINVAL
+
+
+def test_entry_points_reject_bad_arguments_without_launching(lib):
+    # all of these fail validation on the host, before any device call
+    L = B.lib()
+    assert L.h3_euler_step(None, None, 1.0, 0.0, 16, None) == B.H3_EINVAL
+    assert L.h3_gemm_bf16(16, 64, 16, 64, 16, 64, 0, 8, 64, None, None, 0, 0, None) == B.H3_ESHAPE
+    assert L.h3_gemm_bf16(None, 64, 16, 64, 16, 64, 8, 8, 64, None, None, 0, 0, None) == B.H3_EINVAL
+    assert L.h3_gemm_bf16(16, 64, 16, 64, 16, 64, 4, 4, 60, None, None, 0, 0, None) == B.H3_ESHAPE
+    assert L.h3_attention(16, 128, 16, 128, 16, 128, 16, 128, 1, 1, 1, 96, None) == B.H3_EUNSUPPORTED
+    assert L.h3_quant_rows(16, 16, 16, 1, 1000, 1000, None) == B.H3_ESHAPE
+    assert L.h3_gemm_i8(16, 16, 16, 16, 16, 16, 8, 1, 8, 2048, 512, None) == B.H3_EINVAL
+    g = B.make_geom(2, 8, 8, 1.0)
+    assert L.h3_token_reduce(2, ctypes.byref(g), 512, 16, 16, 32, None) == B.H3_EINVAL
+    assert L.h3_token_reduce(0, ctypes.byref(g), 512, 16, None, 16, None) == B.H3_EINVAL
+    assert b"alias" in L.h3_last_error()

@@ -1,0 +1,140 @@
+"""GPU parity of one DiT block (h3_dit_block_fwd) against the oracle, at the small workload's
+shape and at the 512x512x22 shape, for every FC2 mode; fused and unfused gate/AdaLN
+variants bit-identical.
+
+The oracle receives the same seeded inputs (weights, residual x, text context) and the
+modulation it computes itself; the GPU receives that modulation as float32.  Bars: the
+block output and the block delta (out - in) within rel-L2 2e-2 of the oracle, and so are
+the two branch outputs y (attention) and m (MLP) read back from the workspace, because the
+residual would otherwise hide branch errors.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dit
+from tests.gpu_util import DEV, assert_close, bits, f64, rel_l2
+from tests.oracle_model import oracle_model
+from video_diffusion_transformer_fwd_amd import binding as B
+from video_diffusion_transformer_fwd_amd import synthetic as S
+from video_diffusion_transformer_fwd_amd.runtime import DiTModel
+
+pytestmark = pytest.mark.gpu
+
+_MODELS = {}
+
+
+def gpu_model(name, n_blocks=2, fc2_mode="bf16"):
+    key = (name, n_blocks)
+    if key not in _MODELS:
+        w = dataclasses.replace(S.WORKLOADS[name], n_blocks=n_blocks, layers=0, fc2_mode=fc2_mode)
+        _MODELS[key] = (w, DiTModel(w, with_int8=True), oracle_model(w))
+    return _MODELS[key]
+
+
+def ws_view(ws, off, shape, dtype=torch.bfloat16):
+    n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+    return ws[off:off + n].view(dtype).view(*shape)
+
+
+def run_block(model, w, b, x, mod_dev, opts, n1_next=None, mod_next=None):
+    ws = model.workspace(model.geo.n_tokens, opts)
+    B.h3_dit_block_fwd(model.handle, b, model.geo.geom, opts, x, None, n1_next, mod_dev[b],
+                       mod_next, model.ctx_kv[b], ws)
+    torch.cuda.synchronize()
+    return ws
+
+
+@pytest.mark.parametrize("name", ["tiny_256sq_5f", "512sq_22f"])
+@pytest.mark.parametrize("fc2_mode", ["bf16", "row", "grouped"])
+def test_block_parity(name, fc2_mode):
+    w, model, om = gpu_model(name)
+    n, d = model.geo.n_tokens, w.d_model
+    sigma = 0.75
+    mod, fin = dit.modulation(om["global"], sigma)
+    mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
+    coords = dit.rope_coords(model.geo.f_lat, model.geo.grid_h, model.geo.grid_w, model.geo.scale)
+    x0 = S.normal("test.block.x", (n, d), 1.0)
+    opts = B.make_opts(fc2_mode=fc2_mode)
+    for b in range(w.n_blocks):
+        x = x0.to(DEV)
+        ws = run_block(model, w, b, x, mod_dev, opts)
+        lay = B.h3_workspace_layout(model.handle, n, opts)
+        tr = {}
+        ref = dit.block_forward(f64(x0), om["blocks"][b], mod[b], om["ctx"], coords, w.n_heads,
+                                fc2_mode=fc2_mode, trace=tr)
+        got = f64(x)
+        tag = f"{name} {fc2_mode} block {b}"
+        assert_close(got, ref, rel=2e-2, elem=6e-2, what=f"{tag} out")
+        assert rel_l2(got - f64(x0), ref - f64(x0)) < 2e-2, f"{tag} delta"
+        y = f64(ws_view(ws, lay.y, (n, d)))
+        m = f64(ws_view(ws, lay.m, (n, d)))
+        assert rel_l2(y, tr["y"]) < 2e-2, f"{tag} attention branch {rel_l2(y, tr['y'])}"
+        assert rel_l2(m, tr["m"]) < 2e-2, f"{tag} MLP branch {rel_l2(m, tr['m'])}"
+        # q after RMSNorm + RoPE, and the attention outputs, at the same bar
+        qkvq = f64(ws_view(ws, lay.qkvq, (n, 4 * d)))
+        assert rel_l2(qkvq[:, :d], tr["q"].reshape(n, d)) < 2e-2, f"{tag} q"
+        attn = f64(ws_view(ws, lay.attn, (n, 2 * d)))
+        assert rel_l2(attn[:, :d], tr["o"]) < 2e-2, f"{tag} self-attention"
+        assert rel_l2(attn[:, d:], tr["oc"]) < 2e-2, f"{tag} cross-attention"
+
+
+@pytest.mark.parametrize("name", ["tiny_256sq_5f", "512sq_22f"])
+def test_fused_and_unfused_bit_identical(name):
+    w, model, om = gpu_model(name)
+    n, d = model.geo.n_tokens, w.d_model
+    mod, fin = dit.modulation(om["global"], 0.5)
+    mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
+    x0 = S.normal("test.block.x2", (n, d), 1.0).to(DEV)
+    outs = {}
+    for fg, fc in [(1, 1), (0, 0), (1, 0), (0, 1)]:
+        opts = B.make_opts(fused_gate_adaln=fg, fused_cross_block=fc)
+        x = x0.clone()
+        n1n = torch.empty_like(x)
+        ws = run_block(model, w, 0, x, mod_dev, opts, n1n, mod_dev[1])
+        lay = B.h3_workspace_layout(model.handle, n, opts)
+        outs[(fg, fc)] = (x, n1n, ws_view(ws, lay.n2, (n, d)).clone())
+    ref = outs[(1, 1)]
+    for k, v in outs.items():
+        for a, b_, what in zip(v, ref, ("x", "n1_next", "n2")):
+            assert np.array_equal(bits(a), bits(b_)), f"{name} {what} differs for fused={k}"
+    # n1_next is the next block's AdaLN-1 of the output stream
+    want = dit.adaln(f64(ref[0]), mod[1][0], mod[1][1])
+    assert_close(f64(ref[1]), want, rel=1e-2, elem=3e-2, what="n1_next")
+
+
+def test_block_deterministic_run_to_run():
+    w, model, om = gpu_model("512sq_22f")
+    n, d = model.geo.n_tokens, w.d_model
+    mod, _ = dit.modulation(om["global"], 1.0)
+    mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
+    x0 = S.normal("test.block.x3", (n, d), 1.0).to(DEV)
+    res = []
+    for _ in range(2):
+        x = x0.clone()
+        run_block(model, w, 1, x, mod_dev, B.make_opts())
+        res.append(bits(x))
+    assert np.array_equal(res[0], res[1])
+
+
+def test_block_rejects_bad_arguments():
+    w, model, om = gpu_model("tiny_256sq_5f")
+    n, d = model.geo.n_tokens, w.d_model
+    x = torch.zeros((n, d), dtype=torch.bfloat16, device=DEV)
+    mod = torch.zeros((6, d), dtype=torch.float32, device=DEV)
+    opts = B.make_opts()
+    small = torch.empty(1024, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.H3Error) as e:
+        B.h3_dit_block_fwd(model.handle, 0, model.geo.geom, opts, x, None, None, mod, None,
+                           model.ctx_kv[0], small)
+    assert e.value.code == B.H3_EWORKSPACE
+    ws = model.workspace(n, opts)
+    with pytest.raises(B.H3Error) as e:
+        B.h3_dit_block_fwd(model.handle, 5, model.geo.geom, opts, x, None, None, mod, None,
+                           model.ctx_kv[0], ws)
+    assert e.value.code == B.H3_EINVAL
+    with pytest.raises(B.H3Error):
+        B.h3_dit_block_fwd(model.handle, 0, model.geo.geom, opts, x, None, x, mod, None,
+                           model.ctx_kv[0], ws)

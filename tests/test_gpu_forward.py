@@ -1,0 +1,133 @@
+"""GPU parity of the whole fresh evaluation (h3_dit_forward) and of the Euler loop against
+the oracle.
+
+Bars: velocity per evaluation within rel-L2 2e-2; latent after the full step loop within
+rel-L2 5e-2, and so is x_N - x_0 (the part the loop changed).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dit, host
+from tests.gpu_util import DEV, assert_close, bits, f64, rel_l2
+from tests.oracle_model import oracle_model
+from video_diffusion_transformer_fwd_amd import binding as B
+from video_diffusion_transformer_fwd_amd import synthetic as S
+from video_diffusion_transformer_fwd_amd.runtime import DiTModel
+
+pytestmark = pytest.mark.gpu
+
+# A small model with token pairing: 160x128 output -> 4x5 grid (odd width), 2 latent frames,
+# 32 blocks so that the bypass restore lands inside the active list (before position 30 for
+# evaluations past the tenth) as well as before the head.
+TR_SMALL = S.Workload("tr_160x128_5f", 160, 128, 5, 512, 8, 2048, 32, 32, steps=12, reuse=1,
+                      layers=31, token_reduction=True)
+
+
+def loop_parity(w, model, om, opts_kw, steps, reuse, active):
+    geo = model.geo
+    lat0 = model.initial_latent()
+    x = lat0.clone()
+    opts = model.opts(**opts_kw)
+    ev = model.denoise(x, steps, reuse, active, opts)
+    torch.cuda.synchronize()
+    ref, ev_ref = dit.denoise(f64(lat0), om, steps, reuse, active, geo.as_dict(), w.n_heads,
+                              fc2_mode=opts_kw.get("fc2_mode", "bf16"),
+                              token_reduction=opts_kw.get("token_reduction", False))
+    assert ev == ev_ref
+    got = f64(x)
+    assert np.isfinite(got).all()
+    r1 = rel_l2(got, ref)
+    r2 = rel_l2(got - f64(lat0), ref - f64(lat0))
+    assert r1 < 5e-2 and r2 < 5e-2, (r1, r2)
+    return r1, r2
+
+
+def test_tiny_forward_and_loop():
+    w = S.WORKLOADS["tiny_256sq_5f"]
+    model = DiTModel(w)
+    om = oracle_model(w)
+    geo = model.geo
+    assert (geo.f_lat, geo.grid_h, geo.grid_w, geo.scale, geo.n_tokens) == (2, 8, 8, 0.5, 128)
+    lat = model.initial_latent()
+    for sigma, ev in [(1.0, 0), (0.5, 3)]:
+        v = model.forward(lat, sigma, eval_index=ev)
+        torch.cuda.synchronize()
+        ref = dit.dit_forward(f64(lat), om, sigma, [0, 1], geo.as_dict(), w.n_heads)
+        assert_close(f64(v), ref, rel=2e-2, elem=8e-2, what=f"velocity sigma={sigma}")
+    loop_parity(w, model, om, {}, w.steps, w.reuse, [0, 1])
+    # int8 FC2 modes through the whole evaluation
+    model8 = DiTModel(w, with_int8=True)
+    for mode in ("row", "grouped"):
+        v = model8.forward(lat, 1.0, opts=model8.opts(fc2_mode=mode))
+        torch.cuda.synchronize()
+        ref = dit.dit_forward(f64(lat), om, 1.0, [0, 1], geo.as_dict(), w.n_heads, fc2_mode=mode)
+        assert rel_l2(f64(v), ref) < 2e-2
+
+
+def test_token_reduction_forward_and_loop():
+    w = TR_SMALL
+    model = DiTModel(w)
+    om = oracle_model(w)
+    active = model.active()
+    assert active == host.select_layers(om["global"]["mod_table"], w.layers)
+    lat = model.initial_latent()
+    for ev in (0, 10):   # restore before the head / before active position 30
+        v = model.forward(lat, 0.6, active, eval_index=ev)
+        torch.cuda.synchronize()
+        ref = dit.dit_forward(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads,
+                              eval_index=ev, token_reduction=True)
+        assert_close(f64(v), ref, rel=2e-2, elem=8e-2, what=f"token-reduced velocity eval {ev}")
+        ref_full = dit.dit_forward(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads)
+        assert rel_l2(ref, ref_full) > 2 * rel_l2(f64(v), ref), "pairing must change the result"
+    loop_parity(w, model, om, {"token_reduction": True}, w.steps, 1, active)
+    loop_parity(w, model, om, {"token_reduction": True}, 5, 2, active)
+
+
+def test_unfused_forward_bit_identical_to_fused():
+    w = TR_SMALL
+    model = DiTModel(w)
+    lat = model.initial_latent()
+    outs = []
+    for fg, fc in [(1, 1), (0, 0)]:
+        for tr in (False, True):
+            v = model.forward(lat, 0.8, eval_index=0, opts=model.opts(fused_gate_adaln=fg, fused_cross_block=fc,
+                                                                        token_reduction=tr))
+            torch.cuda.synchronize()
+            outs.append(bits(v))
+    assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
+
+
+def test_512sq_loop_reduced_depth():
+    # the 512x512x22 shape with 2 blocks, --steps 4 --reuse 1
+    w = dataclasses.replace(S.WORKLOADS["512sq_22f"], n_blocks=2)
+    model = DiTModel(w)
+    om = oracle_model(w)
+    loop_parity(w, model, om, {}, 4, 1, [0, 1])
+
+
+def test_512sq_full_depth_zero_gates_and_determinism():
+    # all 50 blocks at the full shape, in the launch configuration the benchmark times.
+    # With every gate forced to zero the blocks must leave the residual untouched, so the
+    # velocity is the head of the patch embedding (computed by the oracle at full size).
+    w = S.WORKLOADS["512sq_22f"]
+    model = DiTModel(w)
+    lat = model.initial_latent()
+    v1 = model.forward(lat, 1.0).clone()
+    v2 = model.forward(lat, 1.0).clone()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(v1), bits(v2)), "forward not deterministic"
+    assert np.isfinite(f64(v1)).all()
+    d = w.d_model
+    for r in (2, 5):  # gate rows of the shared projection and of every block's table
+        model.gw["mod_w"][r * d:(r + 1) * d].zero_()
+        model.gw["mod_b"][r * d:(r + 1) * d].zero_()
+        model.gw["mod_table"][:, r].zero_()
+    v0 = model.forward(lat, 1.0)
+    torch.cuda.synchronize()
+    g = {k: f64(model.gw[k].cpu()) for k in model.gw}
+    _, fin = dit.modulation(g, 1.0)
+    ref = dit.final_head(dit.patch_embed(f64(lat), g), g, fin)
+    assert_close(f64(v0), ref, rel=2e-2, elem=8e-2, what="zero-gate velocity")

@@ -1,0 +1,312 @@
+"""GPU parity of every kernel of the path against the oracle, one operation at a time,
+through the C ABI, on seeded inputs.
+
+Tolerances (bf16 outputs): a bf16 store rounds to 2^-9 relative; float32 accumulation
+adds far less.  rel-L2 <= 1e-2 and per-element |err| <= 3e-2 (|ref| + rms(ref)) leave
+room for that rounding while catching any dropped term, wrong index or transposed operand
+(each of which moves rel-L2 to O(1)).  Integer work (int8 codes, int32 sums, the
+dequantised bf16 of identical inputs, token-pair indices) is compared bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dit, host
+from tests.gpu_util import DEV, assert_close, bf16_dev, bits, f64, randn_bf16, rel_l2
+from video_diffusion_transformer_fwd_amd import binding as B
+from video_diffusion_transformer_fwd_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ GEMM
+@pytest.mark.parametrize("M,N,K,epi,f32,two_bias", [
+    (128, 512, 512, 0, 0, 0),
+    (300, 384, 192, 1, 0, 1),       # ragged M, GELU, two biases
+    (1536, 3072, 3072, 0, 0, 0),    # out-projection-sized tile grid
+    (77, 200, 64, 0, 1, 0),         # ragged N, one K slice, float32 out
+    (1, 128, 128, 0, 1, 0),         # single row
+    (129, 12288, 512, 1, 0, 0),     # wide N (FC1 / QKV widths)
+])
+def test_gemm_bf16(M, N, K, epi, f32, two_bias):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    A = randn_bf16(rng, (M, K))
+    W = randn_bf16(rng, (N, K), 0.02)
+    b = randn_bf16(rng, (N,), 0.02)
+    b2 = randn_bf16(rng, (N,), 0.02) if two_bias else None
+    C = torch.empty((M, N), dtype=torch.float32 if f32 else torch.bfloat16, device=DEV)
+    B.h3_gemm_bf16(A, W, C, bias=b, bias2=b2, epilogue=epi)
+    sync()
+    bias = f64(b) + (f64(b2) if two_bias else 0.0)
+    ref = dit.linear(f64(A), f64(W), bias)
+    if epi:
+        ref = dit.gelu(ref)
+    if f32:
+        assert_close(f64(C), ref, rel=2e-5, elem=2e-4, what="gemm f32")
+    else:
+        assert_close(f64(C), ref, rel=6e-3, elem=1.5e-2, what="gemm bf16")
+
+
+def test_gemm_strided_operands():
+    # operands that are column slices of wider rows (as the block's [O | Oc] and qkvq are)
+    rng = np.random.default_rng(5)
+    M, K, N = 200, 256, 320
+    big = randn_bf16(rng, (M, 3 * K))
+    A = big[:, K:2 * K]
+    W = randn_bf16(rng, (N, K), 0.05)
+    out = torch.zeros((M, 2 * N), dtype=torch.bfloat16, device=DEV)
+    B.h3_gemm_bf16(A, W, out[:, N:], M=M, N=N, K=K, lda=3 * K, ldb=K, ldc=2 * N)
+    sync()
+    assert_close(f64(out[:, N:]), dit.linear(f64(A), f64(W)), rel=6e-3, elem=1.5e-2)
+    assert (f64(out[:, :N]) == 0).all()
+
+
+# ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("nq,nk,H,D", [
+    (128, 128, 8, 64),     # the small workload's self-attention
+    (128, 32, 8, 64),      # its cross-attention (32 text tokens)
+    (300, 77, 3, 128),     # ragged queries and keys
+    (1536, 1536, 2, 128),  # 512x512x22 self-attention length, two heads
+    (1536, 256, 2, 128),   # cross-attention length
+    (5, 1, 1, 64),         # one key: output is that value
+    (64, 600, 2, 64),      # keys span several tiles with a ragged tail
+])
+def test_attention(nq, nk, H, D):
+    rng = np.random.default_rng(nq + 13 * nk + H * D)
+    Q, K, V = (randn_bf16(rng, (n, H * D)) for n in (nq, nk, nk))
+    O = torch.empty((nq, H * D), dtype=torch.bfloat16, device=DEV)
+    B.h3_attention(Q, K, V, O, nq, nk, H, D)
+    sync()
+    ref = dit.attention(f64(Q).reshape(nq, H, D), f64(K).reshape(nk, H, D), f64(V).reshape(nk, H, D))
+    assert_close(f64(O), ref.reshape(nq, H * D), rel=1e-2, elem=3e-2, what="attention")
+
+
+def test_attention_strided_views_of_qkvq():
+    # the block's layout: q, k, v, qc as column slices of one [N, 4d] buffer, output into [N, 2d]
+    rng = np.random.default_rng(11)
+    n, H, D = 257, 4, 128
+    d = H * D
+    qkvq = randn_bf16(rng, (n, 4 * d))
+    out = torch.zeros((n, 2 * d), dtype=torch.bfloat16, device=DEV)
+    B.h3_attention(qkvq[:, :d], qkvq[:, d:2 * d], qkvq[:, 2 * d:3 * d], out[:, :d], n, n, H, D)
+    sync()
+    a = f64(qkvq)
+    ref = dit.attention(a[:, :d].reshape(n, H, D), a[:, d:2 * d].reshape(n, H, D), a[:, 2 * d:3 * d].reshape(n, H, D))
+    assert_close(f64(out[:, :d]), ref.reshape(n, d), rel=1e-2, elem=3e-2)
+    assert (f64(out[:, d:]) == 0).all()
+
+
+# ------------------------------------------------------------------ gate + AdaLN
+@pytest.mark.parametrize("rows,d", [(5, 512), (1536, 3072), (130, 5120), (64, 1024)])
+def test_gate_adaln_fused_bit_identical_and_oracle(rows, d):
+    rng = np.random.default_rng(rows + d)
+    x = randn_bf16(rng, (rows, d))
+    y = randn_bf16(rng, (rows, d))
+    gate = torch.tensor(rng.standard_normal(d) * 0.2, dtype=torch.float32, device=DEV)
+    sh = torch.tensor(rng.standard_normal(d) * 0.2, dtype=torch.float32, device=DEV)
+    sc = torch.tensor(rng.standard_normal(d) * 0.2, dtype=torch.float32, device=DEV)
+    # fused
+    xf = x.clone()
+    nf = torch.empty_like(x)
+    B.h3_gate_adaln(xf, y, gate, xf, sh, sc, nf)
+    # unfused: gate, then AdaLN of the stored residual
+    xu = x.clone()
+    nu = torch.empty_like(x)
+    B.h3_gate_adaln(xu, y, gate, xu, None, None, None)
+    B.h3_gate_adaln(xu, None, None, None, sh, sc, nu)
+    sync()
+    assert np.array_equal(bits(xf), bits(xu)), "gated residual differs fused vs unfused"
+    assert np.array_equal(bits(nf), bits(nu)), "AdaLN output differs fused vs unfused"
+    gx = dit.gated_residual(f64(x), f64(gate), f64(y))
+    assert_close(f64(xf), gx, rel=4e-3, elem=1e-2, what="gated residual")
+    assert_close(f64(nf), dit.adaln(gx, f64(sh), f64(sc)), rel=1e-2, elem=3e-2, what="adaln(fused)")
+    # AdaLN alone on the stored input is the oracle's AdaLN of that input
+    n_only = torch.empty_like(x)
+    B.h3_gate_adaln(x, None, None, None, sh, sc, n_only)
+    sync()
+    assert_close(f64(n_only), dit.adaln(f64(x), f64(sh), f64(sc)), rel=6e-3, elem=2e-2, what="adaln")
+
+
+def test_zero_gate_leaves_residual_bit_exact():
+    rng = np.random.default_rng(2)
+    x = randn_bf16(rng, (40, 3072))
+    y = randn_bf16(rng, (40, 3072))
+    z = torch.zeros(3072, dtype=torch.float32, device=DEV)
+    out = torch.empty_like(x)
+    B.h3_gate_adaln(x, y, z, out, None, None, None)
+    sync()
+    assert np.array_equal(bits(out), bits(x))
+
+
+# ------------------------------------------------------------------ Q/K RMSNorm + RoPE
+@pytest.mark.parametrize("geom_args,H,D,qk_norm", [
+    ((2, 8, 8, 0.5, 0), 8, 64, 1),     # small workload: halved RoPE at the 8x8 grid
+    ((6, 16, 16, 1.0, 0), 24, 128, 1), # 512x512x22
+    ((6, 16, 16, 1.0, 1), 4, 128, 1),  # paired tokens
+    ((1, 3, 5, 1.0, 1), 4, 128, 0),    # odd width pairing, no norm
+    ((2, 8, 8, 1.0, 0), 8, 64, 1),     # reference RoPE coordinates
+])
+def test_qk_norm_rope(geom_args, H, D, qk_norm):
+    f, gh, gw, sc, paired = geom_args
+    geom = B.make_geom(f, gh, gw, sc, paired)
+    n = B.h3_geom_tokens(geom)
+    d = H * D
+    rng = np.random.default_rng(n + d)
+    buf = randn_bf16(rng, (n, 4 * d), 2.0)
+    qg = bf16_dev(1 + rng.standard_normal(D) * 0.1)
+    kg = bf16_dev(1 + rng.standard_normal(D) * 0.1)
+    table = torch.empty((n, D // 2, 2), dtype=torch.float32, device=DEV)
+    before = f64(buf)
+    B.h3_rope_table(geom, D, table)
+    B.h3_qk_norm_rope(buf, n, d, D, qg, kg, qk_norm, table)
+    sync()
+    after = f64(buf)
+    pairs = host.token_plan(f, gh, gw, 0, 10)["pairs"] if paired else None
+    coords = dit.rope_coords(f, gh, gw, sc, pairs)
+    q = before[:, :d].reshape(n, H, D)
+    k = before[:, d:2 * d].reshape(n, H, D)
+    if qk_norm:
+        q, k = dit.rms_norm_heads(q, f64(qg)), dit.rms_norm_heads(k, f64(kg))
+    assert_close(after[:, :d], dit.rope_apply(q, coords).reshape(n, d), rel=6e-3, elem=2e-2, what="q")
+    assert_close(after[:, d:2 * d], dit.rope_apply(k, coords).reshape(n, d), rel=6e-3, elem=2e-2, what="k")
+    assert np.array_equal(after[:, 2 * d:], before[:, 2 * d:]), "v / qc must be untouched"
+
+
+# ------------------------------------------------------------------ token pairing
+@pytest.mark.parametrize("f,gh,gw,d", [(6, 16, 16, 3072), (1, 15, 27, 512), (2, 3, 5, 1024)])
+def test_token_merge_restore_exact(f, gh, gw, d):
+    geom = B.make_geom(f, gh, gw, 1.0, 0)
+    n = f * gh * gw
+    plan = host.token_plan(f, gh, gw, 0, 10)
+    rng = np.random.default_rng(n)
+    # values k/64 with |k| < 128: every pair mean is exactly representable in bf16, so the merge
+    # must equal the oracle bit for bit and a wrong pair index shows as a mismatch
+    S_np = rng.integers(-127, 128, size=(n, d)) / 64.0
+    Sx = bf16_dev(S_np)
+    xr = torch.empty((plan["n_reduced"], d), dtype=torch.bfloat16, device=DEV)
+    B.h3_token_reduce(0, geom, d, Sx, None, xr)
+    sync()
+    assert np.array_equal(f64(xr), dit.token_merge(S_np, plan["pairs"]))
+    # merge then restore with nothing between returns S bit for bit
+    out = torch.empty_like(Sx)
+    B.h3_token_reduce(1, geom, d, xr, Sx, out)
+    sync()
+    assert np.array_equal(bits(out), bits(Sx))
+    # a changed reduced stream moves both pair members by the change (in place on the bypass)
+    delta = rng.integers(-8, 9, size=xr.shape) / 64.0
+    xr2 = bf16_dev(f64(xr) + delta)
+    S2 = Sx.clone()
+    B.h3_token_reduce(1, geom, d, xr2, S2, S2)
+    sync()
+    want = dit.f32_to_bf16(dit.token_restore(S_np, f64(xr2), plan["pairs"]).astype(np.float32))
+    assert np.array_equal(f64(S2), want.astype(np.float64))
+
+
+# ------------------------------------------------------------------ int8 FC2
+@pytest.mark.parametrize("rows,K,group", [(300, 2048, 2048), (300, 2048, 1024), (1536, 12288, 12288),
+                                          (64, 20480, 1024)])
+def test_quant_rows_bit_exact(rows, K, group):
+    rng = np.random.default_rng(rows + K + group)
+    X = randn_bf16(rng, (rows, K), 0.7)
+    X[3] = 0            # zero row -> s = 0, q = 0
+    X[4, :7] = 50.0     # an outlier row
+    Q = torch.empty((rows, K), dtype=torch.int8, device=DEV)
+    Sc = torch.empty((rows, K // group), dtype=torch.float32, device=DEV)
+    B.h3_quant_rows(X, Q, Sc, group)
+    sync()
+    q_ref, s_ref = dit.quantize_rows(f64(X).astype(np.float32), None if group == K else group)
+    assert np.array_equal(Q.cpu().numpy(), q_ref)
+    assert np.array_equal(Sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K,group", [(300, 256, 2048, 2048), (300, 256, 2048, 1024),
+                                         (1536, 3072, 12288, 12288), (130, 640, 4096, 1024)])
+def test_gemm_i8_bit_exact(M, N, K, group):
+    rng = np.random.default_rng(M + N + K + group)
+    qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    sa = (rng.random((M, K // group)) * 0.01).astype(np.float32)
+    sw = (rng.random(N) * 0.001).astype(np.float32)
+    bias = bf16_dev(rng.standard_normal(N) * 0.02)
+    Cm = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    B.h3_gemm_i8(torch.from_numpy(qa).to(DEV), torch.from_numpy(sa).to(DEV), torch.from_numpy(qw).to(DEV),
+                 torch.from_numpy(sw).to(DEV), bias, Cm, group)
+    sync()
+    acc = dit.int8_accumulate(qa, qw, None if group == K else group)
+    ref = dit.f32_to_bf16(dit.dequant(acc, sa, sw, f64(bias).astype(np.float32)))
+    got = Cm.cpu().to(torch.float32).numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_int8_fc2_pipeline_bit_exact_on_seeded_input():
+    # the same bf16 FC2 input through both quantisers and both int8 products
+    w = S.WORKLOADS["tiny_256sq_5f"]
+    blk = S.block_weights(w, 0)
+    rng = np.random.default_rng(9)
+    h = randn_bf16(rng, (128, w.ffn_dim), 0.5)
+    W2 = blk["fc2_w"].to(DEV)
+    b2 = blk["fc2_b"].to(DEV)
+    for mode, group in (("row", w.ffn_dim), ("grouped", 1024)):
+        qw = torch.empty((w.d_model, w.ffn_dim), dtype=torch.int8, device=DEV)
+        sw = torch.empty((w.d_model, 1), dtype=torch.float32, device=DEV)
+        B.h3_quant_rows(W2, qw, sw, w.ffn_dim)
+        qa = torch.empty((128, w.ffn_dim), dtype=torch.int8, device=DEV)
+        sa = torch.empty((128, w.ffn_dim // group), dtype=torch.float32, device=DEV)
+        B.h3_quant_rows(h, qa, sa, group)
+        out = torch.empty((128, w.d_model), dtype=torch.bfloat16, device=DEV)
+        B.h3_gemm_i8(qa, sa, qw, sw, b2, out, group)
+        sync()
+        qw_ref, sw_ref = dit.quantize_weight(f64(W2).astype(np.float32))
+        assert np.array_equal(qw.cpu().numpy(), qw_ref)
+        g = None if mode == "row" else 1024
+        qa_ref, sa_ref = dit.quantize_rows(f64(h).astype(np.float32), g)
+        assert np.array_equal(qa.cpu().numpy(), qa_ref)
+        acc = dit.int8_accumulate(qa_ref, qw_ref, g)
+        ref = dit.f32_to_bf16(dit.dequant(acc, sa_ref, sw_ref[:, 0], f64(b2).astype(np.float32)))
+        assert np.array_equal(out.cpu().to(torch.float32).numpy().view(np.uint32), ref.view(np.uint32))
+        # and the int8 product stays close to the float64 bf16 product
+        ref_f = dit.linear(f64(h), f64(W2), f64(b2))
+        assert rel_l2(f64(out), ref_f) < 2e-2
+
+
+# ------------------------------------------------------------------ Euler
+def test_euler_step():
+    rng = np.random.default_rng(4)
+    n = 1536 * 128 + 3  # ragged tail after the 4-wide vectors
+    x = torch.tensor(rng.standard_normal(n), dtype=torch.float32, device=DEV)
+    v = torch.tensor(rng.standard_normal(n), dtype=torch.float32, device=DEV)
+    x0 = f64(x)
+    sig, _ = host.schedule(4)
+    B.h3_euler_step(x, v, float(sig[1]), float(sig[2]))
+    sync()
+    ref = dit.euler_step(x0, f64(v), sig[1], sig[2])
+    assert np.max(np.abs(f64(x) - ref)) <= 1e-6 * (1 + np.max(np.abs(ref)))
+
+
+# ------------------------------------------------------------------ modulation
+def test_modulation_matches_oracle():
+    w = S.WORKLOADS["tiny_256sq_5f"]
+    g = S.global_weights(w)
+    gd = {k: v.to(DEV) for k, v in g.items()}
+    dims = B.h3_dims(w.d_model, w.n_heads, w.ffn_dim, w.ctx_len, w.latent_ch, w.n_blocks)
+    gs = B.h3_global_weights(*[gd[n].data_ptr() for n in B.GLOBAL_FIELDS])
+    dummy = torch.zeros(w.ffn_dim * w.d_model, dtype=torch.bfloat16, device=DEV)
+    blk = B.h3_block_weights(*([dummy.data_ptr()] * 15 + [None, None]))
+    m = B.h3_model_create(dims, gs, [blk] * w.n_blocks)
+    try:
+        ws = torch.empty(B.h3_workspace_size(m, 1, B.make_opts()), dtype=torch.uint8, device=DEV)
+        mod = torch.empty((w.n_blocks, 6, w.d_model), dtype=torch.float32, device=DEV)
+        fin = torch.empty((2, w.d_model), dtype=torch.float32, device=DEV)
+        g64 = {k: f64(v) for k, v in g.items()}
+        for sigma in (1.0, 0.75, 0.25, 0.0):
+            B.h3_modulation(m, sigma, mod, fin, ws)
+            sync()
+            mod_ref, fin_ref = dit.modulation(g64, sigma)
+            assert_close(f64(mod), mod_ref, rel=1e-4, elem=1e-3, what=f"mod sigma={sigma}")
+            assert_close(f64(fin), fin_ref, rel=1e-4, elem=1e-3, what=f"fin sigma={sigma}")
+    finally:
+        B.h3_model_destroy(m)

@@ -1,0 +1,335 @@
+"""ctypes binding of libh3dit.so: the C ABI of include/h3dit.h under the same names.
+
+Argument marshalling only: tensors become raw device pointers, host arrays become ctypes
+buffers, error codes become ``H3Error``.  Loading fails loudly when the library has not
+been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libh3dit.so")
+
+H3_OK, H3_EINVAL, H3_ESHAPE, H3_EUNSUPPORTED, H3_EWORKSPACE, H3_EHIP = 0, -1, -2, -3, -4, -5
+H3_FC2_BF16, H3_FC2_INT8_ROW, H3_FC2_INT8_GROUPED = 0, 1, 2
+FC2_MODES = {"bf16": H3_FC2_BF16, "row": H3_FC2_INT8_ROW, "grouped": H3_FC2_INT8_GROUPED}
+H3_EPI_NONE, H3_EPI_GELU = 0, 1
+
+
+class H3Error(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"h3 error {code}: {msg}")
+        self.code = code
+
+
+class h3_dims(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in
+                ("d_model", "n_heads", "ffn_dim", "ctx_len", "latent_ch", "n_blocks")]
+
+
+GLOBAL_FIELDS = ("t1_w", "t1_b", "t2_w", "t2_b", "mod_w", "mod_b", "fin_w", "fin_b", "fin_t",
+                 "mod_table", "patch_w", "patch_b", "head_w", "head_b")
+BLOCK_FIELDS = ("qkvq_w", "qkvq_b", "kc_w", "kc_b", "vc_w", "vc_b", "out_w", "out_b", "outc_b",
+                "q_gamma", "k_gamma", "fc1_w", "fc1_b", "fc2_w", "fc2_b", "fc2_q", "fc2_s")
+
+
+class h3_global_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in GLOBAL_FIELDS]
+
+
+class h3_block_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in BLOCK_FIELDS]
+
+
+class h3_geom(C.Structure):
+    _fields_ = [("f_lat", C.c_int32), ("grid_h", C.c_int32), ("grid_w", C.c_int32),
+                ("rope_spatial_scale", C.c_float), ("paired", C.c_int32)]
+
+
+class h3_run_opts(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in
+                ("fc2_mode", "fused_gate_adaln", "fused_cross_block", "qk_norm", "token_reduction")]
+
+
+class h3_ws_layout(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in
+                ("n1", "qkvq", "attn", "y", "n2", "h", "m", "hq", "hs", "rope", "total")]
+
+
+_VP, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+_PI32, _PF, _PU8, _PU16 = C.POINTER(C.c_int32), C.POINTER(C.c_float), C.POINTER(C.c_uint8), C.POINTER(C.c_uint16)
+
+# name -> (restype, argtypes); every symbol declared in include/h3dit.h
+SIGNATURES = {
+    "h3_last_error": (C.c_char_p, []),
+    "h3_abi_version": (_I32, []),
+    "h3_align_frames": (_I32, [_I32, _PI32]),
+    "h3_frames_for_seconds": (_I32, [C.c_double, _PI32]),
+    "h3_latent_frames": (_I32, [_I32, _PI32]),
+    "h3_token_grid": (_I32, [_I32, _I32, _I32, _PI32, _PI32, _PF]),
+    "h3_schedule": (_I32, [_I32, _I32, _I32, _PF, _PU8, _PI32]),
+    "h3_select_layers": (_I32, [_PU16, _I32, _I32, _I32, _PI32]),
+    "h3_token_plan": (_I32, [_I32, _I32, _I32, _I32, _I32, _PI32, _PI32, _PI32, _PI32]),
+    "h3_model_create": (_I32, [C.POINTER(h3_dims), C.POINTER(h3_global_weights),
+                               C.POINTER(h3_block_weights), _I32, C.POINTER(_VP)]),
+    "h3_model_destroy": (None, [_VP]),
+    "h3_geom_tokens": (_I32, [C.POINTER(h3_geom), _PI32]),
+    "h3_workspace_size": (_I32, [_VP, _I32, C.POINTER(h3_run_opts), C.POINTER(_SZ)]),
+    "h3_workspace_layout": (_I32, [_VP, _I32, C.POINTER(h3_run_opts), C.POINTER(h3_ws_layout)]),
+    "h3_prepare_context": (_I32, [_VP, _VP, _VP, _VP]),
+    "h3_quantize_fc2_weights": (_I32, [_VP, _VP]),
+    "h3_modulation": (_I32, [_VP, _F, _VP, _VP, _VP, _SZ, _VP]),
+    "h3_dit_block_fwd": (_I32, [_VP, _I32, C.POINTER(h3_geom), C.POINTER(h3_run_opts), _VP, _VP,
+                                _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "h3_dit_forward": (_I32, [_VP, C.POINTER(h3_geom), C.POINTER(h3_run_opts), _VP, _F, _PI32,
+                              _I32, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "h3_euler_step": (_I32, [_VP, _VP, _F, _F, _I64, _VP]),
+    "h3_token_reduce": (_I32, [_I32, C.POINTER(h3_geom), _I32, _VP, _VP, _VP, _VP]),
+    "h3_gemm_bf16": (_I32, [_VP, _I64, _VP, _I64, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _I32,
+                            _I32, _VP]),
+    "h3_attention": (_I32, [_VP, _I64, _VP, _I64, _VP, _I64, _VP, _I64, _I32, _I32, _I32, _I32,
+                            _VP]),
+    "h3_quant_rows": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
+    "h3_gemm_i8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _VP]),
+    "h3_gate_adaln": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
+    "h3_rope_table": (_I32, [C.POINTER(h3_geom), _I32, _VP, _VP]),
+    "h3_qk_norm_rope": (_I32, [_VP, _I64, _I32, _I32, _I32, _VP, _VP, _I32, _VP, _VP]),
+    "h3_profile_begin": (_I32, [C.c_uint32, _I32]),
+    "h3_profile_end": (_I32, [C.POINTER(C.c_double), _PI32]),
+}
+
+STAGES = ("modulation", "patch", "adaln", "qkv_gemm", "qk_norm_rope", "self_attn", "cross_attn",
+          "out_gemm", "gate_adaln", "fc1_gemm", "fc2_gemm", "fc2_quant", "fc2_i8_gemm",
+          "token_reduce", "head", "euler")
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m video_diffusion_transformer_fwd_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(code):
+    if code != H3_OK:
+        raise H3Error(code, lib().h3_last_error().decode())
+
+
+def ptr(t):
+    """Raw pointer of a tensor (or None)."""
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def stream_handle(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+# ------------------------------------------------------------------ host integer logic
+def h3_align_frames(requested: int) -> int:
+    out = C.c_int32()
+    _check(lib().h3_align_frames(requested, C.byref(out)))
+    return out.value
+
+
+def h3_frames_for_seconds(seconds: float) -> int:
+    out = C.c_int32()
+    _check(lib().h3_frames_for_seconds(seconds, C.byref(out)))
+    return out.value
+
+
+def h3_latent_frames(frames: int) -> int:
+    out = C.c_int32()
+    _check(lib().h3_latent_frames(frames, C.byref(out)))
+    return out.value
+
+
+def h3_token_grid(width: int, height: int, reference_rope: bool = False):
+    gh, gw, sc = C.c_int32(), C.c_int32(), C.c_float()
+    _check(lib().h3_token_grid(width, height, int(reference_rope), C.byref(gh), C.byref(gw), C.byref(sc)))
+    return gh.value, gw.value, sc.value
+
+
+def h3_schedule(steps: int, reuse: int = 1, core_reuse: int = 1):
+    sig = np.zeros(max(steps, 0) + 1, dtype=np.float32)
+    fresh = np.zeros(max(steps, 1), dtype=np.uint8)
+    nf = C.c_int32()
+    _check(lib().h3_schedule(steps, reuse, core_reuse, sig.ctypes.data_as(_PF),
+                             fresh.ctypes.data_as(_PU8), C.byref(nf)))
+    return sig, fresh[:steps], nf.value
+
+
+def h3_select_layers(mod_table_bf16_bits: np.ndarray, n_active: int):
+    t = np.ascontiguousarray(mod_table_bf16_bits, dtype=np.uint16)
+    nb, six, d = t.shape
+    out = np.zeros(n_active, dtype=np.int32)
+    _check(lib().h3_select_layers(t.ctypes.data_as(_PU16), nb, d, n_active, out.ctypes.data_as(_PI32)))
+    return [int(v) for v in out]
+
+
+def h3_token_plan(f_lat, grid_h, grid_w, eval_index, n_active, with_pairs=True):
+    ma, rb, nr = C.c_int32(), C.c_int32(), C.c_int32()
+    _check(lib().h3_token_plan(f_lat, grid_h, grid_w, eval_index, n_active, C.byref(ma),
+                               C.byref(rb), None, C.byref(nr)))
+    pairs = None
+    if with_pairs:
+        buf = np.zeros(2 * nr.value, dtype=np.int32)
+        _check(lib().h3_token_plan(f_lat, grid_h, grid_w, eval_index, n_active, C.byref(ma),
+                                   C.byref(rb), buf.ctypes.data_as(_PI32), C.byref(nr)))
+        pairs = buf.reshape(-1, 2)
+    return dict(merge_after=ma.value, restore_before=rb.value, pairs=pairs, n_reduced=nr.value)
+
+
+def make_geom(f_lat, grid_h, grid_w, scale, paired=0):
+    return h3_geom(f_lat, grid_h, grid_w, scale, paired)
+
+
+def h3_geom_tokens(geom: h3_geom) -> int:
+    n = C.c_int32()
+    _check(lib().h3_geom_tokens(C.byref(geom), C.byref(n)))
+    return n.value
+
+
+def make_opts(fc2_mode="bf16", fused_gate_adaln=True, fused_cross_block=True, qk_norm=True,
+              token_reduction=False):
+    return h3_run_opts(FC2_MODES[fc2_mode] if isinstance(fc2_mode, str) else fc2_mode,
+                       int(fused_gate_adaln), int(fused_cross_block), int(qk_norm),
+                       int(token_reduction))
+
+
+# ------------------------------------------------------------------ model
+def h3_model_create(dims: h3_dims, g: h3_global_weights, blocks) -> C.c_void_p:
+    arr = (h3_block_weights * len(blocks))(*blocks)
+    out = C.c_void_p()
+    _check(lib().h3_model_create(C.byref(dims), C.byref(g), arr, len(blocks), C.byref(out)))
+    return out
+
+
+def h3_model_destroy(m):
+    lib().h3_model_destroy(m)
+
+
+def h3_workspace_size(m, n_tokens, opts) -> int:
+    out = C.c_size_t()
+    _check(lib().h3_workspace_size(m, n_tokens, C.byref(opts), C.byref(out)))
+    return out.value
+
+
+def h3_workspace_layout(m, n_tokens, opts) -> h3_ws_layout:
+    out = h3_ws_layout()
+    _check(lib().h3_workspace_layout(m, n_tokens, C.byref(opts), C.byref(out)))
+    return out
+
+
+def h3_prepare_context(m, ctx, ctx_kv, stream=None):
+    _check(lib().h3_prepare_context(m, ptr(ctx), ptr(ctx_kv), stream_handle(stream)))
+
+
+def h3_quantize_fc2_weights(m, stream=None):
+    _check(lib().h3_quantize_fc2_weights(m, stream_handle(stream)))
+
+
+def h3_modulation(m, sigma, mod, mod_final, ws, stream=None):
+    _check(lib().h3_modulation(m, sigma, ptr(mod), ptr(mod_final), ptr(ws), ws.numel() * ws.element_size(),
+                               stream_handle(stream)))
+
+
+def h3_dit_block_fwd(m, block, geom, opts, x, n1_in, n1_next, mod, mod_next, ctx_kv, ws, stream=None):
+    _check(lib().h3_dit_block_fwd(m, block, C.byref(geom), C.byref(opts), ptr(x), ptr(n1_in),
+                                  ptr(n1_next), ptr(mod), ptr(mod_next), ptr(ctx_kv), ptr(ws),
+                                  ws.numel() * ws.element_size(), stream_handle(stream)))
+
+
+def h3_dit_forward(m, geom, opts, latent, sigma, active, eval_index, ctx_kv, velocity, ws, stream=None):
+    act = np.ascontiguousarray(active, dtype=np.int32)
+    _check(lib().h3_dit_forward(m, C.byref(geom), C.byref(opts), ptr(latent), sigma,
+                                act.ctypes.data_as(_PI32), len(act), eval_index, ptr(ctx_kv),
+                                ptr(velocity), ptr(ws), ws.numel() * ws.element_size(),
+                                stream_handle(stream)))
+
+
+def h3_euler_step(latent, velocity, sigma_cur, sigma_next, stream=None):
+    _check(lib().h3_euler_step(ptr(latent), ptr(velocity), sigma_cur, sigma_next, latent.numel(),
+                               stream_handle(stream)))
+
+
+def h3_token_reduce(direction, geom, d_model, src, bypass, dst, stream=None):
+    _check(lib().h3_token_reduce(direction, C.byref(geom), d_model, ptr(src), ptr(bypass), ptr(dst),
+                                 stream_handle(stream)))
+
+
+# ------------------------------------------------------------------ single operations
+def h3_gemm_bf16(A, B, C_out, bias=None, bias2=None, epilogue=H3_EPI_NONE, lda=None, ldb=None,
+                 ldc=None, M=None, N=None, K=None, stream=None):
+    M = M if M is not None else A.shape[0]
+    K = K if K is not None else A.shape[1]
+    N = N if N is not None else B.shape[0]
+    out_f32 = 1 if C_out.dtype.itemsize == 4 else 0
+    _check(lib().h3_gemm_bf16(ptr(A), lda or A.stride(0), ptr(B), ldb or B.stride(0), ptr(C_out),
+                              ldc or C_out.stride(0), M, N, K, ptr(bias), ptr(bias2), epilogue,
+                              out_f32, stream_handle(stream)))
+
+
+def h3_attention(Q, K, V, O, n_q, n_k, n_heads, head_dim, stream=None):
+    _check(lib().h3_attention(ptr(Q), Q.stride(0), ptr(K), K.stride(0), ptr(V), V.stride(0), ptr(O),
+                              O.stride(0), n_q, n_k, n_heads, head_dim, stream_handle(stream)))
+
+
+def h3_quant_rows(X, Q, S, group, stream=None):
+    rows, K = X.shape
+    _check(lib().h3_quant_rows(ptr(X), ptr(Q), ptr(S), rows, K, group, stream_handle(stream)))
+
+
+def h3_gemm_i8(QA, SA, QW, SW, bias, C_out, group, stream=None):
+    M, K = QA.shape
+    N = QW.shape[0]
+    _check(lib().h3_gemm_i8(ptr(QA), ptr(SA), ptr(QW), ptr(SW), ptr(bias), ptr(C_out),
+                            C_out.stride(0), M, N, K, group, stream_handle(stream)))
+
+
+def h3_gate_adaln(x, y, gate, x_out, shift, scale, n_out, stream=None):
+    rows, d = x.shape
+    _check(lib().h3_gate_adaln(ptr(x), ptr(y), ptr(gate), ptr(x_out), ptr(shift), ptr(scale),
+                               ptr(n_out), rows, d, stream_handle(stream)))
+
+
+def h3_rope_table(geom, head_dim, table, stream=None):
+    _check(lib().h3_rope_table(C.byref(geom), head_dim, ptr(table), stream_handle(stream)))
+
+
+def h3_qk_norm_rope(qkvq, n_tokens, d_model, head_dim, q_gamma, k_gamma, qk_norm, table,
+                    stream=None):
+    _check(lib().h3_qk_norm_rope(ptr(qkvq), qkvq.stride(0), n_tokens, d_model, head_dim,
+                                 ptr(q_gamma), ptr(k_gamma), int(qk_norm), ptr(table),
+                                 stream_handle(stream)))
+
+
+def h3_profile_begin(stages, max_launches=100000):
+    mask = 0
+    for st in stages:
+        mask |= 1 << STAGES.index(st)
+    _check(lib().h3_profile_begin(mask, max_launches))
+
+
+def h3_profile_end():
+    """{stage: (total_ms, launches)} for the stages that were timed."""
+    ms = (C.c_double * len(STAGES))()
+    cnt = (C.c_int32 * len(STAGES))()
+    _check(lib().h3_profile_end(ms, cnt))
+    return {st: (ms[i], cnt[i]) for i, st in enumerate(STAGES) if cnt[i]}

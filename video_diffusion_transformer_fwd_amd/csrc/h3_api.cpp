@@ -1,0 +1,602 @@
+// C ABI entry points: model handle, workspace plan, block / forward orchestration, and the
+// single-operation entry points.  Every argument is validated before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "h3_internal.h"
+
+struct h3_model : h3::Model {};
+
+namespace h3 {
+namespace {
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool supported_width(int d) {
+  const int v = d / 512;
+  return d % 512 == 0 && (v == 1 || v == 2 || v == 3 || v == 4 || v == 5 || v == 6 || v == 8 ||
+                          v == 10 || v == 12 || v == 16);
+}
+
+int32_t check_opts(const h3_run_opts *o) {
+  if (!o) return fail(H3_EINVAL, "run options are NULL");
+  if (o->fc2_mode < H3_FC2_BF16 || o->fc2_mode > H3_FC2_INT8_GROUPED)
+    return fail(H3_EINVAL, "fc2_mode must be 0, 1 or 2");
+  return H3_OK;
+}
+
+size_t bytes_bf16(int64_t n) { return static_cast<size_t>(n) * 2; }
+
+}  // namespace
+
+WsPlan plan_workspace(const Model &m, int32_t n, const h3_run_opts &o) {
+  const int64_t d = m.dims.d_model, F = m.dims.ffn_dim, C = m.dims.latent_ch;
+  const int64_t nb = m.dims.n_blocks, half = m.head_dim / 2;
+  WsPlan p{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + align_up(bytes));
+    return at;
+  };
+  p.n1 = take(bytes_bf16(n * d));
+  p.qkvq = take(bytes_bf16(n * 4 * d));
+  p.attn = take(bytes_bf16(n * 2 * d));
+  p.y = take(bytes_bf16(n * d));
+  p.n2 = take(bytes_bf16(n * d));
+  p.h = take(bytes_bf16(n * F));
+  p.m = take(bytes_bf16(n * d));
+  const bool i8 = o.fc2_mode != H3_FC2_BF16;
+  p.hq = take(i8 ? static_cast<size_t>(n * F) : 0);
+  p.hs = take(i8 ? static_cast<size_t>(n * (F / 1024)) * sizeof(float) : 0);
+  p.rope = take(static_cast<size_t>(n * half) * sizeof(float2));
+  // forward / modulation
+  p.mod = take(static_cast<size_t>(nb * 6 * d) * sizeof(float));
+  p.fin = take(static_cast<size_t>(2 * d) * sizeof(float));
+  p.tmp = take(static_cast<size_t>(256 + 2 * d + 6 * d) * sizeof(float));
+  p.x = take(bytes_bf16(n * d));
+  p.xr = take(bytes_bf16(n * d));
+  p.n1b = take(bytes_bf16(n * d));
+  p.lat16 = take(bytes_bf16(n * C));
+  p.rope_r = take(static_cast<size_t>(n * half) * sizeof(float2));
+  p.total = off;
+  return p;
+}
+
+}  // namespace h3
+
+using namespace h3;
+
+namespace {
+
+int32_t validate_model(const h3_model *m) {
+  if (!m) return fail(H3_EINVAL, "model is NULL");
+  return H3_OK;
+}
+
+// Launches the block on validated arguments.  rows = tokens of this geometry.
+int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t rows,
+                  const h3_run_opts &o, bf16_t *x, const bf16_t *n1_in, bf16_t *n1_next,
+                  const float *mod, const float *mod_next, const bf16_t *ctx_kv, char *ws,
+                  const WsPlan &p, hipStream_t s, const float2 *rope_table) {
+  const int d = m->dims.d_model, F = m->dims.ffn_dim, H = m->dims.n_heads, D = m->head_dim;
+  const int L = m->dims.ctx_len;
+  const h3_block_weights &w = m->blocks[b];
+  bf16_t *n1 = reinterpret_cast<bf16_t *>(ws + p.n1);
+  bf16_t *qkvq = reinterpret_cast<bf16_t *>(ws + p.qkvq);
+  bf16_t *attn = reinterpret_cast<bf16_t *>(ws + p.attn);
+  bf16_t *y = reinterpret_cast<bf16_t *>(ws + p.y);
+  bf16_t *n2 = reinterpret_cast<bf16_t *>(ws + p.n2);
+  bf16_t *h = reinterpret_cast<bf16_t *>(ws + p.h);
+  bf16_t *mo = reinterpret_cast<bf16_t *>(ws + p.m);
+  const float *sh1 = mod, *sc1 = mod + d, *g1 = mod + 2 * d;
+  const float *sh2 = mod + 3 * d, *sc2 = mod + 4 * d, *g2 = mod + 5 * d;
+
+  // AdaLN-1 (unless the caller already has it, e.g. from the previous block's fused gate)
+  if (!n1_in) {
+    ProfScope ps(H3_ST_ADALN, s);
+    launch_gate_adaln(x, nullptr, nullptr, nullptr, sh1, sc1, n1, rows, d, s);
+    n1_in = n1;
+  }
+  // [q | k | v | qc] = n1 W_qkvq^T + b
+  {
+    ProfScope ps(H3_ST_QKV_GEMM, s);
+    launch_gemm_bf16(n1_in, d, reinterpret_cast<const bf16_t *>(w.qkvq_w), d, qkvq, 4 * d, rows,
+                     4 * d, d, reinterpret_cast<const bf16_t *>(w.qkvq_b), nullptr, H3_EPI_NONE,
+                     0, s);
+  }
+  // Q/K RMSNorm + 3D RoPE, in place
+  {
+    ProfScope ps(H3_ST_QK_NORM_ROPE, s);
+    launch_qk_norm_rope(qkvq, 4 * d, rows, d, D, reinterpret_cast<const bf16_t *>(w.q_gamma),
+                        reinterpret_cast<const bf16_t *>(w.k_gamma), o.qk_norm, rope_table, s);
+  }
+  // self-attention -> attn[:, 0:d]; cross-attention -> attn[:, d:2d]
+  {
+    ProfScope ps(H3_ST_SELF_ATTN, s);
+    launch_attention(qkvq, 4 * d, qkvq + d, 4 * d, qkvq + 2 * d, 4 * d, attn, 2 * d, rows, rows,
+                     H, D, s);
+  }
+  {
+    ProfScope ps(H3_ST_CROSS_ATTN, s);
+    launch_attention(qkvq + 3 * d, 4 * d, ctx_kv, d, ctx_kv + static_cast<size_t>(L) * d, d,
+                     attn + d, 2 * d, rows, L, H, D, s);
+  }
+  // y = [O | Oc] [W_o | W_oc]^T + b_o + b_oc
+  {
+    ProfScope ps(H3_ST_OUT_GEMM, s);
+    launch_gemm_bf16(attn, 2 * d, reinterpret_cast<const bf16_t *>(w.out_w), 2 * d, y, d, rows,
+                     d, 2 * d, reinterpret_cast<const bf16_t *>(w.out_b),
+                     reinterpret_cast<const bf16_t *>(w.outc_b), H3_EPI_NONE, 0, s);
+  }
+  // x <- x + g1 y ; n2 = AdaLN(x; sh2, sc2)
+  if (o.fused_gate_adaln) {
+    ProfScope ps(H3_ST_GATE_ADALN, s);
+    launch_gate_adaln(x, y, g1, x, sh2, sc2, n2, rows, d, s);
+  } else {
+    ProfScope ps(H3_ST_GATE_ADALN, s);
+    launch_gate_adaln(x, y, g1, x, nullptr, nullptr, nullptr, rows, d, s);
+    launch_gate_adaln(x, nullptr, nullptr, nullptr, sh2, sc2, n2, rows, d, s);
+  }
+  // h = GELU(n2 W1^T + b1)
+  {
+    ProfScope ps(H3_ST_FC1_GEMM, s);
+    launch_gemm_bf16(n2, d, reinterpret_cast<const bf16_t *>(w.fc1_w), d, h, F, rows, F, d,
+                     reinterpret_cast<const bf16_t *>(w.fc1_b), nullptr, H3_EPI_GELU, 0, s);
+  }
+  // m = FC2(h)
+  if (o.fc2_mode == H3_FC2_BF16) {
+    ProfScope ps(H3_ST_FC2_GEMM, s);
+    launch_gemm_bf16(h, F, reinterpret_cast<const bf16_t *>(w.fc2_w), F, mo, d, rows, d, F,
+                     reinterpret_cast<const bf16_t *>(w.fc2_b), nullptr, H3_EPI_NONE, 0, s);
+  } else {
+    const int group = o.fc2_mode == H3_FC2_INT8_ROW ? F : 1024;
+    int8_t *hq = reinterpret_cast<int8_t *>(ws + p.hq);
+    float *hs = reinterpret_cast<float *>(ws + p.hs);
+    {
+      ProfScope ps(H3_ST_FC2_QUANT, s);
+      launch_quant_rows(h, hq, hs, rows, F, group, s);
+    }
+    ProfScope ps(H3_ST_FC2_I8_GEMM, s);
+    launch_gemm_i8(hq, hs, reinterpret_cast<const int8_t *>(w.fc2_q),
+                   reinterpret_cast<const float *>(w.fc2_s),
+                   reinterpret_cast<const bf16_t *>(w.fc2_b), mo, d, rows, d, F, group, s);
+  }
+  // x <- x + g2 m ; optionally n1_next = AdaLN(x; next shift, scale)
+  if (n1_next && o.fused_cross_block) {
+    ProfScope ps(H3_ST_GATE_ADALN, s);
+    launch_gate_adaln(x, mo, g2, x, mod_next, mod_next + d, n1_next, rows, d, s);
+  } else {
+    ProfScope ps(H3_ST_GATE_ADALN, s);
+    launch_gate_adaln(x, mo, g2, x, nullptr, nullptr, nullptr, rows, d, s);
+    if (n1_next) launch_gate_adaln(x, nullptr, nullptr, nullptr, mod_next, mod_next + d, n1_next, rows, d, s);
+  }
+  (void)geom;
+  return check_launch("h3_dit_block_fwd");
+}
+
+int32_t run_modulation(const h3_model *m, float sigma, float *mod, float *mod_final, char *ws,
+                       const WsPlan &p, hipStream_t s) {
+  const int d = m->dims.d_model, nb = m->dims.n_blocks;
+  const h3_global_weights &g = m->g;
+  float *tmp = reinterpret_cast<float *>(ws + p.tmp);
+  float *e = tmp, *h1 = tmp + 256, *u = h1 + d, *Mv = u + d;
+  launch_timestep_sinusoid(sigma, e, s);
+  launch_gemv(reinterpret_cast<const bf16_t *>(g.t1_w), e, reinterpret_cast<const bf16_t *>(g.t1_b),
+              nullptr, h1, d, 256, 1, s);
+  launch_gemv(reinterpret_cast<const bf16_t *>(g.t2_w), h1, reinterpret_cast<const bf16_t *>(g.t2_b),
+              nullptr, u, d, d, 1, s);
+  launch_gemv(reinterpret_cast<const bf16_t *>(g.mod_w), u, reinterpret_cast<const bf16_t *>(g.mod_b),
+              nullptr, Mv, 6 * d, d, 0, s);
+  launch_add_table(Mv, reinterpret_cast<const bf16_t *>(g.mod_table), mod, nb, 6 * d, s);
+  launch_gemv(reinterpret_cast<const bf16_t *>(g.fin_w), u, reinterpret_cast<const bf16_t *>(g.fin_b),
+              reinterpret_cast<const bf16_t *>(g.fin_t), mod_final, 2 * d, d, 0, s);
+  return check_launch("h3_modulation");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t h3_model_create(const h3_dims *dims, const h3_global_weights *g,
+                        const h3_block_weights *blocks, int32_t n_blocks, h3_model **out) {
+  if (!dims || !g || !blocks || !out) return fail(H3_EINVAL, "h3_model_create: NULL argument");
+  *out = nullptr;
+  const h3_dims &dm = *dims;
+  if (dm.n_blocks != n_blocks || n_blocks < 1)
+    return fail(H3_ESHAPE, "h3_model_create: n_blocks mismatch");
+  if (!supported_width(dm.d_model))
+    return fail(H3_ESHAPE, "h3_model_create: d_model must be 512 * {1,2,3,4,5,6,8,10,12,16}");
+  if (dm.n_heads < 1 || dm.d_model % dm.n_heads)
+    return fail(H3_ESHAPE, "h3_model_create: n_heads must divide d_model");
+  const int D = dm.d_model / dm.n_heads;
+  if (D != 64 && D != 128) return fail(H3_ESHAPE, "h3_model_create: head_dim must be 64 or 128");
+  if (dm.ffn_dim < 1024 || dm.ffn_dim % 1024)
+    return fail(H3_ESHAPE, "h3_model_create: ffn_dim must be a positive multiple of 1024");
+  if (dm.ctx_len < 1) return fail(H3_ESHAPE, "h3_model_create: ctx_len must be >= 1");
+  if (dm.latent_ch < 64 || dm.latent_ch % 64)
+    return fail(H3_ESHAPE, "h3_model_create: latent_ch must be a positive multiple of 64");
+  const void *gp[] = {g->t1_w, g->t1_b, g->t2_w, g->t2_b, g->mod_w, g->mod_b, g->fin_w,
+                      g->fin_b, g->fin_t, g->mod_table, g->patch_w, g->patch_b, g->head_w,
+                      g->head_b};
+  for (const void *q : gp)
+    if (!q) return fail(H3_EINVAL, "h3_model_create: NULL global weight");
+  for (int b = 0; b < n_blocks; ++b) {
+    const h3_block_weights &w = blocks[b];
+    const void *bp[] = {w.qkvq_w, w.qkvq_b, w.kc_w, w.kc_b, w.vc_w, w.vc_b, w.out_w, w.out_b,
+                        w.outc_b, w.q_gamma, w.k_gamma, w.fc1_w, w.fc1_b, w.fc2_w, w.fc2_b};
+    for (const void *q : bp)
+      if (!q) return fail(H3_EINVAL, "h3_model_create: NULL weight in block " + std::to_string(b));
+  }
+  h3_model *m = new (std::nothrow) h3_model();
+  if (!m) return fail(H3_EINVAL, "h3_model_create: out of host memory");
+  m->dims = dm;
+  m->head_dim = D;
+  m->g = *g;
+  m->blocks = new (std::nothrow) h3_block_weights[n_blocks];
+  if (!m->blocks) {
+    delete m;
+    return fail(H3_EINVAL, "h3_model_create: out of host memory");
+  }
+  std::memcpy(m->blocks, blocks, sizeof(h3_block_weights) * n_blocks);
+  *out = m;
+  clear_error();
+  return H3_OK;
+}
+
+void h3_model_destroy(h3_model *m) {
+  if (!m) return;
+  delete[] m->blocks;
+  delete m;
+}
+
+int32_t h3_workspace_size(const h3_model *m, int32_t n_tokens, const h3_run_opts *o,
+                          size_t *bytes) {
+  if (int32_t e = validate_model(m)) return e;
+  if (int32_t e = check_opts(o)) return e;
+  if (!bytes) return fail(H3_EINVAL, "h3_workspace_size: bytes is NULL");
+  if (n_tokens < 1) return fail(H3_ESHAPE, "h3_workspace_size: n_tokens must be >= 1");
+  *bytes = plan_workspace(*m, n_tokens, *o).total;
+  return H3_OK;
+}
+
+int32_t h3_workspace_layout(const h3_model *m, int32_t n_tokens, const h3_run_opts *o,
+                            h3_ws_layout *layout) {
+  if (int32_t e = validate_model(m)) return e;
+  if (int32_t e = check_opts(o)) return e;
+  if (!layout) return fail(H3_EINVAL, "h3_workspace_layout: layout is NULL");
+  if (n_tokens < 1) return fail(H3_ESHAPE, "h3_workspace_layout: n_tokens must be >= 1");
+  const WsPlan p = plan_workspace(*m, n_tokens, *o);
+  layout->n1 = p.n1; layout->qkvq = p.qkvq; layout->attn = p.attn; layout->y = p.y;
+  layout->n2 = p.n2; layout->h = p.h; layout->m = p.m; layout->hq = p.hq; layout->hs = p.hs;
+  layout->rope = p.rope; layout->total = p.total;
+  return H3_OK;
+}
+
+int32_t h3_prepare_context(const h3_model *m, const void *ctx, void *ctx_kv, void *stream) {
+  if (int32_t e = validate_model(m)) return e;
+  if (!ctx || !ctx_kv) return fail(H3_EINVAL, "h3_prepare_context: NULL pointer");
+  const int d = m->dims.d_model, L = m->dims.ctx_len;
+  hipStream_t s = as_stream(stream);
+  bf16_t *kv = reinterpret_cast<bf16_t *>(ctx_kv);
+  for (int b = 0; b < m->dims.n_blocks; ++b) {
+    const h3_block_weights &w = m->blocks[b];
+    bf16_t *kb = kv + static_cast<size_t>(b) * 2 * L * d;
+    launch_gemm_bf16(reinterpret_cast<const bf16_t *>(ctx), d, reinterpret_cast<const bf16_t *>(w.kc_w),
+                     d, kb, d, L, d, d, reinterpret_cast<const bf16_t *>(w.kc_b), nullptr,
+                     H3_EPI_NONE, 0, s);
+    launch_gemm_bf16(reinterpret_cast<const bf16_t *>(ctx), d, reinterpret_cast<const bf16_t *>(w.vc_w),
+                     d, kb + static_cast<size_t>(L) * d, d, L, d, d,
+                     reinterpret_cast<const bf16_t *>(w.vc_b), nullptr, H3_EPI_NONE, 0, s);
+  }
+  return check_launch("h3_prepare_context");
+}
+
+int32_t h3_quantize_fc2_weights(const h3_model *m, void *stream) {
+  if (int32_t e = validate_model(m)) return e;
+  for (int b = 0; b < m->dims.n_blocks; ++b)
+    if (!m->blocks[b].fc2_q || !m->blocks[b].fc2_s)
+      return fail(H3_EINVAL, "h3_quantize_fc2_weights: fc2_q/fc2_s not set in block " + std::to_string(b));
+  hipStream_t s = as_stream(stream);
+  const int d = m->dims.d_model, F = m->dims.ffn_dim;
+  for (int b = 0; b < m->dims.n_blocks; ++b) {
+    const h3_block_weights &w = m->blocks[b];
+    launch_quant_rows(reinterpret_cast<const bf16_t *>(w.fc2_w), reinterpret_cast<int8_t *>(w.fc2_q),
+                      reinterpret_cast<float *>(w.fc2_s), d, F, F, s);
+  }
+  return check_launch("h3_quantize_fc2_weights");
+}
+
+int32_t h3_modulation(const h3_model *m, float sigma, float *mod, float *mod_final, void *ws,
+                      size_t ws_bytes, void *stream) {
+  if (int32_t e = validate_model(m)) return e;
+  if (!mod || !mod_final) return fail(H3_EINVAL, "h3_modulation: NULL output");
+  if (!std::isfinite(sigma)) return fail(H3_EINVAL, "h3_modulation: sigma must be finite");
+  h3_run_opts o{};
+  const WsPlan p = plan_workspace(*m, 1, o);
+  if (!ws || ws_bytes < p.total) return fail(H3_EWORKSPACE, "h3_modulation: workspace too small");
+  return run_modulation(m, sigma, mod, mod_final, reinterpret_cast<char *>(ws), p, as_stream(stream));
+}
+
+int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
+                         const h3_run_opts *o, void *x, const void *n1_in, void *n1_next,
+                         const float *mod, const float *mod_next, const void *ctx_kv, void *ws,
+                         size_t ws_bytes, void *stream) {
+  if (int32_t e = validate_model(m)) return e;
+  if (int32_t e = check_opts(o)) return e;
+  if (block < 0 || block >= m->dims.n_blocks) return fail(H3_EINVAL, "h3_dit_block_fwd: bad block index");
+  int32_t n = 0;
+  if (int32_t e = h3_geom_tokens(geom, &n)) return e;
+  if (!x || !mod || !ctx_kv) return fail(H3_EINVAL, "h3_dit_block_fwd: NULL x, mod or ctx_kv");
+  if (n1_next && !mod_next) return fail(H3_EINVAL, "h3_dit_block_fwd: n1_next needs mod_next");
+  if (o->fc2_mode != H3_FC2_BF16 && (!m->blocks[block].fc2_q || !m->blocks[block].fc2_s))
+    return fail(H3_EINVAL, "h3_dit_block_fwd: int8 FC2 needs quantised weights");
+  const WsPlan p = plan_workspace(*m, n, *o);
+  if (!ws || ws_bytes < p.total) return fail(H3_EWORKSPACE, "h3_dit_block_fwd: workspace too small");
+  hipStream_t s = as_stream(stream);
+  char *w = reinterpret_cast<char *>(ws);
+  float2 *rope = reinterpret_cast<float2 *>(w + p.rope);
+  launch_rope_table(rope, *geom, n, m->head_dim, s);
+  return run_block(m, block, *geom, n, *o, reinterpret_cast<bf16_t *>(x),
+                   reinterpret_cast<const bf16_t *>(n1_in), reinterpret_cast<bf16_t *>(n1_next),
+                   mod, mod_next, reinterpret_cast<const bf16_t *>(ctx_kv), w, p, s, rope);
+}
+
+int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts *o,
+                       const float *latent, float sigma, const int32_t *active, int32_t n_active,
+                       int32_t eval_index, const void *ctx_kv, float *velocity, void *ws,
+                       size_t ws_bytes, void *stream) {
+  if (int32_t e = validate_model(m)) return e;
+  if (int32_t e = check_opts(o)) return e;
+  if (!geom || geom->paired) return fail(H3_EINVAL, "h3_dit_forward: geom must be the full grid");
+  int32_t n = 0;
+  if (int32_t e = h3_geom_tokens(geom, &n)) return e;
+  if (!latent || !velocity || !active || !ctx_kv) return fail(H3_EINVAL, "h3_dit_forward: NULL pointer");
+  if (!std::isfinite(sigma)) return fail(H3_EINVAL, "h3_dit_forward: sigma must be finite");
+  const int nb = m->dims.n_blocks;
+  if (n_active < 1 || n_active > nb) return fail(H3_EINVAL, "h3_dit_forward: bad n_active");
+  for (int i = 0; i < n_active; ++i) {
+    if (active[i] < 0 || active[i] >= nb) return fail(H3_EINVAL, "h3_dit_forward: active index out of range");
+    if (i && active[i] <= active[i - 1]) return fail(H3_EINVAL, "h3_dit_forward: active must ascend");
+    if (o->fc2_mode != H3_FC2_BF16 && (!m->blocks[active[i]].fc2_q || !m->blocks[active[i]].fc2_s))
+      return fail(H3_EINVAL, "h3_dit_forward: int8 FC2 needs quantised weights");
+  }
+  if (eval_index < 0) return fail(H3_EINVAL, "h3_dit_forward: eval_index must be >= 0");
+  int32_t merge_after = 0, restore_before = 0, n_red = 0;
+  if (o->token_reduction) {
+    if (int32_t e = h3_token_plan(geom->f_lat, geom->grid_h, geom->grid_w, eval_index, n_active,
+                                  &merge_after, &restore_before, nullptr, &n_red))
+      return e;
+  }
+  const WsPlan p = plan_workspace(*m, n, *o);
+  if (!ws || ws_bytes < p.total) return fail(H3_EWORKSPACE, "h3_dit_forward: workspace too small");
+
+  hipStream_t s = as_stream(stream);
+  char *w = reinterpret_cast<char *>(ws);
+  const int d = m->dims.d_model, C = m->dims.latent_ch, L = m->dims.ctx_len;
+  float *mod = reinterpret_cast<float *>(w + p.mod);
+  float *fin = reinterpret_cast<float *>(w + p.fin);
+  bf16_t *x = reinterpret_cast<bf16_t *>(w + p.x);
+  bf16_t *xr = reinterpret_cast<bf16_t *>(w + p.xr);
+  bf16_t *na = reinterpret_cast<bf16_t *>(w + p.n1b);
+  bf16_t *nb_ = reinterpret_cast<bf16_t *>(w + p.n1);
+  bf16_t *lat16 = reinterpret_cast<bf16_t *>(w + p.lat16);
+  float2 *rope_full = reinterpret_cast<float2 *>(w + p.rope);
+  float2 *rope_red = reinterpret_cast<float2 *>(w + p.rope_r);
+  const bf16_t *kv = reinterpret_cast<const bf16_t *>(ctx_kv);
+
+  {
+    ProfScope ps(H3_ST_MODULATION, s);
+    if (int32_t e = run_modulation(m, sigma, mod, fin, w, p, s)) return e;
+  }
+  {
+    // patch embedding: x = bf16(latent) W_p^T + b_p
+    ProfScope ps(H3_ST_PATCH, s);
+    launch_f32_to_bf16(latent, lat16, static_cast<int64_t>(n) * C, s);
+    launch_gemm_bf16(lat16, C, reinterpret_cast<const bf16_t *>(m->g.patch_w), C, x, d, n, d, C,
+                     reinterpret_cast<const bf16_t *>(m->g.patch_b), nullptr, H3_EPI_NONE, 0, s);
+  }
+  launch_rope_table(rope_full, *geom, n, m->head_dim, s);
+  h3_geom red = *geom;
+  red.paired = 1;
+  if (o->token_reduction) launch_rope_table(rope_red, red, n_red, m->head_dim, s);
+
+  // n1 of the first block; the n1 buffers alternate between na and the block plan's n1 slot
+  bf16_t *cur = x;
+  int rows = n;
+  const float2 *rope = rope_full;
+  const h3_geom *g_cur = geom;
+  bf16_t *n1 = na, *n1_other = nb_;
+  bool n1_valid = false;
+  for (int pos = 0; pos < n_active; ++pos) {
+    const int b = active[pos];
+    const float *mb = mod + static_cast<size_t>(b) * 6 * d;
+    if (o->token_reduction && pos == merge_after) {
+      ProfScope ps(H3_ST_TOKEN_REDUCE, s);
+      launch_token_reduce(0, *geom, d, x, nullptr, xr, s);
+      cur = xr; rows = n_red; rope = rope_red; g_cur = &red; n1_valid = false;
+    }
+    if (o->token_reduction && pos == restore_before - 1) {
+      ProfScope ps(H3_ST_TOKEN_REDUCE, s);
+      launch_token_reduce(1, *geom, d, xr, x, x, s);
+      cur = x; rows = n; rope = rope_full; g_cur = geom; n1_valid = false;
+    }
+    if (!n1_valid) {
+      ProfScope ps(H3_ST_ADALN, s);
+      launch_gate_adaln(cur, nullptr, nullptr, nullptr, mb, mb + d, n1, rows, d, s);
+    }
+    // the next AdaLN can be fused into this block's MLP gate when no token op sits between
+    const bool last = pos + 1 == n_active;
+    const bool token_op_next = o->token_reduction && !last &&
+                               (pos + 1 == merge_after || pos + 1 == restore_before - 1);
+    const bool restore_before_head = o->token_reduction && last && restore_before == n_active + 1 &&
+                                     merge_after < n_active;
+    const float *mnext = nullptr;
+    bf16_t *n1n = nullptr;
+    if (!last && !token_op_next) {
+      mnext = mod + static_cast<size_t>(active[pos + 1]) * 6 * d;
+      n1n = n1_other;
+    } else if (last && !restore_before_head) {
+      mnext = fin;
+      n1n = n1_other;
+    }
+    // n1 is always supplied, so the block never writes its own n1 slot (p.n1), which serves
+    // here as the second of the two alternating n1 buffers
+    int32_t e = run_block(m, b, *g_cur, rows, *o, cur, n1, n1n, mb, mnext,
+                          kv + static_cast<size_t>(b) * 2 * L * d, w, p, s, rope);
+    if (e) return e;
+    if (n1n) {
+      std::swap(n1, n1_other);
+      n1_valid = true;
+    } else {
+      n1_valid = false;
+    }
+    if (last && restore_before_head) {
+      {
+        ProfScope ps(H3_ST_TOKEN_REDUCE, s);
+        launch_token_reduce(1, *geom, d, xr, x, x, s);
+      }
+      cur = x; rows = n;
+      ProfScope ps(H3_ST_ADALN, s);
+      launch_gate_adaln(x, nullptr, nullptr, nullptr, fin, fin + d, n1, rows, d, s);
+      n1_valid = true;
+    }
+  }
+  // head: velocity = AdaLN_final(x) W_h^T + b_h, float32
+  {
+    ProfScope ps(H3_ST_HEAD, s);
+    launch_gemm_bf16(n1, d, reinterpret_cast<const bf16_t *>(m->g.head_w), d, velocity, C, n, C,
+                     d, reinterpret_cast<const bf16_t *>(m->g.head_b), nullptr, H3_EPI_NONE, 1, s);
+  }
+  return check_launch("h3_dit_forward");
+}
+
+int32_t h3_euler_step(float *latent, const float *velocity, float sigma_cur, float sigma_next,
+                      int64_t n_elems, void *stream) {
+  if (!latent || !velocity) return fail(H3_EINVAL, "h3_euler_step: NULL pointer");
+  if (n_elems < 0) return fail(H3_EINVAL, "h3_euler_step: n_elems must be >= 0");
+  if (!std::isfinite(sigma_cur) || !std::isfinite(sigma_next))
+    return fail(H3_EINVAL, "h3_euler_step: sigmas must be finite");
+  if (reinterpret_cast<uintptr_t>(latent) % 16 || reinterpret_cast<uintptr_t>(velocity) % 16)
+    return fail(H3_EINVAL, "h3_euler_step: pointers must be 16-byte aligned");
+  if (n_elems == 0) return H3_OK;
+  const float dt = sigma_next - sigma_cur;
+  ProfScope ps(H3_ST_EULER, as_stream(stream));
+  launch_euler(latent, velocity, dt, n_elems, as_stream(stream));
+  return check_launch("h3_euler_step");
+}
+
+int32_t h3_token_reduce(int32_t direction, const h3_geom *geom, int32_t d_model, const void *src,
+                        const void *bypass, void *dst, void *stream) {
+  if (direction != 0 && direction != 1) return fail(H3_EINVAL, "h3_token_reduce: direction must be 0 or 1");
+  int32_t n = 0;
+  if (int32_t e = h3_geom_tokens(geom, &n)) return e;
+  if (geom->paired) return fail(H3_EINVAL, "h3_token_reduce: geom must be the full grid");
+  if (d_model < 8 || d_model % 8) return fail(H3_ESHAPE, "h3_token_reduce: d_model must be a multiple of 8");
+  if (!src || !dst || (direction == 1 && !bypass)) return fail(H3_EINVAL, "h3_token_reduce: NULL pointer");
+  if (dst == src) return fail(H3_EINVAL, "h3_token_reduce: dst must not alias src");
+  if (direction == 0 && bypass) return fail(H3_EINVAL, "h3_token_reduce: merge takes no bypass");
+  launch_token_reduce(direction, *geom, d_model, reinterpret_cast<const bf16_t *>(src),
+                      reinterpret_cast<const bf16_t *>(bypass), reinterpret_cast<bf16_t *>(dst),
+                      as_stream(stream));
+  return check_launch("h3_token_reduce");
+}
+
+int32_t h3_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C, int64_t ldc,
+                     int32_t M, int32_t N, int32_t K, const void *bias, const void *bias2,
+                     int32_t epilogue, int32_t out_f32, void *stream) {
+  if (!A || !B || !C) return fail(H3_EINVAL, "h3_gemm_bf16: NULL pointer");
+  if (M < 1 || N < 1 || K < 64 || K % 64) return fail(H3_ESHAPE, "h3_gemm_bf16: need M,N >= 1 and K % 64 == 0");
+  if (lda < K || ldb < K || ldc < N || lda % 8 || ldb % 8)
+    return fail(H3_ESHAPE, "h3_gemm_bf16: strides too small or not multiples of 8");
+  if (epilogue != H3_EPI_NONE && epilogue != H3_EPI_GELU) return fail(H3_EINVAL, "h3_gemm_bf16: bad epilogue");
+  if (out_f32 && epilogue != H3_EPI_NONE) return fail(H3_EUNSUPPORTED, "h3_gemm_bf16: GELU with float output");
+  launch_gemm_bf16(reinterpret_cast<const bf16_t *>(A), lda, reinterpret_cast<const bf16_t *>(B), ldb,
+                   C, ldc, M, N, K, reinterpret_cast<const bf16_t *>(bias),
+                   reinterpret_cast<const bf16_t *>(bias2), epilogue, out_f32, as_stream(stream));
+  return check_launch("h3_gemm_bf16");
+}
+
+int32_t h3_attention(const void *Q, int64_t ldq, const void *K, int64_t ldk, const void *V,
+                     int64_t ldv, void *O, int64_t ldo, int32_t n_q, int32_t n_k, int32_t n_heads,
+                     int32_t head_dim, void *stream) {
+  if (!Q || !K || !V || !O) return fail(H3_EINVAL, "h3_attention: NULL pointer");
+  if (head_dim != 64 && head_dim != 128) return fail(H3_EUNSUPPORTED, "h3_attention: head_dim must be 64 or 128");
+  if (n_q < 1 || n_k < 1 || n_heads < 1 || n_heads > 65535) return fail(H3_ESHAPE, "h3_attention: bad sizes");
+  const int64_t w = static_cast<int64_t>(n_heads) * head_dim;
+  if (ldq < w || ldk < w || ldv < w || ldo < w || ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8)
+    return fail(H3_ESHAPE, "h3_attention: strides too small or not multiples of 8");
+  launch_attention(reinterpret_cast<const bf16_t *>(Q), ldq, reinterpret_cast<const bf16_t *>(K), ldk,
+                   reinterpret_cast<const bf16_t *>(V), ldv, reinterpret_cast<bf16_t *>(O), ldo, n_q,
+                   n_k, n_heads, head_dim, as_stream(stream));
+  return check_launch("h3_attention");
+}
+
+int32_t h3_quant_rows(const void *X, void *Q, float *S, int32_t rows, int32_t K, int32_t group,
+                      void *stream) {
+  if (!X || !Q || !S) return fail(H3_EINVAL, "h3_quant_rows: NULL pointer");
+  if (rows < 1 || K < 1024 || K % 1024) return fail(H3_ESHAPE, "h3_quant_rows: K must be a multiple of 1024");
+  if (group != K && group != 1024) return fail(H3_EINVAL, "h3_quant_rows: group must be K or 1024");
+  launch_quant_rows(reinterpret_cast<const bf16_t *>(X), reinterpret_cast<int8_t *>(Q), S, rows, K,
+                    group, as_stream(stream));
+  return check_launch("h3_quant_rows");
+}
+
+int32_t h3_gemm_i8(const void *QA, const float *SA, const void *QW, const float *SW,
+                   const void *bias, void *C, int64_t ldc, int32_t M, int32_t N, int32_t K,
+                   int32_t group, void *stream) {
+  if (!QA || !SA || !QW || !SW || !bias || !C) return fail(H3_EINVAL, "h3_gemm_i8: NULL pointer");
+  if (M < 1 || N < 1 || K < 1024 || K % 1024) return fail(H3_ESHAPE, "h3_gemm_i8: K must be a multiple of 1024");
+  if (group != K && group != 1024) return fail(H3_EINVAL, "h3_gemm_i8: group must be K or 1024");
+  if (ldc < N) return fail(H3_ESHAPE, "h3_gemm_i8: ldc < N");
+  launch_gemm_i8(reinterpret_cast<const int8_t *>(QA), SA, reinterpret_cast<const int8_t *>(QW), SW,
+                 reinterpret_cast<const bf16_t *>(bias), reinterpret_cast<bf16_t *>(C), ldc, M, N, K,
+                 group, as_stream(stream));
+  return check_launch("h3_gemm_i8");
+}
+
+int32_t h3_gate_adaln(const void *x, const void *y, const float *gate, void *x_out,
+                      const float *shift, const float *scale, void *n_out, int32_t rows,
+                      int32_t d_model, void *stream) {
+  if (!x) return fail(H3_EINVAL, "h3_gate_adaln: x is NULL");
+  if (!y && !n_out) return fail(H3_EINVAL, "h3_gate_adaln: nothing to compute");
+  if (y && (!gate || !x_out)) return fail(H3_EINVAL, "h3_gate_adaln: gate needs gate and x_out");
+  if (n_out && (!shift || !scale)) return fail(H3_EINVAL, "h3_gate_adaln: AdaLN needs shift and scale");
+  if (rows < 1) return fail(H3_ESHAPE, "h3_gate_adaln: rows must be >= 1");
+  if (!supported_width(d_model)) return fail(H3_ESHAPE, "h3_gate_adaln: unsupported d_model");
+  launch_gate_adaln(reinterpret_cast<const bf16_t *>(x), reinterpret_cast<const bf16_t *>(y), gate,
+                    reinterpret_cast<bf16_t *>(x_out), shift, scale, reinterpret_cast<bf16_t *>(n_out),
+                    rows, d_model, as_stream(stream));
+  return check_launch("h3_gate_adaln");
+}
+
+int32_t h3_rope_table(const h3_geom *geom, int32_t head_dim, void *table, void *stream) {
+  int32_t n = 0;
+  if (int32_t e = h3_geom_tokens(geom, &n)) return e;
+  if (!table) return fail(H3_EINVAL, "h3_rope_table: table is NULL");
+  if (head_dim != 64 && head_dim != 128) return fail(H3_EUNSUPPORTED, "h3_rope_table: head_dim must be 64 or 128");
+  launch_rope_table(reinterpret_cast<float2 *>(table), *geom, n, head_dim, as_stream(stream));
+  return check_launch("h3_rope_table");
+}
+
+int32_t h3_qk_norm_rope(void *qkvq, int64_t ld, int32_t n_tokens, int32_t d_model,
+                        int32_t head_dim, const void *q_gamma, const void *k_gamma,
+                        int32_t qk_norm, const void *table, void *stream) {
+  if (!qkvq || !table || (qk_norm && (!q_gamma || !k_gamma)))
+    return fail(H3_EINVAL, "h3_qk_norm_rope: NULL pointer");
+  if (head_dim != 64 && head_dim != 128) return fail(H3_EUNSUPPORTED, "h3_qk_norm_rope: head_dim must be 64 or 128");
+  if (n_tokens < 1 || d_model < 512 || d_model % 512 || d_model % head_dim)
+    return fail(H3_ESHAPE, "h3_qk_norm_rope: d_model must be a multiple of 512 and of head_dim");
+  if (ld < 2 * d_model || ld % 8) return fail(H3_ESHAPE, "h3_qk_norm_rope: ld too small or not a multiple of 8");
+  launch_qk_norm_rope(reinterpret_cast<bf16_t *>(qkvq), ld, n_tokens, d_model, head_dim,
+                      reinterpret_cast<const bf16_t *>(q_gamma), reinterpret_cast<const bf16_t *>(k_gamma),
+                      qk_norm, reinterpret_cast<const float2 *>(table), as_stream(stream));
+  return check_launch("h3_qk_norm_rope");
+}
+
+}  // extern "C"

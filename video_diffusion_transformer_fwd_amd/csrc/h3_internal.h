@@ -1,0 +1,108 @@
+// Internal declarations shared by the HIP sources of libh3dit.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/h3dit.h"
+
+namespace h3 {
+
+// ---------------------------------------------------------------- errors
+void set_error(const std::string &msg);
+void clear_error();
+int32_t fail(int32_t code, const std::string &msg);
+// Checks the launch status of the last kernel(s); returns H3_OK or H3_EHIP.
+int32_t check_launch(const char *what);
+
+// ---------------------------------------------------------------- bf16 helpers
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+// Round-to-nearest-even float32 -> bf16 bits (inputs are finite on this path; NaN is kept NaN).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// ---------------------------------------------------------------- model
+struct Model {
+  h3_dims dims;
+  int32_t head_dim;
+  h3_global_weights g;
+  h3_block_weights *blocks;  // n_blocks entries (host copy of the pointer table)
+};
+
+// Workspace plan for a token count and options (all offsets 256-byte aligned).
+struct WsPlan {
+  // block part
+  size_t n1, qkvq, attn, y, n2, h, m, hq, hs, rope;
+  // forward / modulation part
+  size_t mod, fin, tmp, x, xr, n1b, lat16, rope_r;
+  size_t total;
+};
+WsPlan plan_workspace(const Model &m, int32_t n_tokens, const h3_run_opts &o);
+
+// ---------------------------------------------------------------- kernel launchers
+// All launchers assume validated arguments and enqueue on `s`.
+void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, void *C,
+                      int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
+                      int epilogue, int out_f32, hipStream_t s);
+void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
+                    const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
+                    hipStream_t s);
+void launch_attention(const bf16_t *Q, int64_t ldq, const bf16_t *K, int64_t ldk,
+                      const bf16_t *V, int64_t ldv, bf16_t *O, int64_t ldo, int nq, int nk,
+                      int heads, int head_dim, hipStream_t s);
+// x_out = bf16(x + gate*y) (if y != nullptr), then n_out = bf16(LN(x_out)(1+scale)+shift)
+// (if n_out != nullptr).  With y == nullptr the row is read from x.  x_out may equal x.
+void launch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
+                       const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
+                       hipStream_t s);
+void launch_rope_table(float2 *table, const h3_geom &geom, int n_tokens, int head_dim,
+                       hipStream_t s);
+void launch_qk_norm_rope(bf16_t *qkvq, int64_t ld, int n_tokens, int d, int head_dim,
+                         const bf16_t *q_gamma, const bf16_t *k_gamma, int qk_norm,
+                         const float2 *table, hipStream_t s);
+void launch_token_reduce(int direction, const h3_geom &geom, int d, const bf16_t *src,
+                         const bf16_t *bypass, bf16_t *dst, hipStream_t s);
+void launch_euler(float *x, const float *v, float dt, int64_t n, hipStream_t s);
+void launch_quant_rows(const bf16_t *X, int8_t *Q, float *S, int rows, int K, int group,
+                       hipStream_t s);
+void launch_f32_to_bf16(const float *src, bf16_t *dst, int64_t n, hipStream_t s);
+void launch_timestep_sinusoid(float sigma, float *e, hipStream_t s);
+// y[r] = act(sum_k W[r,k] x[k] + b[r]) + add[r]; act: 0 none, 1 SiLU.
+void launch_gemv(const bf16_t *W, const float *x, const bf16_t *b, const bf16_t *add, float *y,
+                 int rows, int K, int act, hipStream_t s);
+// out[b, i] = M[i] + T[b, i] for b < nb, i < width (T bf16).
+void launch_add_table(const float *Mv, const bf16_t *T, float *out, int nb, int width,
+                      hipStream_t s);
+
+inline size_t align_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+// Records a begin event now and an end event at scope exit on stream s when a profiling
+// session selects this stage (h3_profile_begin); otherwise does nothing.
+class ProfScope {
+ public:
+  ProfScope(int stage, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope &) = delete;
+  ProfScope &operator=(const ProfScope &) = delete;
+
+ private:
+  int stage_;
+  hipStream_t stream_;
+  int pair_;
+};
+
+}  // namespace h3

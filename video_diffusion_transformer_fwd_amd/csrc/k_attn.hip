@@ -1,0 +1,220 @@
+// Flash-style multi-head attention on the gfx950 matrix cores (self-attention over the video
+// tokens and cross-attention to the text context use the same kernel).
+//
+// Workgroup = 4 wave64s = 128 query rows of one head; each wave owns 32 queries.  Keys and
+// values stream through LDS in tiles of 64.  Per tile a wave computes the transposed scores
+// S^T = K Q^T (32 keys x 32 queries per v_mfma_f32_32x32x16_bf16 block), so every lane holds
+// scores of a single query (lane % 32) and the row max / row sum need only the partner lane
+// (lane ^ 32): one cross-lane swap instead of a 32-lane reduction.  The exponentiated scores
+// stay in registers and are fed straight back as the B operand of O^T += V^T P^T: the 16 keys of
+// each PV step are taken in the order the score accumulator already holds them, and V is
+// staged transposed in LDS so the matching A operand is two 8-byte LDS reads per lane.
+// Softmax is online (running max m, running sum l, float32, base-2 exponentials).
+// Keys beyond n_k are masked to -inf; query rows beyond n_q are computed and not stored.
+#include <hip/hip_runtime.h>
+
+#include "h3_internal.h"
+
+namespace h3 {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+constexpr int kBlockM = 128;  // queries per workgroup
+constexpr int kBlockN = 64;   // keys per tile
+
+template <int D>
+struct AttnCfg {
+  static constexpr int KS = D + 8;         // K tile row stride (elements)
+  static constexpr int VS = kBlockN + 8;   // V^T tile row stride (elements)
+  static constexpr int CH = D / 8;         // 16-byte chunks per row
+  static constexpr int K_PASSES = kBlockN * CH / 256;
+  static constexpr int V_GROUPS = 256 / 32;          // chunk groups per pass (32 key pairs)
+  static constexpr int V_PASSES = CH / V_GROUPS;
+  static constexpr size_t LDS_BYTES = (kBlockN * KS + D * VS) * sizeof(bf16_t);
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attention_kernel(
+    const bf16_t *__restrict__ Q, int64_t ldq, const bf16_t *__restrict__ K, int64_t ldk,
+    const bf16_t *__restrict__ V, int64_t ldv, bf16_t *__restrict__ O, int64_t ldo, int nq,
+    int nk, float scale_log2) {
+  using Cfg = AttnCfg<D>;
+  __shared__ __align__(16) bf16_t Ks[kBlockN * Cfg::KS];
+  __shared__ __align__(16) bf16_t Vt[D * Cfg::VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.y;
+  const int q_base = blockIdx.x * kBlockM + wave * 32;
+  const int hoff = head * D;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // Q fragments: B operand of S^T = K Q^T; lane holds Q[q_base + l32][ks*16 + 8g .. +7]
+  bf16x8_t qf[D / 16];
+  {
+    const int q = q_base + l32;
+    if (q < nq) {
+      const bf16_t *qp = Q + static_cast<int64_t>(q) * ldq + hoff + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t *>(qp + ks * 16);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qf[ks] = bf16x8_t{};
+    }
+  }
+
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // staging registers for the next K/V tile
+  uint4 kreg[Cfg::K_PASSES];
+  uint4 vreg[Cfg::V_PASSES][2];
+  const int k_row = tid / Cfg::CH, k_chunk = tid % Cfg::CH;  // K: 256/CH rows per pass
+  const int v_pair = tid & 31, v_group = tid >> 5;             // V: key pair, chunk group
+
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int p = 0; p < Cfg::K_PASSES; ++p) {
+      const int r = kv0 + k_row + p * (256 / Cfg::CH);
+      kreg[p] = r < nk ? *reinterpret_cast<const uint4 *>(K + static_cast<int64_t>(r) * ldk + hoff + k_chunk * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < Cfg::V_PASSES; ++p) {
+      const int chunk = v_group + p * Cfg::V_GROUPS;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = kv0 + 2 * v_pair + e;
+        vreg[p][e] = r < nk ? *reinterpret_cast<const uint4 *>(V + static_cast<int64_t>(r) * ldv + hoff + chunk * 8)
+                            : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int p = 0; p < Cfg::K_PASSES; ++p)
+      *reinterpret_cast<uint4 *>(Ks + (k_row + p * (256 / Cfg::CH)) * Cfg::KS + k_chunk * 8) = kreg[p];
+#pragma unroll
+    for (int p = 0; p < Cfg::V_PASSES; ++p) {
+      const int chunk = v_group + p * Cfg::V_GROUPS;
+      const uint32_t *a = reinterpret_cast<const uint32_t *>(&vreg[p][0]);
+      const uint32_t *b = reinterpret_cast<const uint32_t *>(&vreg[p][1]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // channels chunk*8 + 2w and +1; keys 2*v_pair (low half) and 2*v_pair+1 (high half)
+        const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);
+        const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t *>(Vt + (chunk * 8 + 2 * w) * Cfg::VS + 2 * v_pair) = lo;
+        *reinterpret_cast<uint32_t *>(Vt + (chunk * 8 + 2 * w + 1) * Cfg::VS + 2 * v_pair) = hi;
+      }
+    }
+  };
+
+  const int n_tiles = (nk + kBlockN - 1) / kBlockN;
+  load_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int kv0 = t * kBlockN;
+    __syncthreads();  // previous tile fully consumed
+    store_tile();
+    __syncthreads();
+    if (t + 1 < n_tiles) load_tile(kv0 + kBlockN);
+
+    // S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks)
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16_t{};
+      const bf16_t *kp = Ks + (kb * 32 + l32) * Cfg::KS + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(kp + ks * 16);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+    // scale, mask, tile max (lane's 32 scores + partner lane)
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kv0 + kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+        float v = s[kb][i] * scale_log2;
+        v = key < nk ? v : -INFINITY;
+        s[kb][i] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_new);
+        s[kb][i] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+
+    // O^T += V^T P^T over 4 steps of 16 keys
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st >> 1, half = st & 1;
+      bf16x8_t pb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(s[kb][8 * half + j]);
+      const int kbase = kb * 32 + 16 * half + 4 * g;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16_t *vp = Vt + (db * 32 + l32) * Cfg::VS + kbase;
+        const bf16x4_t v0 = *reinterpret_cast<const bf16x4_t *>(vp);
+        const bf16x4_t v1 = *reinterpret_cast<const bf16x4_t *>(vp + 8);
+        const bf16x8_t a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  const int q = q_base + l32;
+  if (q < nq) {
+    bf16_t *op = O + static_cast<int64_t>(q) * ldo + hoff;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dch = db * 32 + 8 * r4 + 4 * g;
+        uint2 w;
+        w.x = pack_bf2(o[db][4 * r4 + 0] * inv, o[db][4 * r4 + 1] * inv);
+        w.y = pack_bf2(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<uint2 *>(op + dch) = w;
+      }
+  }
+}
+
+}  // namespace
+
+void launch_attention(const bf16_t *Q, int64_t ldq, const bf16_t *K, int64_t ldk,
+                      const bf16_t *V, int64_t ldv, bf16_t *O, int64_t ldo, int nq, int nk,
+                      int heads, int head_dim, hipStream_t s) {
+  dim3 grid((nq + kBlockM - 1) / kBlockM, heads), block(256);
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
+  if (head_dim == 128)
+    attention_kernel<128><<<grid, block, 0, s>>>(Q, ldq, K, ldk, V, ldv, O, ldo, nq, nk, scale_log2);
+  else
+    attention_kernel<64><<<grid, block, 0, s>>>(Q, ldq, K, ldk, V, ldv, O, ldo, nq, nk, scale_log2);
+}
+
+}  // namespace h3

@@ -1,0 +1,478 @@
+// Memory-bound kernels of the block: gated residual + AdaLN (fused and unfused), Q/K
+// RMSNorm + 3D RoPE, the RoPE table, horizontal token pairing, Euler update, dynamic int8
+// row quantisation, and the small timestep/modulation kernels.
+//
+// Row kernels map one row to one 64-lane wavefront (4 rows per 256-thread workgroup): a row
+// of d bf16 values is d/512 16-byte vectors per lane, loaded with consecutive lanes on
+// consecutive 16-byte chunks (1 KiB per wave instruction), kept in registers, reduced with
+// cross-lane butterflies.  No LDS and no barriers are needed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "h3_internal.h"
+
+namespace h3 {
+
+namespace {
+
+constexpr float kLnEps = 1e-6f;
+constexpr float kRmsEps = 1e-6f;
+
+__device__ __forceinline__ float wave_sum(float v) {
+  // xor butterfly: lanes i and i^o add the same two values (commutative), so every lane ends
+  // with the identical total.
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(const uint4 &q, float *f) {
+  f[0] = bf_lo(q.x); f[1] = bf_hi(q.x); f[2] = bf_lo(q.y); f[3] = bf_hi(q.y);
+  f[4] = bf_lo(q.z); f[5] = bf_hi(q.z); f[6] = bf_lo(q.w); f[7] = bf_hi(q.w);
+}
+__device__ __forceinline__ uint4 pack8(const float *f) {
+  uint4 q;
+  q.x = pack_bf2(f[0], f[1]); q.y = pack_bf2(f[2], f[3]);
+  q.z = pack_bf2(f[4], f[5]); q.w = pack_bf2(f[6], f[7]);
+  return q;
+}
+__device__ __forceinline__ void load8f(const float *p, float *f) {
+  float4 a = reinterpret_cast<const float4 *>(p)[0];
+  float4 b = reinterpret_cast<const float4 *>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// ------------------------------------------------------------------ gate + AdaLN
+// GATE: x' = bf16(x + g*y) stored to x_out.  NORM: n = bf16((v - mean) * rstd * (1 + sc) + sh)
+// over the row v (= x' when GATE, else the row of x).  The fused variant (GATE && NORM)
+// normalises the bf16-rounded x' held in registers; the unfused pair writes x' and reads it
+// back.  Both run the identical NORM code below (same lane mapping, order and operations),
+// so their outputs are bit-identical.
+template <int VPL, bool GATE, bool NORM>
+__global__ __launch_bounds__(256) void gate_adaln_kernel(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ y, const float *__restrict__ gate,
+    bf16_t *x_out, const float *__restrict__ shift, const float *__restrict__ scale,
+    bf16_t *__restrict__ n_out, int rows, int d) {
+#pragma clang fp contract(off)
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const size_t base = static_cast<size_t>(row) * d;
+  float v[VPL][8];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = (i * 64 + lane) * 8;
+    uint4 xv = *reinterpret_cast<const uint4 *>(x + base + e);
+    unpack8(xv, v[i]);
+    if constexpr (GATE) {
+      float yv[8], gv[8];
+      unpack8(*reinterpret_cast<const uint4 *>(y + base + e), yv);
+      load8f(gate + e, gv);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[i][k] = bf2f(f2bf(v[i][k] + gv[k] * yv[k]));
+      *reinterpret_cast<uint4 *>(x_out + base + e) = pack8(v[i]);
+    }
+  }
+  if constexpr (NORM) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s += v[i][k];
+    s = wave_sum(s);
+    const float mean = s / static_cast<float>(d);
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float c = v[i][k] - mean;
+        q += c * c;
+      }
+    q = wave_sum(q);
+    const float rstd = 1.0f / sqrtf(q / static_cast<float>(d) + kLnEps);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = (i * 64 + lane) * 8;
+      float sh[8], sc[8], o[8];
+      load8f(shift + e, sh);
+      load8f(scale + e, sc);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = ((v[i][k] - mean) * rstd) * (1.0f + sc[k]) + sh[k];
+      *reinterpret_cast<uint4 *>(n_out + base + e) = pack8(o);
+    }
+  }
+}
+
+template <bool GATE, bool NORM>
+void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
+                         const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
+                         hipStream_t s) {
+  dim3 grid((rows + 3) / 4), block(256);
+  switch (d / 512) {
+#define H3_CASE(V)                                                                      \
+  case V:                                                                               \
+    gate_adaln_kernel<V, GATE, NORM><<<grid, block, 0, s>>>(x, y, gate, x_out, shift, scale, \
+                                                            n_out, rows, d);           \
+    break;
+    H3_CASE(1) H3_CASE(2) H3_CASE(3) H3_CASE(4) H3_CASE(5) H3_CASE(6) H3_CASE(8) H3_CASE(10)
+    H3_CASE(12) H3_CASE(16)
+#undef H3_CASE
+    default: break;
+  }
+}
+
+// ------------------------------------------------------------------ RoPE table
+// table[n * (D/2) + p] = (cos, sin) of coord_axis(n) * 10000^(-2 j / D_axis) for pair p, where
+// the head splits into [t | h | w] slices of D - 4 floor(D/6), 2 floor(D/6), 2 floor(D/6)
+// channels and j is the pair index inside its slice.  Computed in double.
+__global__ void rope_table_kernel(float2 *table, int n_tokens, int half, int pairs_t,
+                                  int pairs_h, int gh, int gw, int paired, float sscale) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n_tokens * half) return;
+  const int n = idx / half, p = idx - n * half;
+  double f, h, w;
+  if (!paired) {
+    w = n % gw;
+    h = (n / gw) % gh;
+    f = n / (gw * gh);
+  } else {
+    const int wr = (gw + 1) / 2;
+    const int c = n % wr;
+    h = (n / wr) % gh;
+    f = n / (wr * gh);
+    const int w0 = 2 * c, w1 = (2 * c + 1 < gw) ? 2 * c + 1 : 2 * c;
+    w = 0.5 * (w0 + w1);
+  }
+  h *= sscale;
+  w *= sscale;
+  double coord;
+  int j, da;
+  if (p < pairs_t) {
+    coord = f; j = p; da = 2 * pairs_t;
+  } else if (p < pairs_t + pairs_h) {
+    coord = h; j = p - pairs_t; da = 2 * pairs_h;
+  } else {
+    coord = w; j = p - pairs_t - pairs_h; da = 2 * pairs_h;
+  }
+  const double ang = coord * pow(10000.0, -2.0 * j / da);
+  table[idx] = make_float2(static_cast<float>(cos(ang)), static_cast<float>(sin(ang)));
+}
+
+// ------------------------------------------------------------------ Q/K RMSNorm + RoPE
+// One wave per token.  The [q | k] span (2d channels at the start of the qkvq row) is walked
+// in 512-channel chunks; each lane owns 8 consecutive channels = 4 rotation pairs, so a head
+// of D channels lives on D/8 adjacent lanes and its RMS is a butterfly over those lanes.
+template <int D>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(
+    bf16_t *qkvq, int64_t ld, int n_tokens, int d, const bf16_t *__restrict__ q_gamma,
+    const bf16_t *__restrict__ k_gamma, int qk_norm, const float2 *__restrict__ table) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_tokens) return;
+  bf16_t *rp = qkvq + static_cast<size_t>(row) * ld;
+  const float2 *tr = table + static_cast<size_t>(row) * (D / 2);
+  const int chunks = (2 * d) / 512;
+  const int pos = (lane * 8) % D;  // channel offset inside the head
+  for (int c = 0; c < chunks; ++c) {
+    const int e = c * 512 + lane * 8;
+    float a[8];
+    unpack8(*reinterpret_cast<const uint4 *>(rp + e), a);
+    if (qk_norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ss += a[k] * a[k];
+#pragma unroll
+      for (int o = 1; o < D / 8; o <<= 1) ss += __shfl_xor(ss, o);
+      const float r = 1.0f / sqrtf(ss / static_cast<float>(D) + kRmsEps);
+      const bf16_t *gp = (e < d ? q_gamma : k_gamma) + pos;
+      uint4 gq = *reinterpret_cast<const uint4 *>(gp);
+      float g[8];
+      unpack8(gq, g);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a[k] = a[k] * r * g[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 cs = tr[pos / 2 + k];
+      const float x0 = a[2 * k], x1 = a[2 * k + 1];
+      a[2 * k] = x0 * cs.x - x1 * cs.y;
+      a[2 * k + 1] = x0 * cs.y + x1 * cs.x;
+    }
+    *reinterpret_cast<uint4 *>(rp + e) = pack8(a);
+  }
+}
+
+// ------------------------------------------------------------------ token pairing
+// One thread per (reduced token, 8-channel vector).  The pair of reduced token j in row
+// (f, h) is (row*gw + 2c, row*gw + min(2c+1, gw-1)) with c = j % ceil(gw/2).
+__device__ __forceinline__ void pair_of(int j, int gw, int &p0, int &p1) {
+  const int wr = (gw + 1) / 2;
+  const int row = j / wr, c = j - row * wr;
+  p0 = row * gw + 2 * c;
+  p1 = (2 * c + 1 < gw) ? p0 + 1 : p0;
+}
+
+__global__ void token_merge_kernel(const bf16_t *__restrict__ src, bf16_t *__restrict__ dst,
+                                   int n_red, int gw, int d) {
+  const int vecs = d / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(n_red) * vecs) return;
+  const int j = static_cast<int>(idx / vecs), v = static_cast<int>(idx - static_cast<int64_t>(j) * vecs);
+  int p0, p1;
+  pair_of(j, gw, p0, p1);
+  float a[8], b[8], o[8];
+  unpack8(*reinterpret_cast<const uint4 *>(src + static_cast<size_t>(p0) * d + v * 8), a);
+  unpack8(*reinterpret_cast<const uint4 *>(src + static_cast<size_t>(p1) * d + v * 8), b);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = (a[k] + b[k]) * 0.5f;
+  *reinterpret_cast<uint4 *>(dst + static_cast<size_t>(j) * d + v * 8) = pack8(o);
+}
+
+// dst may equal bypass: each thread reads both pair members before writing them and pairs
+// are disjoint.
+__global__ void token_restore_kernel(const bf16_t *__restrict__ xr, const bf16_t *bypass,
+                                     bf16_t *dst, int n_red, int gw, int d) {
+#pragma clang fp contract(off)
+  const int vecs = d / 8;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(n_red) * vecs) return;
+  const int j = static_cast<int>(idx / vecs), v = static_cast<int>(idx - static_cast<int64_t>(j) * vecs);
+  int p0, p1;
+  pair_of(j, gw, p0, p1);
+  float a[8], b[8], r[8], o0[8], o1[8];
+  unpack8(*reinterpret_cast<const uint4 *>(bypass + static_cast<size_t>(p0) * d + v * 8), a);
+  unpack8(*reinterpret_cast<const uint4 *>(bypass + static_cast<size_t>(p1) * d + v * 8), b);
+  unpack8(*reinterpret_cast<const uint4 *>(xr + static_cast<size_t>(j) * d + v * 8), r);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float m0 = bf2f(f2bf((a[k] + b[k]) * 0.5f));  // the merge value exactly as stored
+    const float delta = r[k] - m0;
+    o0[k] = a[k] + delta;
+    o1[k] = b[k] + delta;
+  }
+  *reinterpret_cast<uint4 *>(dst + static_cast<size_t>(p0) * d + v * 8) = pack8(o0);
+  if (p1 != p0) *reinterpret_cast<uint4 *>(dst + static_cast<size_t>(p1) * d + v * 8) = pack8(o1);
+}
+
+// ------------------------------------------------------------------ Euler
+__global__ void euler_kernel(float *__restrict__ x, const float *__restrict__ v, float dt,
+                             int64_t n) {
+#pragma clang fp contract(off)
+  const int64_t i4 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i4 + 3 < n) {
+    float4 a = *reinterpret_cast<float4 *>(x + i4);
+    const float4 b = *reinterpret_cast<const float4 *>(v + i4);
+    a.x = a.x + dt * b.x; a.y = a.y + dt * b.y; a.z = a.z + dt * b.z; a.w = a.w + dt * b.w;
+    *reinterpret_cast<float4 *>(x + i4) = a;
+  } else {
+    for (int64_t i = i4; i < n; ++i) x[i] = x[i] + dt * v[i];
+  }
+}
+
+// ------------------------------------------------------------------ int8 row quantisation
+// One wave per row.  Per group of `group` channels: s = absmax / 127 (IEEE float32 division),
+// q = clamp(rint(x / s), -127, 127) with ties to even; s == 0 gives q = 0.  With
+// group == 1024 a group is two 8-channel vectors per lane and stays in registers; with one
+// group per row the row is read twice (the second read hits the cache).
+__device__ __forceinline__ uint32_t quant4(const float *x, float s) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int q = 0;
+    if (s > 0.f) {
+      float t = rintf(x[k] / s);
+      t = fminf(fmaxf(t, -127.f), 127.f);
+      q = static_cast<int>(t);
+    }
+    w |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * k);
+  }
+  return w;
+}
+
+__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t *__restrict__ X,
+                                                         int8_t *__restrict__ Q,
+                                                         float *__restrict__ S, int rows,
+                                                         int K, int group) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const bf16_t *xr = X + static_cast<size_t>(row) * K;
+  int8_t *qr = Q + static_cast<size_t>(row) * K;
+  if (group == 1024) {
+    const int ng = K / 1024;
+    for (int g = 0; g < ng; ++g) {
+      float a[16];
+      const int e0 = g * 1024 + lane * 8, e1 = e0 + 512;
+      unpack8(*reinterpret_cast<const uint4 *>(xr + e0), a);
+      unpack8(*reinterpret_cast<const uint4 *>(xr + e1), a + 8);
+      float m = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(a[k]));
+      m = wave_max(m);
+      const float s = m / 127.0f;
+      uint2 w0, w1;
+      w0.x = quant4(a, s); w0.y = quant4(a + 4, s);
+      w1.x = quant4(a + 8, s); w1.y = quant4(a + 12, s);
+      *reinterpret_cast<uint2 *>(qr + e0) = w0;
+      *reinterpret_cast<uint2 *>(qr + e1) = w1;
+      if (lane == 0) S[static_cast<size_t>(row) * ng + g] = s;
+    }
+  } else {
+    float m = 0.f;
+    for (int e = lane * 8; e < K; e += 512) {
+      float a[8];
+      unpack8(*reinterpret_cast<const uint4 *>(xr + e), a);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(a[k]));
+    }
+    m = wave_max(m);
+    const float s = m / 127.0f;
+    for (int e = lane * 8; e < K; e += 512) {
+      float a[8];
+      unpack8(*reinterpret_cast<const uint4 *>(xr + e), a);
+      uint2 w;
+      w.x = quant4(a, s);
+      w.y = quant4(a + 4, s);
+      *reinterpret_cast<uint2 *>(qr + e) = w;
+    }
+    if (lane == 0) S[row] = s;
+  }
+}
+
+// ------------------------------------------------------------------ small kernels
+__global__ void f32_to_bf16_kernel(const float *__restrict__ src, bf16_t *__restrict__ dst,
+                                   int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = static_cast<bf16_t>(f2bf(src[i]));
+}
+
+// e = [cos(t w_j) | sin(t w_j)], j < 128, t = 1000 sigma, w_j = 10000^(-j/128), in double.
+__global__ void sinusoid_kernel(float sigma, float *e) {
+  const int j = threadIdx.x;
+  if (j >= 128) return;
+  const double t = 1000.0 * static_cast<double>(sigma);
+  const double w = pow(10000.0, -static_cast<double>(j) / 128.0);
+  e[j] = static_cast<float>(cos(t * w));
+  e[128 + j] = static_cast<float>(sin(t * w));
+}
+
+// One wave per output row; float32 accumulation.
+__global__ __launch_bounds__(256) void gemv_kernel(const bf16_t *__restrict__ W,
+                                                   const float *__restrict__ x,
+                                                   const bf16_t *__restrict__ b,
+                                                   const bf16_t *__restrict__ add,
+                                                   float *__restrict__ y, int rows, int K,
+                                                   int act) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const bf16_t *wr = W + static_cast<size_t>(r) * K;
+  float acc = 0.f;
+  for (int e = lane * 8; e < K; e += 512) {
+    float w[8], xv[8];
+    unpack8(*reinterpret_cast<const uint4 *>(wr + e), w);
+    load8f(x + e, xv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += w[k] * xv[k];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    float v = acc + (b ? bf2f(b[r]) : 0.f);
+    if (act == 1) v = v / (1.0f + expf(-v));
+    if (add) v += bf2f(add[r]);
+    y[r] = v;
+  }
+}
+
+__global__ void add_table_kernel(const float *__restrict__ Mv, const bf16_t *__restrict__ T,
+                                 float *__restrict__ out, int nb, int width) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(nb) * width) return;
+  out[i] = Mv[i % width] + bf2f(T[i]);
+}
+
+}  // namespace
+
+void launch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
+                       const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
+                       hipStream_t s) {
+  if (rows <= 0) return;
+  if (y && n_out)
+    dispatch_gate_adaln<true, true>(x, y, gate, x_out, shift, scale, n_out, rows, d, s);
+  else if (y)
+    dispatch_gate_adaln<true, false>(x, y, gate, x_out, shift, scale, n_out, rows, d, s);
+  else
+    dispatch_gate_adaln<false, true>(x, y, gate, x_out, shift, scale, n_out, rows, d, s);
+}
+
+void launch_rope_table(float2 *table, const h3_geom &geom, int n_tokens, int head_dim,
+                       hipStream_t s) {
+  const int half = head_dim / 2;
+  const int hw = 2 * (head_dim / 6);
+  const int pairs_h = hw / 2, pairs_t = (head_dim - 2 * hw) / 2;
+  const int total = n_tokens * half;
+  rope_table_kernel<<<(total + 255) / 256, 256, 0, s>>>(table, n_tokens, half, pairs_t, pairs_h,
+                                                        geom.grid_h, geom.grid_w, geom.paired,
+                                                        geom.rope_spatial_scale);
+}
+
+void launch_qk_norm_rope(bf16_t *qkvq, int64_t ld, int n_tokens, int d, int head_dim,
+                         const bf16_t *q_gamma, const bf16_t *k_gamma, int qk_norm,
+                         const float2 *table, hipStream_t s) {
+  dim3 grid((n_tokens + 3) / 4), block(256);
+  if (head_dim == 128)
+    qk_norm_rope_kernel<128><<<grid, block, 0, s>>>(qkvq, ld, n_tokens, d, q_gamma, k_gamma,
+                                                     qk_norm, table);
+  else
+    qk_norm_rope_kernel<64><<<grid, block, 0, s>>>(qkvq, ld, n_tokens, d, q_gamma, k_gamma,
+                                                    qk_norm, table);
+}
+
+void launch_token_reduce(int direction, const h3_geom &geom, int d, const bf16_t *src,
+                         const bf16_t *bypass, bf16_t *dst, hipStream_t s) {
+  const int n_red = geom.f_lat * geom.grid_h * ((geom.grid_w + 1) / 2);
+  const int64_t total = static_cast<int64_t>(n_red) * (d / 8);
+  const int blocks = static_cast<int>((total + 255) / 256);
+  if (direction == 0)
+    token_merge_kernel<<<blocks, 256, 0, s>>>(src, dst, n_red, geom.grid_w, d);
+  else
+    token_restore_kernel<<<blocks, 256, 0, s>>>(src, bypass, dst, n_red, geom.grid_w, d);
+}
+
+void launch_euler(float *x, const float *v, float dt, int64_t n, hipStream_t s) {
+  const int64_t threads = (n + 3) / 4;
+  euler_kernel<<<static_cast<int>((threads + 255) / 256), 256, 0, s>>>(x, v, dt, n);
+}
+
+void launch_quant_rows(const bf16_t *X, int8_t *Q, float *S, int rows, int K, int group,
+                       hipStream_t s) {
+  quant_rows_kernel<<<(rows + 3) / 4, 256, 0, s>>>(X, Q, S, rows, K, group);
+}
+
+void launch_f32_to_bf16(const float *src, bf16_t *dst, int64_t n, hipStream_t s) {
+  f32_to_bf16_kernel<<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(src, dst, n);
+}
+
+void launch_timestep_sinusoid(float sigma, float *e, hipStream_t s) {
+  sinusoid_kernel<<<1, 128, 0, s>>>(sigma, e);
+}
+
+void launch_gemv(const bf16_t *W, const float *x, const bf16_t *b, const bf16_t *add, float *y,
+                 int rows, int K, int act, hipStream_t s) {
+  gemv_kernel<<<(rows + 3) / 4, 256, 0, s>>>(W, x, b, add, y, rows, K, act);
+}
+
+void launch_add_table(const float *Mv, const bf16_t *T, float *out, int nb, int width,
+                      hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(nb) * width;
+  add_table_kernel<<<static_cast<int>((total + 255) / 256), 256, 0, s>>>(Mv, T, out, nb, width);
+}
+
+}  // namespace h3
