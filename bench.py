@@ -1,0 +1,172 @@
+"""Benchmark of the DiT denoiser hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 512sq_22f] [--no-cpu]
+
+One step = one denoise transition of the --steps 4 --reuse 1 schedule at 512x512x22 frames
+(1536 tokens, 50 blocks): a fresh DiT evaluation (modulation, patch, 50 blocks, final
+AdaLN + head) followed by the Euler update; steps walk the 4-step sigma grid cyclically.
+The model (bf16 weights, 15 GB) and the latent are resident in HBM before timing starts.
+
+Prints one JSON line: tokens*blocks/s over the K timed steps, ms per denoise step, the
+roofline of the dominant kernel (FC1 GEMM: its launches are timed with HIP events on the
+launch stream during the timed steps; its algorithmic FLOPs per launch = 2 N d F), and the
+oracle's throughput on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="512sq_22f")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def traffic_for(kernel_src: str):
+    """HBM bytes per launch from the committed counter summary, if taken on this source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = open(os.path.join(ROOT, "video_diffusion_transformer_fwd_amd", "csrc", kernel_src), "rb").read()
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """Oracle (float64 NumPy) on a bounded sample: whole blocks of one fresh evaluation."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import dit
+    from video_diffusion_transformer_fwd_amd import synthetic as S
+    from video_diffusion_transformer_fwd_amd.runtime import Geometry
+
+    geo = Geometry(w)
+    to64 = lambda t: t.to("cpu").double().numpy()
+    g = {k: to64(v) for k, v in S.global_weights(w).items()}
+    ctx = to64(S.context(w))
+    mod, _ = dit.modulation(g, 1.0)
+    coords = dit.rope_coords(geo.f_lat, geo.grid_h, geo.grid_w, geo.scale)
+    x = dit.patch_embed(to64(S.latent(w, geo.n_tokens)), g)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    done, t_used = 0, 0.0
+    while done < w.n_blocks:
+        blk = {k: to64(v) for k, v in S.block_weights(w, done).items()}
+        t0 = time.perf_counter()
+        x = dit.block_forward(x, blk, mod[done], ctx, coords, w.n_heads)
+        t_used += time.perf_counter() - t0
+        done += 1
+        if t_used >= budget_s:
+            break
+    return {"value": geo.n_tokens * done / t_used, "unit": "tokens*blocks/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of the {w.n_blocks} blocks of one fresh evaluation at "
+                      f"{w.name} ({geo.n_tokens} tokens), float64 NumPy, {t_used:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus N > 1 is not "
+                                   "supported (the multi-GPU sequence split is a design note)"}))
+        sys.exit(2)
+    import torch
+    from video_diffusion_transformer_fwd_amd import binding as B
+    from video_diffusion_transformer_fwd_amd import synthetic as S
+    from video_diffusion_transformer_fwd_amd.runtime import DiTModel
+
+    w = S.WORKLOADS[args.workload]
+    t0 = time.time()
+    model = DiTModel(w)
+    print(f"# model resident in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    geo = model.geo
+    n, nb_act = geo.n_tokens, w.n_active
+    active = model.active()
+    opts = model.opts()
+    sig, fresh, n_fresh = B.h3_schedule(w.steps, w.reuse, 1)
+    lat = model.initial_latent()
+    v = torch.empty((n, w.latent_ch), dtype=torch.float32, device=model.device)
+    ev_count = [0]
+
+    def step(k):
+        i = k % w.steps
+        if fresh[i]:
+            model.forward(lat, float(sig[i]), active, ev_count[0] % max(n_fresh, 1), opts, v)
+            ev_count[0] += 1
+        B.h3_euler_step(lat, v, float(sig[i]), float(sig[i + 1]))
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    fresh_before = ev_count[0]
+    B.h3_profile_begin(["fc1_gemm"], max_launches=args.steps * nb_act + 16)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.warmup, args.warmup + args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    prof = B.h3_profile_end()
+    n_evals = ev_count[0] - fresh_before
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tok_blocks = n * nb_act * n_evals / elapsed
+    fc1_ms, fc1_launches = prof.get("fc1_gemm", (0.0, 0))
+    fc1_avg_ms = fc1_ms / max(fc1_launches, 1)
+    fc1_flops = 2.0 * n * w.d_model * w.ffn_dim
+    achieved = fc1_flops / (fc1_avg_ms * 1e-3) / 1e12 if fc1_launches else 0.0
+    fwd_flops = nb_act * (2 * n * w.d_model * 4 * w.d_model + 4 * n * n * w.d_model
+                          + 4 * n * w.ctx_len * w.d_model + 4 * n * w.d_model * w.d_model
+                          + 4 * n * w.d_model * w.ffn_dim)
+    out = {
+        "metric": "DiT denoise-step ms & tokens·blocks/s at 512²×22f; % bf16 MFMA peak",
+        "value": round(tok_blocks, 1),
+        "unit": "tokens·blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) latent)",
+        "config": {"workload": w.name, "width": w.width, "height": w.height, "frames": w.frames,
+                   "tokens": n, "blocks": nb_act, "d_model": w.d_model, "heads": w.n_heads,
+                   "ffn": w.ffn_dim, "ctx_len": w.ctx_len, "steps": w.steps, "reuse": w.reuse,
+                   "fc2": w.fc2_mode, "token_reduction": w.token_reduction},
+        "ms_per_fresh_eval": round(elapsed * 1e3 / max(n_evals, 1), 3),
+        "mfma_frac_forward": round(fwd_flops * n_evals / elapsed / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "fc1_gemm (bf16 GEMM + GELU epilogue)",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "flops_per_launch": fc1_flops, "avg_launch_ms": round(fc1_avg_ms, 5),
+                     "launches": fc1_launches, "traffic": traffic_for("k_gemm.hip")},
+    }
+    if not args.no_cpu:
+        del model
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,9 +4,11 @@ variants bit-identical.
 
 The oracle receives the same seeded inputs (weights, residual x, text context) and the
 modulation it computes itself; the GPU receives that modulation as float32.  Bars: the
-block output and the block delta (out - in) within rel-L2 2e-2 of the oracle, and so are
-the two branch outputs y (attention) and m (MLP) read back from the workspace, because the
-residual would otherwise hide branch errors.
+block output within rel-L2 2e-2 of the oracle; the block delta (out - in) within 2e-2 of
+its norm plus the bf16 rounding floor of the stored output; and, because the residual would
+otherwise hide branch errors, the two branch outputs y (attention) and m (MLP), q after
+RMSNorm + RoPE and both attention outputs, read back from the workspace, each within
+rel-L2 2e-2.
 """
 import dataclasses
 
@@ -68,7 +70,11 @@ def test_block_parity(name, fc2_mode):
         got = f64(x)
         tag = f"{name} {fc2_mode} block {b}"
         assert_close(got, ref, rel=2e-2, elem=6e-2, what=f"{tag} out")
-        assert rel_l2(got - f64(x0), ref - f64(x0)) < 2e-2, f"{tag} delta"
+        # block delta: the stored output is bf16, whose rounding (at most 2^-8 relative per
+        # element) is a floor under any comparison of a delta that is small next to x
+        dx, dref = got - f64(x0), ref - f64(x0)
+        err = np.linalg.norm(dx - dref)
+        assert err <= 2e-2 * np.linalg.norm(dref) + 2.0 ** -8 * np.linalg.norm(ref), f"{tag} delta"
         y = f64(ws_view(ws, lay.y, (n, d)))
         m = f64(ws_view(ws, lay.m, (n, d)))
         assert rel_l2(y, tr["y"]) < 2e-2, f"{tag} attention branch {rel_l2(y, tr['y'])}"
