@@ -31,6 +31,9 @@ def sync():
     (77, 200, 64, 0, 1, 0),         # ragged N, one K slice, float32 out
     (1, 128, 128, 0, 1, 0),         # single row
     (129, 12288, 512, 1, 0, 0),     # wide N (FC1 / QKV widths)
+    (1000, 700, 256, 1, 0, 1),      # 192x192 tiles with ragged M and N
+    (4100, 2304, 256, 0, 0, 0),     # 256x256 tiles, ragged M
+    (4100, 2100, 128, 1, 0, 0),     # 256x256 tiles, ragged M and N, GELU
 ])
 def test_gemm_bf16(M, N, K, epi, f32, two_bias):
     rng = np.random.default_rng(M * 7 + N * 3 + K)

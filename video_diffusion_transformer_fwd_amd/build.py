@@ -29,7 +29,8 @@ COMMON = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
 ]
 
-SOURCES = ["h3_host.cpp", "h3_api.cpp", "h3_profile.cpp", "k_rowwise.hip", "k_gemm.hip", "k_attn.hip"]
+SOURCES = ["h3_host.cpp", "h3_api.cpp", "h3_profile.cpp", "k_rowwise.hip", "k_gemm.hip", "k_gemm_i8.hip",
+           "k_attn.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -1,23 +1,35 @@
-// Dense products of the block on the gfx950 matrix cores.
+// bf16 products of the block on the gfx950 matrix cores:
+// C[M,N] = A[M,K] B[N,K]^T (+ bias) (+ bias2) (+ exact GELU), v_mfma_f32_32x32x16_bf16,
+// float32 accumulation, bf16 or float32 output.
 //
-// bf16: C[M,N] = A[M,K] B[N,K]^T (+ bias) (+ GELU), v_mfma_f32_32x32x16_bf16, float32
-// accumulation.  int8: per-group int32 sums with v_mfma_i32_32x32x32_i8 and a float32
-// dequantisation epilogue.
+// Tiling: a workgroup of WM x WN wave64s owns a BM x BN output tile (each wave a
+// (BM/WM) x (BN/WN) block of 32x32 MFMA tiles) and walks K in BK = 64 slices.  Both operands
+// are K-contiguous, so A and B tiles are staged identically: 16-byte global loads (8
+// consecutive lanes cover one 128-byte row slice) into registers, then into LDS; LDS is
+// double-buffered with one barrier per K slice, the next slice's global loads in flight while
+// the current slice feeds the MFMAs.
 //
-// Tiling: a 256-thread workgroup (4 wave64s, WM x WN) owns a BM x BN output tile and walks K in
-// BK slices.  Both operands are K-contiguous, so A and B tiles are staged identically:
-// 16-byte global loads (8 consecutive lanes cover one 128-byte row slice), registers, then a
-// padded LDS tile (row stride BK + 16 bytes, which keeps the 16-byte MFMA-operand reads of 8
-// consecutive rows on distinct banks).  LDS is double-buffered with one barrier per K slice:
-// the next slice's global loads are in flight while the current slice feeds the MFMAs.
+// LDS rows are 64 bf16 = 128 bytes = 8 chunks of 16 bytes, stored without padding: chunk c of
+// row r sits at slot c ^ (r & 7).  The MFMA-operand reads (16 bytes per lane, 8 consecutive
+// rows at one chunk) then hit 8 distinct bank groups.
 //
 // Operand layouts (32x32x16 bf16): lane l supplies A[m = l%32][k = 8(l/32) .. +7] and
 // B[n = l%32][k = 8(l/32) .. +7]; accumulator register i of lane l is
-// C[8(i/4) + 4(l/32) + i%4][l%32].  (i8 32x32x32: 16 consecutive k per lane, k = 16(l/32).)
+// C[8(i/4) + 4(l/32) + i%4][l%32].
 //
-// Workgroup order is XCD-aware: consecutive workgroup ids land on different XCDs, so ids are
-// regrouped so that each XCD walks a contiguous band of tiles, and tiles are visited in
-// groups of GROUP_M tile-rows so neighbours share A rows and B columns in that XCD's L2.
+// Tile shapes are chosen per problem: the 1536-token workload uses 192x192 tiles (4 waves of
+// 96x96, three LDS stages), which fill whole rounds of the 256 CUs (8 x 64 = 512 tiles at
+// N = 12288; 8 x 16 = 128 tiles x 2 K halves at N = 3072 with split-K); large M uses 256x256
+// tiles with 8 waves of 128x64 (two waves per SIMD, two LDS stages).
+//
+// Split-K (two K halves per tile): each half stores its float32 partial tile, fences, and bumps
+// the tile's arrival counter; the second to arrive adds the other half's partial to its own
+// (a + b == b + a in IEEE arithmetic, so the result does not depend on which arrives first),
+// runs the epilogue and resets the counter to zero.  No workgroup waits for another.
+//
+// Workgroup order is XCD-aware: consecutive hardware ids land on different XCDs, so ids are
+// regrouped so that each XCD walks a contiguous band of tiles, visited in groups of 8 tile
+// rows so neighbours share A rows and B columns in that XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include "h3_internal.h"
@@ -28,101 +40,131 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-typedef __attribute__((ext_vector_type(4))) int i32x4_t;
-typedef __attribute__((ext_vector_type(16))) int i32x16_t;
 
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
-
-// Maps the hardware workgroup id to a (tile_m, tile_n) pair.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn) {
-  const int nwg = tiles_m * tiles_n;
-  int id = blockIdx.x;
-  // regroup: hardware id -> XCD-contiguous id (only when the grid divides evenly)
-  if (nwg % kXcds == 0) {
-    const int per = nwg / kXcds;
-    id = (id % kXcds) * per + id / kXcds;
-  }
-  const int in_group = kGroupM * tiles_n;
-  const int group = id / in_group;
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int r = id - group * in_group;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
 
 __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
 }
 
-// ------------------------------------------------------------------------ bf16 GEMM
-template <int BM, int BN, int WM, int WN>
+// LDS holds 64 banks of 4 bytes; a 16-byte-per-lane read is served 16 lanes per cycle.  Tile
+// rows are 128 bytes, so two rows share one 256-byte bank line: chunk c of row r is stored in
+// slot c ^ ((r >> 1) & 7), which puts the 16 rows an MFMA-operand read touches at one chunk
+// on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations are outstanding
+// (expcnt and lgkmcnt left unconstrained): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
+
+// Waits for this thread's direct-to-LDS loads down to `VM` outstanding, then meets the other
+// waves at a barrier; afterwards every wave sees the LDS bytes those loads wrote.
+template <int VM>
+__device__ __forceinline__ void lds_dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int BM, int BN, int WM, int WN, int NS = 2>
 struct GemmCfg {
+  static constexpr int NT = 64 * WM * WN;
   static constexpr int BK = 64;
-  static constexpr int LDS_STRIDE = BK + 8;  // elements
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
-  static constexpr int A_CHUNKS = BM * BK / 8 / 256;  // 16-byte chunks per thread
-  static constexpr int B_CHUNKS = BN * BK / 8 / 256;
-  static constexpr int LDS_A = BM * LDS_STRIDE;
-  static constexpr int LDS_B = BN * LDS_STRIDE;
-  static constexpr size_t LDS_BYTES = 2 * (LDS_A + LDS_B) * sizeof(bf16_t);
+  static constexpr int A_CHUNKS = BM * 8 / NT;  // 16-byte chunks per thread
+  static constexpr int B_CHUNKS = BN * 8 / NT;
+  static constexpr int STAGE = (BM + BN) * 128;  // bytes
+  static constexpr size_t LDS_BYTES = NS * static_cast<size_t>(STAGE);
+  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile rows must split evenly over threads");
+  static_assert(TM >= 1 && TN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0,
+                "wave tile must be whole 32x32 blocks");
 };
 
-template <int BM, int BN, int WM, int WN, int EPI, int OUT_F32>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(
-    const bf16_t *__restrict__ A, int64_t lda, const bf16_t *__restrict__ B, int64_t ldb,
-    void *__restrict__ C, int64_t ldc, int M, int N, int K, const bf16_t *__restrict__ bias,
-    const bf16_t *__restrict__ bias2) {
-  using Cfg = GemmCfg<BM, BN, WM, WN>;
-  constexpr int BK = Cfg::BK, LS = Cfg::LDS_STRIDE, TM = Cfg::TM, TN = Cfg::TN;
-  extern __shared__ __align__(16) bf16_t smem[];
-  bf16_t *As = smem;                    // [2][BM][LS]
-  bf16_t *Bs = smem + 2 * Cfg::LDS_A;   // [2][BN][LS]
+struct GemmArgs {
+  const bf16_t *A;
+  int64_t lda;
+  const bf16_t *B;
+  int64_t ldb;
+  void *C;
+  int64_t ldc;
+  int M, N, K;
+  const bf16_t *bias, *bias2;
+  float *part;    // split-K partial tiles
+  int *counters;  // split-K arrival counters, zero between launches
+};
 
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
+  using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
+  constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int ticket;
+
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int tile_id = blockIdx.x / SPLIT;
+  const int split = blockIdx.x % SPLIT;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  {
+    const int ntiles = tiles_m * tiles_n;
+    int id = tile_id;
+    if (ntiles % kXcds == 0) {
+      const int per = ntiles / kXcds;
+      id = (id % kXcds) * per + id / kXcds;
+    }
+    const int in_group = kGroupM * tiles_n;
+    const int group = id / in_group;
+    const int first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int r = id - group * in_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
+  const int kc = g.K / SPLIT, kbeg = split * kc;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // global -> register staging coordinates: chunk c covers row (tid/8 + c*32), col (tid%8)*8
-  const int ld_row = tid >> 3, ld_col = (tid & 7) * 8;
-  const bf16_t *a_src[Cfg::A_CHUNKS];
-  const bf16_t *b_src[Cfg::B_CHUNKS];
+  // Staging: direct global -> LDS loads (global_load_lds_dwordx4).  One wave instruction fills
+  // 8 consecutive tile rows = 1 KiB of LDS, lane L landing at byte 16 L: row R = R0 + L/8, slot
+  // L%8, which holds chunk (L%8) ^ ((R >> 1) & 7) of that row.  Row blocks R0 = (i * NW + wave)
+  // * 8 walk the A rows then the B rows.
+  constexpr int NW = NT / 64;
+  constexpr int ROW_BLOCKS = (BM + BN) / 8;
+  constexpr int LOADS = ROW_BLOCKS / NW;  // load instructions per wave per K slice
+  static_assert(ROW_BLOCKS % NW == 0 && BM % 8 == 0, "row blocks must split evenly over waves");
+  const unsigned char *abase = reinterpret_cast<const unsigned char *>(g.A);
+  const unsigned char *bbase = reinterpret_cast<const unsigned char *>(g.B);
+  uint32_t goff[LOADS];
+  {
+    const int lrow = lane >> 3;
 #pragma unroll
-  for (int c = 0; c < Cfg::A_CHUNKS; ++c) {
-    int r = m0 + ld_row + c * 32;
-    r = r < M ? r : M - 1;
-    a_src[c] = A + static_cast<int64_t>(r) * lda + ld_col;
+    for (int i = 0; i < LOADS; ++i) {
+      const int R = (i * NW + wave) * 8 + lrow;
+      const int chunk = (lane & 7) ^ ((R >> 1) & 7);
+      if (R < BM) {
+        int r = m0 + R;
+        r = r < g.M ? r : g.M - 1;
+        goff[i] = static_cast<uint32_t>((static_cast<int64_t>(r) * g.lda + kbeg + chunk * 8) * 2);
+      } else {
+        int r = n0 + R - BM;
+        r = r < g.N ? r : g.N - 1;
+        goff[i] = static_cast<uint32_t>((static_cast<int64_t>(r) * g.ldb + kbeg + chunk * 8) * 2);
+      }
+    }
   }
+  auto issue_slice = [&](int stage, int kt) {
+    const uint32_t kb = static_cast<uint32_t>(kt * BK * 2);
+    unsigned char *st = smem + stage * Cfg::STAGE;
 #pragma unroll
-  for (int c = 0; c < Cfg::B_CHUNKS; ++c) {
-    int r = n0 + ld_row + c * 32;
-    r = r < N ? r : N - 1;
-    b_src[c] = B + static_cast<int64_t>(r) * ldb + ld_col;
-  }
-  uint4 ra[Cfg::A_CHUNKS], rb[Cfg::B_CHUNKS];
-
-  auto load_global = [&](int k0) {
-#pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c) ra[c] = *reinterpret_cast<const uint4 *>(a_src[c] + k0);
-#pragma unroll
-    for (int c = 0; c < Cfg::B_CHUNKS; ++c) rb[c] = *reinterpret_cast<const uint4 *>(b_src[c] + k0);
-  };
-  auto store_lds = [&](int buf) {
-    bf16_t *as = As + buf * Cfg::LDS_A;
-    bf16_t *bs = Bs + buf * Cfg::LDS_B;
-#pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c)
-      *reinterpret_cast<uint4 *>(as + (ld_row + c * 32) * LS + ld_col) = ra[c];
-#pragma unroll
-    for (int c = 0; c < Cfg::B_CHUNKS; ++c)
-      *reinterpret_cast<uint4 *>(bs + (ld_row + c * 32) * LS + ld_col) = rb[c];
+    for (int i = 0; i < LOADS; ++i) {
+      const int R0 = (i * NW + wave) * 8;
+      const unsigned char *src = (R0 < BM ? abase : bbase) + (goff[i] + kb);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(st + R0 * 128), 16, 0, 0);
+    }
   };
 
   f32x16_t acc[TM][TN];
@@ -131,69 +173,133 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
 
-  const int KT = K / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
+  const int fr = lane & 31, fh = lane >> 5;
+  int a_row[TM], b_row[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row[i] = (wm * TM + i) * 32 + fr;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_row[j] = (wn * TN + j) * 32 + fr;
 
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 8;
+  // NS-stage pipeline: slices kt+1 .. kt+NS-1 stream into LDS while slice kt feeds the MFMAs.
+  const int KT = kc / BK;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < KT) issue_slice(p, p);
+  if (KT >= NS - 1)
+    lds_dma_barrier<LOADS * (NS - 2)>();
+  else
+    lds_dma_barrier<0>();
+
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_global((kt + 1) * BK);
-    const bf16_t *as = As + buf * Cfg::LDS_A + (wm * TM * 32 + frag_row) * LS + frag_k;
-    const bf16_t *bs = Bs + buf * Cfg::LDS_B + (wn * TN * 32 + frag_row) * LS + frag_k;
+    const unsigned char *st = smem + (kt % NS) * Cfg::STAGE;
+    const bool more = kt + NS - 1 < KT;
+    if (more) issue_slice((kt + NS - 1) % NS, kt + NS - 1);
+    bf16x8_t af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const bf16x8_t *>(st + swz(a_row[i], fh));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8_t *>(st + BM * 128 + swz(b_row[j], fh));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t af[TM], bfr[TN];
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 16) {
+        const int ch = 2 * (ks + 1) + fh;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t *>(as + i * 32 * LS + ks * 16);
+        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t *>(st + swz(a_row[i], ch));
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t *>(bs + j * 32 * LS + ks * 16);
+        for (int j = 0; j < TN; ++j)
+          bfr[cur ^ 1][j] = *reinterpret_cast<const bf16x8_t *>(st + BM * 128 + swz(b_row[j], ch));
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+      // interleave: one MFMA, one fragment read of the next step, ... so the reads are in flight
+      // while this step's MFMAs run
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int q = 0; q < TM + TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+      }
     }
-    if (kt + 1 < KT) store_lds(buf ^ 1);
-    __syncthreads();
+    // slice kt+1 must be complete (later slices may still be in flight); every wave must be
+    // done reading stage kt % NS before the next iteration refills it
+    if (more)
+      lds_dma_barrier<LOADS * (NS - 2)>();
+    else
+      lds_dma_barrier<0>();
   }
 
-  // epilogue
+  if constexpr (SPLIT == 2) {
+    // partial tile in register order: [tile][half][(i, j, quad)][thread] float4s
+    float4 *mine = reinterpret_cast<float4 *>(g.part) + (static_cast<int64_t>(tile_id) * 2 + split) * (BM * BN / 4);
+    const float4 *other = reinterpret_cast<const float4 *>(g.part) + (static_cast<int64_t>(tile_id) * 2 + (split ^ 1)) * (BM * BN / 4);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          mine[((i * TN + j) * 4 + r4) * NT + tid] =
+              make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) ticket = atomicAdd(g.counters + tile_id, 1);
+    __syncthreads();
+    if (ticket == 0) return;
+    __threadfence();
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 v = other[((i * TN + j) * 4 + r4) * NT + tid];
+          acc[i][j][4 * r4] += v.x;
+          acc[i][j][4 * r4 + 1] += v.y;
+          acc[i][j][4 * r4 + 2] += v.z;
+          acc[i][j][4 * r4 + 3] += v.w;
+        }
+    if (tid == 0) g.counters[tile_id] = 0;
+  }
+
+  // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 block
   const int col_l = lane & 31, row_l = (lane >> 5) * 4;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int n = n0 + (wn * TN + j) * 32 + col_l;
-    if (n >= N) continue;
+    if (n >= g.N) continue;
     float bsum = 0.f;
-    if (bias) bsum += bf2f(bias[n]);
-    if (bias2) bsum += bf2f(bias2[n]);
+    if (g.bias) bsum += bf2f(g.bias[n]);
+    if (g.bias2) bsum += bf2f(g.bias2[n]);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + (wm * TM + i) * 32 + (r / 4) * 8 + row_l + (r % 4);
-        if (m >= M) continue;
+        if (m >= g.M) continue;
         float v = acc[i][j][r] + bsum;
         if constexpr (EPI == H3_EPI_GELU) v = gelu_erf(v);
         if constexpr (OUT_F32)
-          reinterpret_cast<float *>(C)[static_cast<int64_t>(m) * ldc + n] = v;
+          reinterpret_cast<float *>(g.C)[static_cast<int64_t>(m) * g.ldc + n] = v;
         else
-          reinterpret_cast<bf16_t *>(C)[static_cast<int64_t>(m) * ldc + n] =
+          reinterpret_cast<bf16_t *>(g.C)[static_cast<int64_t>(m) * g.ldc + n] =
               static_cast<bf16_t>(f2bf(v));
       }
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int OUT_F32>
-void run_gemm(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, void *C, int64_t ldc,
-              int M, int N, int K, const bf16_t *bias, const bf16_t *bias2, hipStream_t s) {
-  using Cfg = GemmCfg<BM, BN, WM, WN>;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, EPI, OUT_F32>;
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT>
+void run_gemm(const GemmArgs &a, hipStream_t s) {
+  using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -201,193 +307,66 @@ void run_gemm(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, void *
                         static_cast<int>(Cfg::LDS_BYTES));
     attr_set = true;
   }
-  kern<<<tiles, 256, Cfg::LDS_BYTES, s>>>(A, lda, B, ldb, C, ldc, M, N, K, bias, bias2);
+  kern<<<tiles * SPLIT, Cfg::NT, Cfg::LDS_BYTES, s>>>(a);
 }
 
 template <int EPI, int OUT_F32>
-void gemm_select(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, void *C,
-                 int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
-                 hipStream_t s) {
-  run_gemm<128, 128, 2, 2, EPI, OUT_F32>(A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, s);
+void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
+  if (p.cfg == 2)
+    run_gemm<256, 256, 2, 4, 2, EPI, OUT_F32, 1>(a, s);
+  else if (p.cfg == 1 && p.split == 2)
+    run_gemm<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s);
+  else if (p.cfg == 1)
+    run_gemm<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s);
+  else
+    run_gemm<128, 128, 2, 2, 3, EPI, OUT_F32, 1>(a, s);
 }
 
-// ------------------------------------------------------------------------ int8 GEMM
-// Same structure with int8 operands: BK = 128 bytes, 32x32x32 i8 MFMA.  acc holds the int32
-// sum of the current K group; at each group end it is folded into the float32 total as
-// tot = tot + float(acc) * SA[m, g] (two rounded operations, no fused multiply-add).
-template <int BM, int BN, int WM, int WN>
-struct GemmI8Cfg {
-  static constexpr int BK = 128;
-  static constexpr int LDS_STRIDE = BK + 16;  // bytes
-  static constexpr int TM = BM / WM / 32;
-  static constexpr int TN = BN / WN / 32;
-  static constexpr int A_CHUNKS = BM * BK / 16 / 256;
-  static constexpr int B_CHUNKS = BN * BK / 16 / 256;
-  static constexpr int LDS_A = BM * LDS_STRIDE;
-  static constexpr int LDS_B = BN * LDS_STRIDE;
-  static constexpr size_t LDS_BYTES = 2 * (LDS_A + LDS_B);
-};
-
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void gemm_i8_kernel(
-    const int8_t *__restrict__ QA, const float *__restrict__ SA, const int8_t *__restrict__ QW,
-    const float *__restrict__ SW, const bf16_t *__restrict__ bias, bf16_t *__restrict__ C,
-    int64_t ldc, int M, int N, int K, int group) {
-#pragma clang fp contract(off)
-  using Cfg = GemmI8Cfg<BM, BN, WM, WN>;
-  constexpr int BK = Cfg::BK, LS = Cfg::LDS_STRIDE, TM = Cfg::TM, TN = Cfg::TN;
-  extern __shared__ __align__(16) int8_t smem8[];
-  int8_t *As = smem8;
-  int8_t *Bs = smem8 + 2 * Cfg::LDS_A;
-
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  const int ld_row = tid >> 3, ld_col = (tid & 7) * 16;
-  const int8_t *a_src[Cfg::A_CHUNKS];
-  const int8_t *b_src[Cfg::B_CHUNKS];
-#pragma unroll
-  for (int c = 0; c < Cfg::A_CHUNKS; ++c) {
-    int r = m0 + ld_row + c * 32;
-    r = r < M ? r : M - 1;
-    a_src[c] = QA + static_cast<int64_t>(r) * K + ld_col;
-  }
-#pragma unroll
-  for (int c = 0; c < Cfg::B_CHUNKS; ++c) {
-    int r = n0 + ld_row + c * 32;
-    r = r < N ? r : N - 1;
-    b_src[c] = QW + static_cast<int64_t>(r) * K + ld_col;
-  }
-  uint4 ra[Cfg::A_CHUNKS], rb[Cfg::B_CHUNKS];
-  auto load_global = [&](int k0) {
-#pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c) ra[c] = *reinterpret_cast<const uint4 *>(a_src[c] + k0);
-#pragma unroll
-    for (int c = 0; c < Cfg::B_CHUNKS; ++c) rb[c] = *reinterpret_cast<const uint4 *>(b_src[c] + k0);
-  };
-  auto store_lds = [&](int buf) {
-    int8_t *as = As + buf * Cfg::LDS_A;
-    int8_t *bs = Bs + buf * Cfg::LDS_B;
-#pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c)
-      *reinterpret_cast<uint4 *>(as + (ld_row + c * 32) * LS + ld_col) = ra[c];
-#pragma unroll
-    for (int c = 0; c < Cfg::B_CHUNKS; ++c)
-      *reinterpret_cast<uint4 *>(bs + (ld_row + c * 32) * LS + ld_col) = rb[c];
-  };
-
-  const int col_l = lane & 31, row_l = (lane >> 5) * 4;
-  i32x16_t acc[TM][TN];
-  float tot[TM][TN][16];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      acc[i][j] = i32x16_t{};
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
-    }
-
-  const int KT = K / BK;
-  const int tiles_per_group = group / BK;
-  const int ngroups = K / group;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 16;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_global((kt + 1) * BK);
-    const int8_t *as = As + buf * Cfg::LDS_A + (wm * TM * 32 + frag_row) * LS + frag_k;
-    const int8_t *bs = Bs + buf * Cfg::LDS_B + (wn * TN * 32 + frag_row) * LS + frag_k;
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      i32x4_t af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const i32x4_t *>(as + i * 32 * LS + ks * 32);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const i32x4_t *>(bs + j * 32 * LS + ks * 32);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if ((kt + 1) % tiles_per_group == 0) {
-      const int g = (kt + 1) / tiles_per_group - 1;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int m = m0 + (wm * TM + i) * 32 + (r / 4) * 8 + row_l + (r % 4);
-          m = m < M ? m : M - 1;
-          const float sa = SA[static_cast<int64_t>(m) * ngroups + g];
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const float t = static_cast<float>(acc[i][j][r]) * sa;
-            tot[i][j][r] = tot[i][j][r] + t;
-          }
-        }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = i32x16_t{};
-    }
-    if (kt + 1 < KT) store_lds(buf ^ 1);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + (wn * TN + j) * 32 + col_l;
-    if (n >= N) continue;
-    const float sw = SW[n];
-    const float b = bf2f(bias[n]);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + (wm * TM + i) * 32 + (r / 4) * 8 + row_l + (r % 4);
-        if (m >= M) continue;
-        const float v = tot[i][j][r] * sw;
-        const float o = v + b;
-        C[static_cast<int64_t>(m) * ldc + n] = static_cast<bf16_t>(f2bf(o));
-      }
-  }
+__global__ void fill_i32_kernel(int *p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
 }
 
 }  // namespace
 
-void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, void *C,
-                      int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
-                      int epilogue, int out_f32, hipStream_t s) {
-  if (out_f32)
-    gemm_select<H3_EPI_NONE, 1>(A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, s);
-  else if (epilogue == H3_EPI_GELU)
-    gemm_select<H3_EPI_GELU, 0>(A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, s);
-  else
-    gemm_select<H3_EPI_NONE, 0>(A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, s);
+GemmPlan plan_gemm(int M, int N, int K) {
+  GemmPlan p{};
+  p.split = 1;
+  const int64_t t192 = static_cast<int64_t>((M + 191) / 192) * ((N + 191) / 192);
+  if (M >= 4096 && N >= 2048) {
+    p.cfg = 2;
+  } else if (M >= 192 && N >= 192) {
+    p.cfg = 1;
+    if (t192 < 256 && K % 128 == 0 && K >= 2048) p.split = 2;
+  } else {
+    p.cfg = 0;
+  }
+  if (p.split == 2) {
+    p.part_bytes = static_cast<size_t>(t192) * 2 * 192 * 192 * sizeof(float);
+    p.counters = static_cast<int>(t192);
+  }
+  return p;
 }
 
-void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
-                    const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
-                    hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
-  using Cfg = GemmI8Cfg<BM, BN, 2, 2>;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  auto kern = gemm_i8_kernel<BM, BN, 2, 2>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(Cfg::LDS_BYTES));
-    attr_set = true;
-  }
-  kern<<<tiles, 256, Cfg::LDS_BYTES, s>>>(QA, SA, QW, SW, bias, C, ldc, M, N, K, group);
+void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, void *C,
+                      int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
+                      int epilogue, int out_f32, hipStream_t s, const SplitScratch &sc) {
+  GemmPlan p = plan_gemm(M, N, K);
+  if (p.split == 2 && (!sc.part || !sc.counters || p.part_bytes > sc.part_bytes ||
+                       p.counters > sc.n_counters))
+    p.split = 1;
+  GemmArgs a{A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, sc.part, sc.counters};
+  if (out_f32)
+    gemm_dispatch<H3_EPI_NONE, 1>(p, a, s);
+  else if (epilogue == H3_EPI_GELU)
+    gemm_dispatch<H3_EPI_GELU, 0>(p, a, s);
+  else
+    gemm_dispatch<H3_EPI_NONE, 0>(p, a, s);
+}
+
+void launch_fill_i32(int *p, int n, int value, hipStream_t s) {
+  if (n <= 0) return;
+  fill_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n, value);
 }
 
 }  // namespace h3
