@@ -29,7 +29,7 @@ constexpr int kBlockN = 64;   // keys per tile
 template <int D>
 struct AttnCfg {
   static constexpr int KS = D + 8;         // K tile row stride (elements)
-  static constexpr int VS = kBlockN + 8;   // V^T tile row stride (elements)
+  static constexpr int VS = kBlockN + 4;   // V^T row stride: 136 bytes, so 32 rows of 8-byte reads cover 64 banks once
   static constexpr int CH = D / 8;         // 16-byte chunks per row
   static constexpr int K_PASSES = kBlockN * CH / 256;
   static constexpr int V_GROUPS = 256 / 32;          // chunk groups per pass (32 key pairs)
@@ -38,7 +38,7 @@ struct AttnCfg {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attention_kernel(
+__global__ __launch_bounds__(256, 2) void attention_kernel(
     const bf16_t *__restrict__ Q, int64_t ldq, const bf16_t *__restrict__ K, int64_t ldk,
     const bf16_t *__restrict__ V, int64_t ldv, bf16_t *__restrict__ O, int64_t ldo, int nq,
     int nk, float scale_log2) {

@@ -44,8 +44,26 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0,
+// odd in z; absolute error <= 1.5e-7, far below the bf16 resolution of the GELU output, and
+// branch-free (one reciprocal and one exponential per element).
+__device__ __forceinline__ float erf_as(float x) {
+  const float z = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
+  float poly = 1.061405429f;
+  poly = poly * t - 1.453152027f;
+  poly = poly * t + 1.421413741f;
+  poly = poly * t - 0.284496736f;
+  poly = poly * t + 0.254829592f;
+  poly = poly * t;
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  return copysignf(1.0f - poly * e, x);
+}
+
+// exact-erf GELU: x/2 (1 + erf(x / sqrt 2))
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f));
 }
 
 // LDS holds 64 banks of 4 bytes; a 16-byte-per-lane read is served 16 lanes per cycle.  Tile
