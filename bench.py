@@ -34,7 +34,23 @@ def parse():
     ap.add_argument("--workload", default="512sq_22f")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times), the "
+                         "reference for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int):
+    """A plain copy of known size: counters taken on it scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.empty(mib * 2 ** 20, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": mib * 2 ** 20, "copies": 5}))
 
 
 def traffic_for(kernel_src: str):
@@ -84,6 +100,9 @@ def cpu_baseline(w, budget_s: float):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus N > 1 is not "
                                    "supported (the multi-GPU sequence split is a design note)"}))
