@@ -60,8 +60,8 @@ WsPlan plan_workspace(const Model &m, int32_t n_tokens, const h3_run_opts &o);
 // Tile configuration and split-K choice of a bf16 product; part_bytes / counters give the
 // workspace a split-K launch needs (partial tiles; arrival counters, zero between launches).
 struct GemmPlan {
-  int cfg;    // 0: 128x128, 1: 192x192, 2: 256x256 output tiles
-  int split;  // 1 or 2 (K halves in separate workgroups)
+  int cfg;    // 0: 128x128, 1: 192x192, 2: 256x256, 3: 128x256 output tiles
+  int split;  // pieces of K in separate workgroups (1 or 2)
   size_t part_bytes;
   int counters;
 };

@@ -17,15 +17,16 @@
 // B[n = l%32][k = 8(l/32) .. +7]; accumulator register i of lane l is
 // C[8(i/4) + 4(l/32) + i%4][l%32].
 //
-// Tile shapes are chosen per problem: the 1536-token workload uses 192x192 tiles (4 waves of
-// 96x96, three LDS stages), which fill whole rounds of the 256 CUs (8 x 64 = 512 tiles at
-// N = 12288; 8 x 16 = 128 tiles x 2 K halves at N = 3072 with split-K); large M uses 256x256
-// tiles with 8 waves of 128x64 (two waves per SIMD, two LDS stages).
+// Tile shapes are chosen per problem by plan_gemm (measured on random bf16 operands): 192x192
+// tiles (4 waves of 96x96, three LDS stages) for the wide QKV / FC1 products of the 1536-token
+// workload (8 x 64 = 512 tiles, two full rounds of the 256 CUs), the same tile with K split in
+// two for FC2 (128 tiles x 2), 128x256 for the output projection, and 256x256 tiles with 8
+// waves of 128x64 (two waves per SIMD) for the large-M products of the 768x1344 workload.
 //
-// Split-K (two K halves per tile): each half stores its float32 partial tile, fences, and bumps
-// the tile's arrival counter; the second to arrive adds the other half's partial to its own
-// (a + b == b + a in IEEE arithmetic, so the result does not depend on which arrives first),
-// runs the epilogue and resets the counter to zero.  No workgroup waits for another.
+// Split-K (S pieces of K per tile in separate workgroups): each piece stores its float32 partial
+// tile, fences, and bumps the tile's arrival counter; the last to arrive sums the S partials in
+// piece order 0..S-1 (whichever arrived first, so the result is deterministic), runs the
+// epilogue and resets the counter to zero.  No workgroup waits for another.
 //
 // Workgroup order is XCD-aware: consecutive hardware ids land on different XCDs, so ids are
 // regrouped so that each XCD walks a contiguous band of tiles, visited in groups of 8 tile
@@ -253,35 +254,43 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
       lds_dma_barrier<0>();
   }
 
-  if constexpr (SPLIT == 2) {
-    // partial tile in register order: [tile][half][(i, j, quad)][thread] float4s
-    float4 *mine = reinterpret_cast<float4 *>(g.part) + (static_cast<int64_t>(tile_id) * 2 + split) * (BM * BN / 4);
-    const float4 *other = reinterpret_cast<const float4 *>(g.part) + (static_cast<int64_t>(tile_id) * 2 + (split ^ 1)) * (BM * BN / 4);
+  if constexpr (SPLIT > 1) {
+    // partial tiles in register order: [tile][split][(i, j, quad)][thread] float4s
+    constexpr int TILE4 = BM * BN / 4;
+    float4 *parts = reinterpret_cast<float4 *>(g.part) + static_cast<int64_t>(tile_id) * SPLIT * TILE4;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          mine[((i * TN + j) * 4 + r4) * NT + tid] =
+          parts[split * TILE4 + ((i * TN + j) * 4 + r4) * NT + tid] =
               make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
     __threadfence();
     __syncthreads();
     if (tid == 0) ticket = atomicAdd(g.counters + tile_id, 1);
     __syncthreads();
-    if (ticket == 0) return;
+    if (ticket != SPLIT - 1) return;
     __threadfence();
+    // the last to arrive sums the partials in split order (0, 1, ..., SPLIT-1), whichever
+    // workgroups arrived first, so the result does not depend on the arrival order
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const float4 v = other[((i * TN + j) * 4 + r4) * NT + tid];
-          acc[i][j][4 * r4] += v.x;
-          acc[i][j][4 * r4 + 1] += v.y;
-          acc[i][j][4 * r4 + 2] += v.z;
-          acc[i][j][4 * r4 + 3] += v.w;
+          const int64_t at = ((i * TN + j) * 4 + r4) * NT + tid;
+          float4 t = parts[at];
+#pragma unroll
+          for (int q = 1; q < SPLIT; ++q) {
+            const float4 v = parts[q * TILE4 + at];
+            t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+          }
+          acc[i][j][4 * r4] = t.x;
+          acc[i][j][4 * r4 + 1] = t.y;
+          acc[i][j][4 * r4 + 2] = t.z;
+          acc[i][j][4 * r4 + 3] = t.w;
         }
     if (tid == 0) g.counters[tile_id] = 0;
   }
@@ -330,14 +339,17 @@ void run_gemm(const GemmArgs &a, hipStream_t s) {
 
 template <int EPI, int OUT_F32>
 void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
-  if (p.cfg == 2)
-    run_gemm<256, 256, 2, 4, 2, EPI, OUT_F32, 1>(a, s);
-  else if (p.cfg == 1 && p.split == 2)
-    run_gemm<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s);
-  else if (p.cfg == 1)
-    run_gemm<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s);
-  else
-    run_gemm<128, 128, 2, 2, 3, EPI, OUT_F32, 1>(a, s);
+  switch (p.cfg) {
+    case 2: run_gemm<256, 256, 2, 4, 2, EPI, OUT_F32, 1>(a, s); break;
+    case 1:
+      if (p.split == 2)
+        run_gemm<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s);
+      else
+        run_gemm<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s);
+      break;
+    case 3: run_gemm<128, 256, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
+    default: run_gemm<128, 128, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
+  }
 }
 
 __global__ void fill_i32_kernel(int *p, int n, int v) {
@@ -347,20 +359,30 @@ __global__ void fill_i32_kernel(int *p, int n, int v) {
 
 }  // namespace
 
+// Tile choice measured on the MI355X with random bf16 operands (see the kernel comments):
+//   M >= 4096, N >= 2048          256x256, 8 waves            (768x1344 workload)
+//   N >= 8192                     192x192                     (QKV, FC1 at 1536 / 768 tokens)
+//   K >= 8192, 128..255 tiles     192x192, K split in two     (FC2 at 1536 tokens)
+//   M >= 1024                     128x256                     (output projection at 1536 tokens)
+//   otherwise                     128x128
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   p.split = 1;
   const int64_t t192 = static_cast<int64_t>((M + 191) / 192) * ((N + 191) / 192);
   if (M >= 4096 && N >= 2048) {
     p.cfg = 2;
-  } else if (M >= 192 && N >= 192) {
+  } else if (N >= 8192 && M >= 192) {
     p.cfg = 1;
-    if (t192 < 256 && K % 128 == 0 && K >= 2048) p.split = 2;
+  } else if (K >= 8192 && K % 128 == 0 && t192 >= 128 && t192 < 256) {
+    p.cfg = 1;
+    p.split = 2;
+  } else if (M >= 1024 && N >= 256) {
+    p.cfg = 3;
   } else {
     p.cfg = 0;
   }
-  if (p.split == 2) {
-    p.part_bytes = static_cast<size_t>(t192) * 2 * 192 * 192 * sizeof(float);
+  if (p.split > 1) {
+    p.part_bytes = static_cast<size_t>(t192) * p.split * 192 * 192 * sizeof(float);
     p.counters = static_cast<int>(t192);
   }
   return p;
@@ -370,7 +392,7 @@ void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb
                       int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
                       int epilogue, int out_f32, hipStream_t s, const SplitScratch &sc) {
   GemmPlan p = plan_gemm(M, N, K);
-  if (p.split == 2 && (!sc.part || !sc.counters || p.part_bytes > sc.part_bytes ||
+  if (p.split > 1 && (!sc.part || !sc.counters || p.part_bytes > sc.part_bytes ||
                        p.counters > sc.n_counters))
     p.split = 1;
   GemmArgs a{A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, sc.part, sc.counters};
