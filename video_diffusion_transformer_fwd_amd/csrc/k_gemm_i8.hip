@@ -1,9 +1,15 @@
 // int8 product of the per-row / grouped int8 FC2 on the gfx950 matrix cores.
 //
 // C[M,N] = bf16(((sum_g float(acc_g) * SA[m,g]) * SW[n]) + bias[n]) with acc_g the exact int32
-// sum of QA[m,k] QW[n,k] over K group g (v_mfma_i32_32x32x32_i8: lane l supplies 16
-// consecutive k at 16(l/32) of row l%32 for both operands).  Same tiling skeleton as the bf16
-// product: 256-thread workgroup, 128x128 tile, BK = 128 bytes, padded LDS, double-buffered.
+// sum of QA[m,k] QW[n,k] over K group g (groups ascending, each float operation rounded, no
+// fused multiply-add), v_mfma_i32_32x32x32_i8: lane l supplies 16 consecutive k at 16(l/32) of
+// row l%32 for both operands; accumulator register i of lane l is C[8(i/4) + 4(l/32) + i%4][l%32].
+//
+// Same pipeline as the bf16 product: a K slice is 128 int8 = 128 bytes per row, so the LDS tile
+// rows, their bank swizzle (chunk c of row r in slot c ^ ((r >> 1) & 7)) and the direct
+// global -> LDS staging are identical; three LDS stages; each 32-wide K step's fragment reads
+// are issued while the previous step's MFMAs run.  At each group end the int32 sums are folded
+// into a float32 total and cleared.
 #include <hip/hip_runtime.h>
 
 #include "h3_internal.h"
@@ -18,91 +24,103 @@ typedef __attribute__((ext_vector_type(16))) int i32x16_t;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int &tm, int &tn) {
-  const int nwg = tiles_m * tiles_n;
-  int id = blockIdx.x;
-  if (nwg % kXcds == 0) {
-    const int per = nwg / kXcds;
-    id = (id % kXcds) * per + id / kXcds;
-  }
-  const int in_group = kGroupM * tiles_n;
-  const int group = id / in_group;
-  const int first_m = group * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int r = id - group * in_group;
-  tm = first_m + r % gm;
-  tn = r / gm;
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-// Same structure with int8 operands: BK = 128 bytes, 32x32x32 i8 MFMA.  acc holds the int32
-// sum of the current K group; at each group end it is folded into the float32 total as
-// tot = tot + float(acc) * SA[m, g] (two rounded operations, no fused multiply-add).
-template <int BM, int BN, int WM, int WN>
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
+
+template <int VM>
+__device__ __forceinline__ void lds_dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
 struct GemmI8Cfg {
-  static constexpr int BK = 128;
-  static constexpr int LDS_STRIDE = BK + 16;  // bytes
+  static constexpr int NT = 64 * WM * WN;
+  static constexpr int BK = 128;  // int8 elements = bytes per row per slice
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
-  static constexpr int A_CHUNKS = BM * BK / 16 / 256;
-  static constexpr int B_CHUNKS = BN * BK / 16 / 256;
-  static constexpr int LDS_A = BM * LDS_STRIDE;
-  static constexpr int LDS_B = BN * LDS_STRIDE;
-  static constexpr size_t LDS_BYTES = 2 * (LDS_A + LDS_B);
+  static constexpr int STAGE = (BM + BN) * 128;
+  static constexpr size_t LDS_BYTES = NS * static_cast<size_t>(STAGE);
 };
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void gemm_i8_kernel(
+template <int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
     const int8_t *__restrict__ QA, const float *__restrict__ SA, const int8_t *__restrict__ QW,
     const float *__restrict__ SW, const bf16_t *__restrict__ bias, bf16_t *__restrict__ C,
     int64_t ldc, int M, int N, int K, int group) {
 #pragma clang fp contract(off)
-  using Cfg = GemmI8Cfg<BM, BN, WM, WN>;
-  constexpr int BK = Cfg::BK, LS = Cfg::LDS_STRIDE, TM = Cfg::TM, TN = Cfg::TN;
-  extern __shared__ __align__(16) int8_t smem8[];
-  int8_t *As = smem8;
-  int8_t *Bs = smem8 + 2 * Cfg::LDS_A;
+  using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
+  constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
+  extern __shared__ __align__(16) unsigned char smem8[];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  {
+    const int ntiles = tiles_m * tiles_n;
+    int id = blockIdx.x;
+    if (ntiles % kXcds == 0) {
+      const int per = ntiles / kXcds;
+      id = (id % kXcds) * per + id / kXcds;
+    }
+    const int in_group = kGroupM * tiles_n;
+    const int grp = id / in_group;
+    const int first_m = grp * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM);
+    const int r = id - grp * in_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  const int ld_row = tid >> 3, ld_col = (tid & 7) * 16;
-  const int8_t *a_src[Cfg::A_CHUNKS];
-  const int8_t *b_src[Cfg::B_CHUNKS];
+  // direct global -> LDS staging, as in the bf16 product (1 byte per element here)
+  constexpr int NW = NT / 64;
+  constexpr int ROW_BLOCKS = (BM + BN) / 8;
+  constexpr int LOADS = ROW_BLOCKS / NW;
+  static_assert(ROW_BLOCKS % NW == 0 && BM % 8 == 0, "row blocks must split evenly over waves");
+  const unsigned char *abase = reinterpret_cast<const unsigned char *>(QA);
+  const unsigned char *bbase = reinterpret_cast<const unsigned char *>(QW);
+  uint32_t goff[LOADS];
+  {
+    const int lrow = lane >> 3;
 #pragma unroll
-  for (int c = 0; c < Cfg::A_CHUNKS; ++c) {
-    int r = m0 + ld_row + c * 32;
-    r = r < M ? r : M - 1;
-    a_src[c] = QA + static_cast<int64_t>(r) * K + ld_col;
+    for (int i = 0; i < LOADS; ++i) {
+      const int R = (i * NW + wave) * 8 + lrow;
+      const int chunk = (lane & 7) ^ ((R >> 1) & 7);
+      if (R < BM) {
+        int r = m0 + R;
+        r = r < M ? r : M - 1;
+        goff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * K + chunk * 16);
+      } else {
+        int r = n0 + R - BM;
+        r = r < N ? r : N - 1;
+        goff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * K + chunk * 16);
+      }
+    }
   }
+  auto issue_slice = [&](int stage, int kt) {
+    const uint32_t kb = static_cast<uint32_t>(kt * BK);
+    unsigned char *st = smem8 + stage * Cfg::STAGE;
 #pragma unroll
-  for (int c = 0; c < Cfg::B_CHUNKS; ++c) {
-    int r = n0 + ld_row + c * 32;
-    r = r < N ? r : N - 1;
-    b_src[c] = QW + static_cast<int64_t>(r) * K + ld_col;
-  }
-  uint4 ra[Cfg::A_CHUNKS], rb[Cfg::B_CHUNKS];
-  auto load_global = [&](int k0) {
-#pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c) ra[c] = *reinterpret_cast<const uint4 *>(a_src[c] + k0);
-#pragma unroll
-    for (int c = 0; c < Cfg::B_CHUNKS; ++c) rb[c] = *reinterpret_cast<const uint4 *>(b_src[c] + k0);
-  };
-  auto store_lds = [&](int buf) {
-    int8_t *as = As + buf * Cfg::LDS_A;
-    int8_t *bs = Bs + buf * Cfg::LDS_B;
-#pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c)
-      *reinterpret_cast<uint4 *>(as + (ld_row + c * 32) * LS + ld_col) = ra[c];
-#pragma unroll
-    for (int c = 0; c < Cfg::B_CHUNKS; ++c)
-      *reinterpret_cast<uint4 *>(bs + (ld_row + c * 32) * LS + ld_col) = rb[c];
+    for (int i = 0; i < LOADS; ++i) {
+      const int R0 = (i * NW + wave) * 8;
+      const unsigned char *src = (R0 < BM ? abase : bbase) + (goff[i] + kb);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(st + R0 * 128), 16, 0, 0);
+    }
   };
 
-  const int col_l = lane & 31, row_l = (lane >> 5) * 4;
+  const int fr = lane & 31, fh = lane >> 5;
+  int a_row[TM], b_row[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row[i] = (wm * TM + i) * 32 + fr;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_row[j] = (wn * TN + j) * 32 + fr;
+
+  const int row_l = fh * 4;
   i32x16_t acc[TM][TN];
   float tot[TM][TN][16];
 #pragma unroll
@@ -115,32 +133,54 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(
     }
 
   const int KT = K / BK;
-  const int tiles_per_group = group / BK;
+  const int slices_per_group = group / BK;
   const int ngroups = K / group;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 16;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < KT) issue_slice(p, p);
+  if (KT >= NS - 1)
+    lds_dma_barrier<LOADS * (NS - 2)>();
+  else
+    lds_dma_barrier<0>();
+
   for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_global((kt + 1) * BK);
-    const int8_t *as = As + buf * Cfg::LDS_A + (wm * TM * 32 + frag_row) * LS + frag_k;
-    const int8_t *bs = Bs + buf * Cfg::LDS_B + (wn * TN * 32 + frag_row) * LS + frag_k;
+    const unsigned char *st = smem8 + (kt % NS) * Cfg::STAGE;
+    const bool more = kt + NS - 1 < KT;
+    if (more) issue_slice((kt + NS - 1) % NS, kt + NS - 1);
+    i32x4_t af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const i32x4_t *>(st + swz(a_row[i], fh));
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = *reinterpret_cast<const i32x4_t *>(st + BM * 128 + swz(b_row[j], fh));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      i32x4_t af[TM], bfr[TN];
+      const int cur = ks & 1;
+      if (ks + 1 < BK / 32) {
+        const int ch = 2 * (ks + 1) + fh;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const i32x4_t *>(as + i * 32 * LS + ks * 32);
+        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = *reinterpret_cast<const i32x4_t *>(st + swz(a_row[i], ch));
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const i32x4_t *>(bs + j * 32 * LS + ks * 32);
+        for (int j = 0; j < TN; ++j)
+          bfr[cur ^ 1][j] = *reinterpret_cast<const i32x4_t *>(st + BM * 128 + swz(b_row[j], ch));
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+      if (ks + 1 < BK / 32) {
+#pragma unroll
+        for (int q = 0; q < TM + TN; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (TM * TN > TM + TN) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+      }
     }
-    if ((kt + 1) % tiles_per_group == 0) {
-      const int g = (kt + 1) / tiles_per_group - 1;
+    // group end: tot += float(acc) * SA[m, g], then clear acc
+    if ((kt + 1) % slices_per_group == 0) {
+      const int g = (kt + 1) / slices_per_group - 1;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -159,10 +199,13 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = i32x16_t{};
     }
-    if (kt + 1 < KT) store_lds(buf ^ 1);
-    __syncthreads();
+    if (more)
+      lds_dma_barrier<LOADS * (NS - 2)>();
+    else
+      lds_dma_barrier<0>();
   }
 
+  const int col_l = lane & 31;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int n = n0 + (wn * TN + j) * 32 + col_l;
@@ -182,23 +225,29 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(
   }
 }
 
+template <int BM, int BN, int WM, int WN, int NS>
+void run_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
+                 const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
+                 hipStream_t s) {
+  using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(Cfg::LDS_BYTES));
+    attr_set = true;
+  }
+  kern<<<tiles, Cfg::NT, Cfg::LDS_BYTES, s>>>(QA, SA, QW, SW, bias, C, ldc, M, N, K, group);
+}
+
 }  // namespace
 
 void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
                     hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
-  using Cfg = GemmI8Cfg<BM, BN, 2, 2>;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  auto kern = gemm_i8_kernel<BM, BN, 2, 2>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(Cfg::LDS_BYTES));
-    attr_set = true;
-  }
-  kern<<<tiles, 256, Cfg::LDS_BYTES, s>>>(QA, SA, QW, SW, bias, C, ldc, M, N, K, group);
+  run_gemm_i8<128, 128, 2, 2, 3>(QA, SA, QW, SW, bias, C, ldc, M, N, K, group, s);
 }
 
 }  // namespace h3
