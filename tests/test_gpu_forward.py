@@ -131,3 +131,12 @@ def test_512sq_full_depth_zero_gates_and_determinism():
     _, fin = dit.modulation(g, 1.0)
     ref = dit.final_head(dit.patch_embed(f64(lat), g), g, fin)
     assert_close(f64(v0), ref, rel=2e-2, elem=8e-2, what="zero-gate velocity")
+
+
+def test_512sq_token_reduction_loop_reduced_depth():
+    # the 512x512x22 shape with 5 blocks and token pairing (1536 -> 768 tokens after the third
+    # block, restored before the head), --steps 2 --reuse 1
+    w = dataclasses.replace(S.WORKLOADS["512sq_22f_tr"], n_blocks=5, layers=0, steps=2, reuse=1)
+    model = DiTModel(w)
+    om = oracle_model(w)
+    loop_parity(w, model, om, {"token_reduction": True}, 2, 1, [0, 1, 2, 3, 4])
