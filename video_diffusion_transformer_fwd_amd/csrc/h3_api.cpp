@@ -56,23 +56,17 @@ WsPlan plan_workspace(const Model &m, int32_t n, const h3_run_opts &o) {
   p.hq = take(i8 ? static_cast<size_t>(n * F) : 0);
   p.hs = take(i8 ? static_cast<size_t>(n * (F / 1024)) * sizeof(float) : 0);
   p.rope = take(static_cast<size_t>(n * half) * sizeof(float2));
-  // split-K partial tiles and arrival counters of the block's products
+  // split-K partials of the block's products
   size_t part = 0;
-  int cnt = 0;
   // the block runs at n tokens, or at about n/2 between a token merge and its restore
   for (int64_t rows : {static_cast<int64_t>(n), static_cast<int64_t>((n + 1) / 2)}) {
     const int r = static_cast<int>(rows);
     const GemmPlan gp[] = {plan_gemm(r, 4 * d, d), plan_gemm(r, d, 2 * d), plan_gemm(r, F, d),
                            plan_gemm(r, d, F)};
-    for (const GemmPlan &g : gp) {
-      part = std::max(part, g.part_bytes);
-      cnt = std::max(cnt, g.counters);
-    }
+    for (const GemmPlan &g : gp) part = std::max(part, g.part_bytes);
   }
   p.gpart = take(part);
   p.gpart_bytes = part;
-  p.gcnt = take(static_cast<size_t>(cnt) * sizeof(int));
-  p.n_counters = cnt;
   // forward / modulation
   p.mod = take(static_cast<size_t>(nb * 6 * d) * sizeof(float));
   p.fin = take(static_cast<size_t>(2 * d) * sizeof(float));
@@ -117,8 +111,6 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
   SplitScratch sk;
   sk.part = reinterpret_cast<float *>(ws + p.gpart);
   sk.part_bytes = p.gpart_bytes;
-  sk.counters = reinterpret_cast<int *>(ws + p.gcnt);
-  sk.n_counters = p.n_counters;
 
   // AdaLN-1 (unless the caller already has it, e.g. from the previous block's fused gate)
   if (!n1_in) {
@@ -364,7 +356,6 @@ int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
   hipStream_t s = as_stream(stream);
   char *w = reinterpret_cast<char *>(ws);
   float2 *rope = reinterpret_cast<float2 *>(w + p.rope);
-  launch_fill_i32(reinterpret_cast<int *>(w + p.gcnt), p.n_counters, 0, s);
   launch_rope_table(rope, *geom, n, m->head_dim, s);
   return run_block(m, block, *geom, n, *o, reinterpret_cast<bf16_t *>(x),
                    reinterpret_cast<const bf16_t *>(n1_in), reinterpret_cast<bf16_t *>(n1_next),
@@ -425,7 +416,6 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
     launch_gemm_bf16(lat16, C, reinterpret_cast<const bf16_t *>(m->g.patch_w), C, x, d, n, d, C,
                      reinterpret_cast<const bf16_t *>(m->g.patch_b), nullptr, H3_EPI_NONE, 0, s);
   }
-  launch_fill_i32(reinterpret_cast<int *>(w + p.gcnt), p.n_counters, 0, s);
   launch_rope_table(rope_full, *geom, n, m->head_dim, s);
   h3_geom red = *geom;
   red.paired = 1;

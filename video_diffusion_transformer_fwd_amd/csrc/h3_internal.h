@@ -46,9 +46,8 @@ struct Model {
 // Workspace plan for a token count and options (all offsets 256-byte aligned).
 struct WsPlan {
   // block part
-  size_t n1, qkvq, attn, y, n2, h, m, hq, hs, rope, gpart, gcnt;
+  size_t n1, qkvq, attn, y, n2, h, m, hq, hs, rope, gpart;
   size_t gpart_bytes;
-  int n_counters;
   // forward / modulation part
   size_t mod, fin, tmp, x, xr, n1b, lat16, rope_r;
   size_t total;
@@ -57,29 +56,24 @@ WsPlan plan_workspace(const Model &m, int32_t n_tokens, const h3_run_opts &o);
 
 // ---------------------------------------------------------------- kernel launchers
 // All launchers assume validated arguments and enqueue on `s`.
-// Tile configuration and split-K choice of a bf16 product; part_bytes / counters give the
-// workspace a split-K launch needs (partial tiles; arrival counters, zero between launches).
+// Tile configuration and split-K choice of a bf16 product; part_bytes is the float32 partial
+// buffer [split][M][N] a split-K launch needs.
 struct GemmPlan {
   int cfg;    // 0: 128x128, 1: 192x192, 2: 256x256, 3: 128x256 output tiles
-  int split;  // pieces of K in separate workgroups (1 or 2)
+  int split;  // pieces of K in separate workgroups (1, 2, 3 or 4)
   size_t part_bytes;
-  int counters;
 };
 GemmPlan plan_gemm(int M, int N, int K);
-// Split-K scratch handed to a product: partial tiles and zeroed arrival counters with their
-// capacities.  A product whose plan needs more than the capacity (or gets none) runs without
-// split-K.
+// Split-K scratch handed to a product (float32 partials) with its capacity.  A product whose
+// plan needs more than the capacity (or gets none) runs without split-K.
 struct SplitScratch {
   float *part = nullptr;
   size_t part_bytes = 0;
-  int *counters = nullptr;
-  int n_counters = 0;
 };
 void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, void *C,
                       int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
                       int epilogue, int out_f32, hipStream_t s,
                       const SplitScratch &scratch = SplitScratch());
-void launch_fill_i32(int *p, int n, int value, hipStream_t s);
 void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
                     hipStream_t s);

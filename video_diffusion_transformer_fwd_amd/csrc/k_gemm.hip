@@ -18,15 +18,15 @@
 // C[8(i/4) + 4(l/32) + i%4][l%32].
 //
 // Tile shapes are chosen per problem by plan_gemm (measured on random bf16 operands): 192x192
-// tiles (4 waves of 96x96, three LDS stages) for the wide QKV / FC1 products of the 1536-token
-// workload (8 x 64 = 512 tiles, two full rounds of the 256 CUs), the same tile with K split in
-// two for FC2 (128 tiles x 2), 128x256 for the output projection, and 256x256 tiles with 8
-// waves of 128x64 (two waves per SIMD) for the large-M products of the 768x1344 workload.
+// tiles (4 waves of 96x96, three LDS stages) for the wide QKV / FC1 products, 256x256 tiles with
+// 8 waves of 128x64 (two waves per SIMD) for large M and, with K split in three, for the
+// narrow (N = d) products of the 1536-token workload; 192x192 with K split in four at 768
+// tokens.
 //
 // Split-K (S pieces of K per tile in separate workgroups): each piece stores its float32 partial
-// tile, fences, and bumps the tile's arrival counter; the last to arrive sums the S partials in
-// piece order 0..S-1 (whichever arrived first, so the result is deterministic), runs the
-// epilogue and resets the counter to zero.  No workgroup waits for another.
+// tile with plain stores; a second launch sums the S partials in piece order 0..S-1 and applies
+// the epilogue, so the result is deterministic and no device-scope fence (which would write
+// back and invalidate L2 under every workgroup) is needed.
 //
 // Workgroup order is XCD-aware: consecutive hardware ids land on different XCDs, so ids are
 // regrouped so that each XCD walks a contiguous band of tiles, visited in groups of 8 tile
@@ -111,8 +111,7 @@ struct GemmArgs {
   int64_t ldc;
   int M, N, K;
   const bf16_t *bias, *bias2;
-  float *part;    // split-K partial tiles
-  int *counters;  // split-K arrival counters, zero between launches
+  float *part;  // split-K partials [S][M][N]
 };
 
 template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT>
@@ -120,7 +119,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int ticket;
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int tile_id = blockIdx.x / SPLIT;
@@ -255,44 +253,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   }
 
   if constexpr (SPLIT > 1) {
-    // partial tiles in register order: [tile][split][(i, j, quad)][thread] float4s
-    constexpr int TILE4 = BM * BN / 4;
-    float4 *parts = reinterpret_cast<float4 *>(g.part) + static_cast<int64_t>(tile_id) * SPLIT * TILE4;
+    // split-K: store this K piece's float32 partial tile, row-major [piece][M][N]; a separate
+    // reduction launch sums the pieces in order and applies the epilogue
+    float *part = g.part + static_cast<int64_t>(split) * g.M * g.N;
+    const int col_p = lane & 31, row_p = (lane >> 5) * 4;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int j = 0; j < TN; ++j) {
+      const int n = n0 + (wn * TN + j) * 32 + col_p;
+      if (n >= g.N) continue;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          parts[split * TILE4 + ((i * TN + j) * 4 + r4) * NT + tid] =
-              make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) ticket = atomicAdd(g.counters + tile_id, 1);
-    __syncthreads();
-    if (ticket != SPLIT - 1) return;
-    __threadfence();
-    // the last to arrive sums the partials in split order (0, 1, ..., SPLIT-1), whichever
-    // workgroups arrived first, so the result does not depend on the arrival order
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int64_t at = ((i * TN + j) * 4 + r4) * NT + tid;
-          float4 t = parts[at];
-#pragma unroll
-          for (int q = 1; q < SPLIT; ++q) {
-            const float4 v = parts[q * TILE4 + at];
-            t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
-          }
-          acc[i][j][4 * r4] = t.x;
-          acc[i][j][4 * r4 + 1] = t.y;
-          acc[i][j][4 * r4 + 2] = t.z;
-          acc[i][j][4 * r4 + 3] = t.w;
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + (wm * TM + i) * 32 + (r / 4) * 8 + row_p + (r % 4);
+          if (m < g.M) part[static_cast<int64_t>(m) * g.N + n] = acc[i][j][r];
         }
-    if (tid == 0) g.counters[tile_id] = 0;
+    }
+    return;
   }
 
   // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 block
@@ -337,54 +314,95 @@ void run_gemm(const GemmArgs &a, hipStream_t s) {
   kern<<<tiles * SPLIT, Cfg::NT, Cfg::LDS_BYTES, s>>>(a);
 }
 
-template <int EPI, int OUT_F32>
-void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
-  switch (p.cfg) {
-    case 2: run_gemm<256, 256, 2, 4, 2, EPI, OUT_F32, 1>(a, s); break;
-    case 1:
-      if (p.split == 2)
-        run_gemm<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s);
-      else
-        run_gemm<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s);
-      break;
-    case 3: run_gemm<128, 256, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
-    default: run_gemm<128, 128, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
+// Sums the split-K partials [S][M][N] in piece order and applies the bias / GELU epilogue.
+template <int EPI, int OUT_F32, int S>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int M,
+                                                            int N, const bf16_t *__restrict__ bias,
+                                                            const bf16_t *__restrict__ bias2,
+                                                            void *__restrict__ C, int64_t ldc) {
+  const int64_t i4 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  const int64_t total = static_cast<int64_t>(M) * N;
+  if (i4 >= total) return;
+  const int m = static_cast<int>(i4 / N), n = static_cast<int>(i4 - static_cast<int64_t>(m) * N);
+  float4 t = *reinterpret_cast<const float4 *>(part + i4);
+#pragma unroll
+  for (int q = 1; q < S; ++q) {
+    const float4 v = *reinterpret_cast<const float4 *>(part + q * total + i4);
+    t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+  }
+  float v[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float b = 0.f;
+    if (bias) b += bf2f(bias[n + e]);
+    if (bias2) b += bf2f(bias2[n + e]);
+    v[e] = v[e] + b;
+    if constexpr (EPI == H3_EPI_GELU) v[e] = gelu_erf(v[e]);
+  }
+  if constexpr (OUT_F32) {
+    float *c = reinterpret_cast<float *>(C) + static_cast<int64_t>(m) * ldc + n;
+    c[0] = v[0]; c[1] = v[1]; c[2] = v[2]; c[3] = v[3];
+  } else {
+    uint2 w;
+    w.x = pack_bf2(v[0], v[1]);
+    w.y = pack_bf2(v[2], v[3]);
+    *reinterpret_cast<uint2 *>(reinterpret_cast<bf16_t *>(C) + static_cast<int64_t>(m) * ldc + n) = w;
   }
 }
 
-__global__ void fill_i32_kernel(int *p, int n, int v) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
+// One product: the tiled GEMM, then (split-K) the ordered reduction with the epilogue.
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int S>
+void run_product(const GemmArgs &a, hipStream_t s) {
+  run_gemm<BM, BN, WM, WN, NS, EPI, OUT_F32, S>(a, s);
+  if constexpr (S > 1) {
+    const int64_t total = static_cast<int64_t>(a.M) * a.N;
+    splitk_reduce_kernel<EPI, OUT_F32, S><<<static_cast<int>((total / 4 + 255) / 256), 256, 0, s>>>(
+        a.part, a.M, a.N, a.bias, a.bias2, a.C, a.ldc);
+  }
+}
+
+template <int EPI, int OUT_F32>
+void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
+  switch (p.cfg * 8 + p.split) {
+    case 2 * 8 + 1: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 1>(a, s); break;
+    case 2 * 8 + 3: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 3>(a, s); break;
+    case 1 * 8 + 1: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
+    case 1 * 8 + 2: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s); break;
+    case 1 * 8 + 4: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 4>(a, s); break;
+    case 3 * 8 + 1: run_product<128, 256, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
+    default: run_product<128, 128, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
+  }
 }
 
 }  // namespace
 
-// Tile choice measured on the MI355X with random bf16 operands (see the kernel comments):
-//   M >= 4096, N >= 2048          256x256, 8 waves            (768x1344 workload)
-//   N >= 8192                     192x192                     (QKV, FC1 at 1536 / 768 tokens)
-//   K >= 8192, 128..255 tiles     192x192, K split in two     (FC2 at 1536 tokens)
-//   M >= 1024                     128x256                     (output projection at 1536 tokens)
-//   otherwise                     128x128
+// Tile choice measured on the MI355X with random bf16 operands:
+//   M >= 4096, N >= 2048            256x256, 8 waves                 (768x1344 workload)
+//   N >= 8192, M >= 192             192x192                          (QKV, FC1)
+//   1024 <= M < 4096, N < 8192      256x256, 8 waves, K split in 3   (out-proj, FC2 at 1536)
+//   192 <= M < 1024, N < 8192       192x192, K split in 4            (out-proj, FC2 at 768)
+//   otherwise                       128x128
+// A split needs K % (64 * split) == 0 and N % 4 == 0, else the product runs unsplit.
 GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
+  p.cfg = 0;
   p.split = 1;
-  const int64_t t192 = static_cast<int64_t>((M + 191) / 192) * ((N + 191) / 192);
   if (M >= 4096 && N >= 2048) {
     p.cfg = 2;
   } else if (N >= 8192 && M >= 192) {
     p.cfg = 1;
-  } else if (K >= 8192 && K % 128 == 0 && t192 >= 128 && t192 < 256) {
-    p.cfg = 1;
-    p.split = 2;
   } else if (M >= 1024 && N >= 256) {
-    p.cfg = 3;
-  } else {
-    p.cfg = 0;
+    p.cfg = 2;
+    p.split = 3;
+  } else if (M >= 192 && N >= 192) {
+    p.cfg = 1;
+    p.split = 4;
   }
-  if (p.split > 1) {
-    p.part_bytes = static_cast<size_t>(t192) * p.split * 192 * 192 * sizeof(float);
-    p.counters = static_cast<int>(t192);
+  if (p.split > 1 && (K % (64 * p.split) != 0 || N % 4 != 0 || K / p.split < 1024)) {
+    p.split = 1;
+    if (p.cfg == 2 && M < 4096) p.cfg = 3;
   }
+  if (p.split > 1) p.part_bytes = static_cast<size_t>(p.split) * M * N * sizeof(float);
   return p;
 }
 
@@ -392,21 +410,17 @@ void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb
                       int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
                       int epilogue, int out_f32, hipStream_t s, const SplitScratch &sc) {
   GemmPlan p = plan_gemm(M, N, K);
-  if (p.split > 1 && (!sc.part || !sc.counters || p.part_bytes > sc.part_bytes ||
-                       p.counters > sc.n_counters))
-    p.split = 1;
-  GemmArgs a{A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, sc.part, sc.counters};
+  if (p.split > 1 && (!sc.part || p.part_bytes > sc.part_bytes)) {
+    p.split = 1;  // no split-K scratch: run the whole K per tile
+    if (p.cfg == 2 && M < 4096) p.cfg = 3;
+  }
+  GemmArgs a{A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, sc.part};
   if (out_f32)
     gemm_dispatch<H3_EPI_NONE, 1>(p, a, s);
   else if (epilogue == H3_EPI_GELU)
     gemm_dispatch<H3_EPI_GELU, 0>(p, a, s);
   else
     gemm_dispatch<H3_EPI_NONE, 0>(p, a, s);
-}
-
-void launch_fill_i32(int *p, int n, int value, hipStream_t s) {
-  if (n <= 0) return;
-  fill_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n, value);
 }
 
 }  // namespace h3
