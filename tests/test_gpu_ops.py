@@ -34,6 +34,7 @@ def sync():
     (1000, 700, 256, 1, 0, 1),      # 192x192 tiles with ragged M and N
     (4100, 2304, 256, 0, 0, 0),     # 256x256 tiles, ragged M
     (4100, 2100, 128, 1, 0, 0),     # 256x256 tiles, ragged M and N, GELU
+    (1601, 8300, 256, 1, 0, 1),     # 384x192 tiles, ragged M and N, GELU, two biases
 ])
 def test_gemm_bf16(M, N, K, epi, f32, two_bias):
     rng = np.random.default_rng(M * 7 + N * 3 + K)

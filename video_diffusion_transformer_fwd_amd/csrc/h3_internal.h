@@ -24,15 +24,16 @@ typedef uint16_t bf16_t;
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-// Round-to-nearest-even float32 -> bf16 bits (inputs are finite on this path; NaN is kept NaN).
+// Round-to-nearest-even float32 -> bf16 bits (v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN).
+typedef __attribute__((ext_vector_type(2))) __bf16 h3_bf16x2_t;
 __device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f2bf(lo) | (f2bf(hi) << 16);
+  h3_bf16x2_t r;
+  r.x = static_cast<__bf16>(lo);
+  r.y = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // ---------------------------------------------------------------- model
@@ -59,7 +60,7 @@ WsPlan plan_workspace(const Model &m, int32_t n_tokens, const h3_run_opts &o);
 // Tile configuration and split-K choice of a bf16 product; part_bytes is the float32 partial
 // buffer [split][M][N] a split-K launch needs.
 struct GemmPlan {
-  int cfg;    // 0: 128x128, 1: 192x192, 2: 256x256, 3: 128x256 output tiles
+  int cfg;    // 0: 128x128, 1: 192x192, 2: 256x256, 3: 128x256, 4: 384x192 output tiles
   int split;  // pieces of K in separate workgroups (1, 2, 3 or 4)
   size_t part_bytes;
 };

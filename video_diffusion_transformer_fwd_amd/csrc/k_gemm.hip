@@ -4,24 +4,25 @@
 //
 // Tiling: a workgroup of WM x WN wave64s owns a BM x BN output tile (each wave a
 // (BM/WM) x (BN/WN) block of 32x32 MFMA tiles) and walks K in BK = 64 slices.  Both operands
-// are K-contiguous, so A and B tiles are staged identically: 16-byte global loads (8
-// consecutive lanes cover one 128-byte row slice) into registers, then into LDS; LDS is
-// double-buffered with one barrier per K slice, the next slice's global loads in flight while
-// the current slice feeds the MFMAs.
+// are K-contiguous, so A and B tiles are staged identically, straight from global memory into
+// LDS (global_load_lds_dwordx4: 8 consecutive lanes cover one 128-byte row slice), NS slices
+// in flight; a slice is consumed once its loads have landed (explicit vmcnt wait + barrier).
 //
 // LDS rows are 64 bf16 = 128 bytes = 8 chunks of 16 bytes, stored without padding: chunk c of
-// row r sits at slot c ^ (r & 7).  The MFMA-operand reads (16 bytes per lane, 8 consecutive
-// rows at one chunk) then hit 8 distinct bank groups.
+// row r sits at slot c ^ ((r >> 1) & 7).  The MFMA-operand reads (16 bytes per lane, 32 rows at
+// one chunk, served 16 lanes = 8 row pairs at a time) then hit distinct bank groups.
 //
-// Operand layouts (32x32x16 bf16): lane l supplies A[m = l%32][k = 8(l/32) .. +7] and
-// B[n = l%32][k = 8(l/32) .. +7]; accumulator register i of lane l is
-// C[8(i/4) + 4(l/32) + i%4][l%32].
+// Operand layouts (32x32x16 bf16): lane l supplies rows X[p = l%32][k = 8(l/32) .. +7] of the
+// first operand and Y[q = l%32][k ...] of the second; accumulator register i of lane l is
+// D[8(i/4) + 4(l/32) + i%4][l%32] with D = X Y^T.  The B tile is passed as the first operand
+// (D = C^T), so lane l holds row m = l%32 of C at the four runs of 4 consecutive columns
+// 8(i/4) + 4(l/32) + 0..3: the epilogue writes 8-byte (bf16) or 16-byte (float32) vectors.
 //
-// Tile shapes are chosen per problem by plan_gemm (measured on random bf16 operands): 192x192
-// tiles (4 waves of 96x96, three LDS stages) for the wide QKV / FC1 products, 256x256 tiles with
-// 8 waves of 128x64 (two waves per SIMD) for large M and, with K split in three, for the
-// narrow (N = d) products of the 1536-token workload; 192x192 with K split in four at 768
-// tokens.
+// Tile shapes are chosen per problem by plan_gemm (measured on random bf16 operands): 384x192
+// tiles (8 waves of 96x96, two per SIMD, two LDS stages) for the wide QKV / FC1 products,
+// 256x256 tiles with 8 waves of 128x64 for the narrow products at large M and, with K split in
+// three, for the narrow (N = d) products of the 1536-token workload; 192x192 (4 waves, three
+// LDS stages) with K split in four for the narrow products at 768 tokens.
 //
 // Split-K (S pieces of K per tile in separate workgroups): each piece stores its float32 partial
 // tile with plain stores; a second launch sums the S partials in piece order 0..S-1 and applies
@@ -45,26 +46,24 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
-// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), t = 1 / (1 + p z), z >= 0,
-// odd in z; absolute error <= 1.5e-7, far below the bf16 resolution of the GELU output, and
-// branch-free (one reciprocal and one exponential per element).
-__device__ __forceinline__ float erf_as(float x) {
-  const float z = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
-  float poly = 1.061405429f;
-  poly = poly * t - 1.453152027f;
-  poly = poly * t + 1.421413741f;
-  poly = poly * t - 0.284496736f;
-  poly = poly * t + 0.254829592f;
-  poly = poly * t;
-  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
-  return copysignf(1.0f - poly * e, x);
-}
-
-// exact-erf GELU: x/2 (1 + erf(x / sqrt 2))
+// GELU(x) = x Phi(x) with Phi the standard normal CDF.  erfc by Abramowitz & Stegun, Handbook
+// of Mathematical Functions, formula 7.1.26: erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2) with
+// t = 1 / (1 + p z), z >= 0, absolute error <= 1.5e-7.  With z = |x| / sqrt 2 and
+// q = erfc(z) / 2 = Phi(-|x|), x Phi(x) = x / 2 + |x| (1/2 - q) holds for either sign of x, so
+// the product needs no branch or select: one reciprocal, one exponential, eight FMA/multiplies.
+// The factor 1/2 of q is folded into the coefficients, 1/sqrt 2 into p and the exponent.
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f));
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + (0.3275911f * 0.70710678118654752f) * ax);
+  float h = 0.5f * 1.061405429f;
+  h = h * t - 0.5f * 1.453152027f;
+  h = h * t + 0.5f * 1.421413741f;
+  h = h * t - 0.5f * 0.284496736f;
+  h = h * t + 0.5f * 0.254829592f;
+  h = h * t;
+  const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // exp(-x^2 / 2)
+  const float q = h * e;
+  return __builtin_fmaf(ax, 0.5f - q, 0.5f * x);
 }
 
 // LDS holds 64 banks of 4 bytes; a 16-byte-per-lane read is served 16 lanes per cycle.  Tile
@@ -96,7 +95,12 @@ struct GemmCfg {
   static constexpr int A_CHUNKS = BM * 8 / NT;  // 16-byte chunks per thread
   static constexpr int B_CHUNKS = BN * 8 / NT;
   static constexpr int STAGE = (BM + BN) * 128;  // bytes
-  static constexpr size_t LDS_BYTES = NS * static_cast<size_t>(STAGE);
+  static constexpr int EPI_LD = BN + 4;            // float32 row stride of the epilogue band
+  static constexpr int EPI_BAND = WM * 32 * EPI_LD;  // floats: one 32-row block of every wave row
+  static constexpr size_t EPI_BYTES = (static_cast<size_t>(EPI_BAND) + BN) * 4;
+  static constexpr size_t LDS_BYTES =
+      NS * static_cast<size_t>(STAGE) > EPI_BYTES ? NS * static_cast<size_t>(STAGE) : EPI_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "tile does not fit the 160 KB LDS");
   static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "tile rows must split evenly over threads");
   static_assert(TM >= 1 && TN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0,
                 "wave tile must be whole 32x32 blocks");
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
       // interleave: one MFMA, one fragment read of the next step, ... so the reads are in flight
       // while this step's MFMAs run
       if (ks + 1 < BK / 16) {
@@ -252,48 +256,95 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
       lds_dma_barrier<0>();
   }
 
+  // lane holds C[m_l][n_l + 8q + e], e = 0..3, in accumulator registers 4q + e of each 32x32 block
+  const int m_l = lane & 31, n_l = (lane >> 5) * 4;
   if constexpr (SPLIT > 1) {
-    // split-K: store this K piece's float32 partial tile, row-major [piece][M][N]; a separate
-    // reduction launch sums the pieces in order and applies the epilogue
+    // split-K: store this K piece's float32 partial tile, row-major [piece][M][N] (N % 4 == 0);
+    // a separate reduction launch sums the pieces in order and applies the epilogue
     float *part = g.part + static_cast<int64_t>(split) * g.M * g.N;
-    const int col_p = lane & 31, row_p = (lane >> 5) * 4;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + (wn * TN + j) * 32 + col_p;
-      if (n >= g.N) continue;
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + (wm * TM + i) * 32 + m_l;
+      if (m >= g.M) continue;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + (wm * TM + i) * 32 + (r / 4) * 8 + row_p + (r % 4);
-          if (m < g.M) part[static_cast<int64_t>(m) * g.N + n] = acc[i][j][r];
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (wn * TN + j) * 32 + q * 8 + n_l;
+          if (n < g.N)
+            *reinterpret_cast<float4 *>(part + static_cast<int64_t>(m) * g.N + n) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         }
     }
     return;
   }
 
-  // epilogue: lane holds C[8(r/4) + 4(lane/32) + r%4][lane%32] of each 32x32 block
-  const int col_l = lane & 31, row_l = (lane >> 5) * 4;
+  // Epilogue through LDS (free once the last slice is consumed): the column sums of the biases
+  // are staged once; then, for each 32-row block index i, every wave writes its accumulators
+  // of that block to a float32 band of WM * 32 rows x BN columns (row stride BN + 4: the 16
+  // rows of a 16-lane write group land on distinct banks), and all threads walk the band in
+  // 4-column chunks with a rolled loop: bias, GELU, conversion, one 8-byte (bf16) or 16-byte
+  // (float32) store per chunk, consecutive threads on consecutive columns of a row.  The code
+  // stays compact (a fully unrolled register epilogue is several thousand instructions that
+  // every wave fetches once, cold, while the MFMAs sit idle).
+  constexpr int LD = Cfg::EPI_LD;
+  float *band = reinterpret_cast<float *>(smem);
+  float *sbias = band + Cfg::EPI_BAND;
+  __syncthreads();
+  for (int c = tid; c < BN; c += NT) {
+    const int n = n0 + c;
+    float bs = 0.f;
+    if (n < g.N) {
+      if (g.bias) bs += bf2f(g.bias[n]);
+      if (g.bias2) bs += bf2f(g.bias2[n]);
+    }
+    sbias[c] = bs;
+  }
+  // vector stores need 4 | ldc and an 8-byte (bf16) / 16-byte (float32) aligned C
+  const bool vec = (g.ldc % 4 == 0) &&
+                   (reinterpret_cast<uintptr_t>(g.C) % (OUT_F32 ? 16 : 8) == 0);
+  constexpr int CHUNKS_PER_ROW = BN / 4;
+  constexpr int BAND_CHUNKS = WM * 32 * CHUNKS_PER_ROW;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + (wn * TN + j) * 32 + col_l;
-    if (n >= g.N) continue;
-    float bsum = 0.f;
-    if (g.bias) bsum += bf2f(g.bias[n]);
-    if (g.bias2) bsum += bf2f(g.bias2[n]);
+  for (int i = 0; i < TM; ++i) {
+    if (i > 0) __syncthreads();  // previous band fully read
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + (wm * TM + i) * 32 + (r / 4) * 8 + row_l + (r % 4);
-        if (m >= g.M) continue;
-        float v = acc[i][j][r] + bsum;
-        if constexpr (EPI == H3_EPI_GELU) v = gelu_erf(v);
-        if constexpr (OUT_F32)
-          reinterpret_cast<float *>(g.C)[static_cast<int64_t>(m) * g.ldc + n] = v;
-        else
-          reinterpret_cast<bf16_t *>(g.C)[static_cast<int64_t>(m) * g.ldc + n] =
-              static_cast<bf16_t>(f2bf(v));
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(band + (wm * 32 + m_l) * LD + (wn * TN + j) * 32 + q * 8 + n_l) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    __syncthreads();
+#pragma unroll 2
+    for (int c4 = tid; c4 < BAND_CHUNKS; c4 += NT) {
+      const int row = c4 / CHUNKS_PER_ROW, col = (c4 - row * CHUNKS_PER_ROW) * 4;
+      const int m = m0 + ((row >> 5) * TM + i) * 32 + (row & 31);
+      const int n = n0 + col;
+      if (m >= g.M || n >= g.N) continue;
+      const float4 a4 = *reinterpret_cast<const float4 *>(band + row * LD + col);
+      const float4 b4 = *reinterpret_cast<const float4 *>(sbias + col);
+      float v[4] = {a4.x + b4.x, a4.y + b4.y, a4.z + b4.z, a4.w + b4.w};
+      if constexpr (EPI == H3_EPI_GELU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
+      }
+      const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
+      if (vec && n + 3 < g.N) {
+        if constexpr (OUT_F32) {
+          *reinterpret_cast<float4 *>(reinterpret_cast<float *>(g.C) + off) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          uint2 pk;
+          pk.x = pack_bf2(v[0], v[1]);
+          pk.y = pack_bf2(v[2], v[3]);
+          *reinterpret_cast<uint2 *>(reinterpret_cast<bf16_t *>(g.C) + off) = pk;
+        }
+      } else {
+        for (int e = 0; e < 4 && n + e < g.N; ++e) {
+          if constexpr (OUT_F32)
+            reinterpret_cast<float *>(g.C)[off + e] = v[e];
+          else
+            reinterpret_cast<bf16_t *>(g.C)[off + e] = static_cast<bf16_t>(f2bf(v[e]));
+        }
       }
     }
   }
@@ -364,6 +415,7 @@ void run_product(const GemmArgs &a, hipStream_t s) {
 template <int EPI, int OUT_F32>
 void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
   switch (p.cfg * 8 + p.split) {
+    case 4 * 8 + 1: run_product<384, 192, 4, 2, 2, EPI, OUT_F32, 1>(a, s); break;
     case 2 * 8 + 1: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 1>(a, s); break;
     case 2 * 8 + 3: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 3>(a, s); break;
     case 1 * 8 + 1: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
@@ -377,8 +429,9 @@ void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 // Tile choice measured on the MI355X with random bf16 operands:
-//   M >= 4096, N >= 2048            256x256, 8 waves                 (768x1344 workload)
-//   N >= 8192, M >= 192             192x192                          (QKV, FC1)
+//   N >= 8192, M >= 1536            384x192, 8 waves                 (QKV, FC1)
+//   M >= 4096, N >= 2048            256x256, 8 waves                 (narrow products, 768x1344)
+//   N >= 8192, M >= 192             192x192                          (QKV, FC1 at 768 tokens)
 //   1024 <= M < 4096, N < 8192      256x256, 8 waves, K split in 3   (out-proj, FC2 at 1536)
 //   192 <= M < 1024, N < 8192       192x192, K split in 4            (out-proj, FC2 at 768)
 //   otherwise                       128x128
@@ -387,7 +440,9 @@ GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   p.cfg = 0;
   p.split = 1;
-  if (M >= 4096 && N >= 2048) {
+  if (N >= 8192 && M >= 1536) {
+    p.cfg = 4;
+  } else if (M >= 4096 && N >= 2048) {
     p.cfg = 2;
   } else if (N >= 8192 && M >= 192) {
     p.cfg = 1;
