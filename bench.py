@@ -7,10 +7,12 @@ One step = one denoise transition of the --steps 4 --reuse 1 schedule at 512x512
 AdaLN + head) followed by the Euler update; steps walk the 4-step sigma grid cyclically.
 The model (bf16 weights, 15 GB) and the latent are resident in HBM before timing starts.
 
-Prints one JSON line: tokens*blocks/s over the K timed steps, ms per denoise step, the
-roofline of the dominant kernel (FC1 GEMM: its launches are timed with HIP events on the
-launch stream during the timed steps; its algorithmic FLOPs per launch = 2 N d F), and the
-oracle's throughput on a bounded sample of the same workload on this host's cores.
+Prints one JSON line: tokens*blocks/s over the K timed steps (nominal: N x active blocks per
+fresh evaluation; with token pairing the actual count, sum of each block's own token count,
+is reported beside it), ms per denoise step, the roofline of the dominant kernel (FC1 GEMM: its
+launches are timed with HIP events on the launch stream during the timed steps; its algorithmic
+FLOPs per launch = 2 N_b d F at the block's token count N_b), and the oracle's throughput on a
+bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -125,11 +127,25 @@ def main():
     v = torch.empty((n, w.latent_ch), dtype=torch.float32, device=model.device)
     ev_count = [0]
 
-    def step(k):
+    def rows_per_block(eval_index):
+        """Token count each active position runs at in this evaluation (token pairing shrinks the
+        positions from merge_after up to restore_before - 2 to the reduced count)."""
+        if not w.token_reduction:
+            return [n] * nb_act
+        plan = B.h3_token_plan(geo.f_lat, geo.grid_h, geo.grid_w, eval_index, nb_act, with_pairs=False)
+        lo, hi = plan["merge_after"], plan["restore_before"] - 1
+        return [plan["n_reduced"] if lo <= pos < hi else n for pos in range(nb_act)]
+
+    timed_rows = []
+
+    def step(k, timed=False):
         i = k % w.steps
         if fresh[i]:
-            model.forward(lat, float(sig[i]), active, ev_count[0] % max(n_fresh, 1), opts, v)
+            e = ev_count[0] % max(n_fresh, 1)
+            model.forward(lat, float(sig[i]), active, e, opts, v)
             ev_count[0] += 1
+            if timed:
+                timed_rows.extend(rows_per_block(e))
         B.h3_euler_step(lat, v, float(sig[i]), float(sig[i + 1]))
 
     for k in range(args.warmup):
@@ -140,7 +156,7 @@ def main():
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.warmup, args.warmup + args.steps):
-        step(k)
+        step(k, timed=True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     prof = B.h3_profile_end()
@@ -150,11 +166,14 @@ def main():
     tok_blocks = n * nb_act * n_evals / elapsed
     fc1_ms, fc1_launches = prof.get("fc1_gemm", (0.0, 0))
     fc1_avg_ms = fc1_ms / max(fc1_launches, 1)
-    fc1_flops = 2.0 * n * w.d_model * w.ffn_dim
-    achieved = fc1_flops / (fc1_avg_ms * 1e-3) / 1e12 if fc1_launches else 0.0
-    fwd_flops = nb_act * (2 * n * w.d_model * 4 * w.d_model + 4 * n * n * w.d_model
-                          + 4 * n * w.ctx_len * w.d_model + 4 * n * w.d_model * w.d_model
-                          + 4 * n * w.d_model * w.ffn_dim)
+    # algorithmic FLOPs of the timed FC1 launches: 2 N_b d F per block at its own token count
+    fc1_flops_total = sum(2.0 * r * w.d_model * w.ffn_dim for r in timed_rows)
+    fc1_flops = fc1_flops_total / max(fc1_launches, 1)
+    achieved = fc1_flops_total / (fc1_ms * 1e-3) / 1e12 if fc1_launches else 0.0
+    d_, L_, F_ = w.d_model, w.ctx_len, w.ffn_dim
+    fwd_flops_total = sum(2 * r * d_ * 4 * d_ + 4 * r * r * d_ + 4 * r * L_ * d_ + 4 * r * d_ * d_
+                          + 4 * r * d_ * F_ for r in timed_rows)
+    actual_tok_blocks = sum(timed_rows) / elapsed
     out = {
         "metric": "DiT denoise-step ms & tokens·blocks/s at 512²×22f; % bf16 MFMA peak",
         "value": round(tok_blocks, 1),
@@ -173,7 +192,8 @@ def main():
                    "ffn": w.ffn_dim, "ctx_len": w.ctx_len, "steps": w.steps, "reuse": w.reuse,
                    "fc2": w.fc2_mode, "token_reduction": w.token_reduction},
         "ms_per_fresh_eval": round(elapsed * 1e3 / max(n_evals, 1), 3),
-        "mfma_frac_forward": round(fwd_flops * n_evals / elapsed / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "actual_tokens_blocks_per_s": round(actual_tok_blocks, 1),
+        "mfma_frac_forward": round(fwd_flops_total / elapsed / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "fc1_gemm (bf16 GEMM + GELU epilogue)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
