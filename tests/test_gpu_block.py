@@ -144,3 +144,34 @@ def test_block_rejects_bad_arguments():
     with pytest.raises(B.H3Error):
         B.h3_dit_block_fwd(model.handle, 0, model.geo.geom, opts, x, None, x, mod, None,
                            model.ctx_kv[0], ws)
+
+
+def test_int8_row_split_k_bit_identical_to_unsplit():
+    # inside the block the 1536-row int8 FC2 splits K over four workgroups per tile and adds
+    # the int32 partials in a second launch; the standalone product runs unsplit.  Integer
+    # partial sums are exact, so both must give the same bf16 bits from the same quantised input.
+    w, model, om = gpu_model("512sq_22f")
+    n, d, F = model.geo.n_tokens, w.d_model, w.ffn_dim
+    mod, _ = dit.modulation(om["global"], 0.75)
+    mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
+    x = S.normal("test.block.x3", (n, d), 1.0).to(DEV)
+    opts = B.make_opts(fc2_mode="row")
+    ws = run_block(model, w, 1, x, mod_dev, opts)
+    lay = B.h3_workspace_layout(model.handle, n, opts)
+    hq = ws_view(ws, lay.hq, (n, F), torch.int8).clone()
+    hs = ws_view(ws, lay.hs, (n, 1), torch.float32).clone()
+    m_blk = ws_view(ws, lay.m, (n, d)).clone()
+    blk = model.blocks[1]
+    out = torch.empty((n, d), dtype=torch.bfloat16, device=DEV)
+    B.h3_gemm_i8(hq, hs, blk["fc2_q"], blk["fc2_s"], blk["fc2_b"], out, F)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(m_blk))
+    # and both equal the exact integer product dequantised by the oracle's rule, on sampled rows
+    rows = np.array([0, 1, 517, 1024, n - 1])
+    qa = hq[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    sa = hs[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    acc = dit.int8_accumulate(qa, blk["fc2_q"].cpu().numpy(), None)
+    ref = dit.f32_to_bf16(dit.dequant(acc, sa, blk["fc2_s"].cpu().numpy().reshape(-1),
+                                      f64(blk["fc2_b"]).astype(np.float32)))
+    got = out[torch.as_tensor(rows, device=DEV)].cpu().to(torch.float32).numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))

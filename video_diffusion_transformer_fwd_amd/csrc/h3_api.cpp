@@ -64,6 +64,7 @@ WsPlan plan_workspace(const Model &m, int32_t n, const h3_run_opts &o) {
     const GemmPlan gp[] = {plan_gemm(r, 4 * d, d), plan_gemm(r, d, 2 * d), plan_gemm(r, F, d),
                            plan_gemm(r, d, F)};
     for (const GemmPlan &g : gp) part = std::max(part, g.part_bytes);
+    if (i8) part = std::max(part, plan_gemm_i8(r, d, F, o.fc2_mode == H3_FC2_INT8_ROW ? F : 1024).part_bytes);
   }
   p.gpart = take(part);
   p.gpart_bytes = part;
@@ -180,7 +181,7 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
     ProfScope ps(H3_ST_FC2_I8_GEMM, s);
     launch_gemm_i8(hq, hs, reinterpret_cast<const int8_t *>(w.fc2_q),
                    reinterpret_cast<const float *>(w.fc2_s),
-                   reinterpret_cast<const bf16_t *>(w.fc2_b), mo, d, rows, d, F, group, s);
+                   reinterpret_cast<const bf16_t *>(w.fc2_b), mo, d, rows, d, F, group, s, sk);
   }
   // x <- x + g2 m ; optionally n1_next = AdaLN(x; next shift, scale)
   if (n1_next && o.fused_cross_block) {

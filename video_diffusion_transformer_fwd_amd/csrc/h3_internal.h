@@ -65,7 +65,7 @@ struct GemmPlan {
   size_t part_bytes;
 };
 GemmPlan plan_gemm(int M, int N, int K);
-// Split-K scratch handed to a product (float32 partials) with its capacity.  A product whose
+// Split-K scratch handed to a product (float32 or int32 partials) with its capacity.  A product whose
 // plan needs more than the capacity (or gets none) runs without split-K.
 struct SplitScratch {
   float *part = nullptr;
@@ -75,9 +75,12 @@ void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb
                       int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
                       int epilogue, int out_f32, hipStream_t s,
                       const SplitScratch &scratch = SplitScratch());
+// Tile / split-K choice of an int8 product with `group` K channels per activation scale
+// (group == K: row mode, which may split K; part_bytes is then the int32 partial buffer).
+GemmPlan plan_gemm_i8(int M, int N, int K, int group);
 void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
-                    hipStream_t s);
+                    hipStream_t s, const SplitScratch &scratch = SplitScratch());
 void launch_attention(const bf16_t *Q, int64_t ldq, const bf16_t *K, int64_t ldk,
                       const bf16_t *V, int64_t ldv, bf16_t *O, int64_t ldo, int nq, int nk,
                       int heads, int head_dim, hipStream_t s);

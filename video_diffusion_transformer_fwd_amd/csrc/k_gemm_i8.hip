@@ -2,14 +2,25 @@
 //
 // C[M,N] = bf16(((sum_g float(acc_g) * SA[m,g]) * SW[n]) + bias[n]) with acc_g the exact int32
 // sum of QA[m,k] QW[n,k] over K group g (groups ascending, each float operation rounded, no
-// fused multiply-add), v_mfma_i32_32x32x32_i8: lane l supplies 16 consecutive k at 16(l/32) of
-// row l%32 for both operands; accumulator register i of lane l is C[8(i/4) + 4(l/32) + i%4][l%32].
+// fused multiply-add).  Row mode has one group (the whole K).
+//
+// v_mfma_i32_32x32x32_i8: lane l supplies 16 consecutive k at 16(l/32) of row l%32 of each
+// operand; accumulator register i of lane l is D[8(i/4) + 4(l/32) + i%4][l%32] with D = X Y^T.
+// The weight tile is passed as the first operand (D = C^T), so lane l holds row m = l%32 of C
+// at the four runs of 4 consecutive columns 8(i/4) + 4(l/32) + 0..3: one activation scale per
+// lane and 16-byte vector stores.
 //
 // Same pipeline as the bf16 product: a K slice is 128 int8 = 128 bytes per row, so the LDS tile
 // rows, their bank swizzle (chunk c of row r in slot c ^ ((r >> 1) & 7)) and the direct
-// global -> LDS staging are identical; three LDS stages; each 32-wide K step's fragment reads
-// are issued while the previous step's MFMAs run.  At each group end the int32 sums are folded
-// into a float32 total and cleared.
+// global -> LDS staging are identical; each 32-wide K step's fragment reads are issued while
+// the previous step's MFMAs run.
+//
+// Row mode may split K over S workgroups per tile: each stores its int32 partial tile, and a
+// second launch adds the S partials (integer addition: exact in any order) and dequantises, so
+// the result equals the unsplit product bit for bit.  Grouped mode folds each group's int32
+// sums into a float32 total in group order inside the kernel and is never split (the float
+// fold order is fixed).  The dequantising epilogue runs from an LDS band in a rolled loop, as
+// in the bf16 product.
 #include <hip/hip_runtime.h>
 
 #include "h3_internal.h"
@@ -43,24 +54,43 @@ struct GemmI8Cfg {
   static constexpr int TM = BM / WM / 32;
   static constexpr int TN = BN / WN / 32;
   static constexpr int STAGE = (BM + BN) * 128;
-  static constexpr size_t LDS_BYTES = NS * static_cast<size_t>(STAGE);
+  static constexpr int EPI_LD = BN + 4;              // float32 row stride of the epilogue band
+  static constexpr int EPI_BAND = WM * 32 * EPI_LD;  // one 32-row block of every wave row
+  static constexpr size_t EPI_BYTES = (static_cast<size_t>(EPI_BAND) + 2 * BN) * 4;
+  static constexpr size_t LDS_BYTES =
+      NS * static_cast<size_t>(STAGE) > EPI_BYTES ? NS * static_cast<size_t>(STAGE) : EPI_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "tile does not fit the 160 KB LDS");
+  static_assert(TM >= 1 && TN >= 1 && BM % (WM * 32) == 0 && BN % (WN * 32) == 0,
+                "wave tile must be whole 32x32 blocks");
 };
 
-template <int BM, int BN, int WM, int WN, int NS>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
-    const int8_t *__restrict__ QA, const float *__restrict__ SA, const int8_t *__restrict__ QW,
-    const float *__restrict__ SW, const bf16_t *__restrict__ bias, bf16_t *__restrict__ C,
-    int64_t ldc, int M, int N, int K, int group) {
+struct GemmI8Args {
+  const int8_t *QA;
+  const float *SA;  // [M, ngroups]
+  const int8_t *QW;
+  const float *SW;  // [N]
+  const bf16_t *bias;
+  bf16_t *C;
+  int64_t ldc;
+  int M, N, K, group;
+  int32_t *part;  // split-K int32 partials [S][M][N] (row mode)
+};
+
+template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
 #pragma clang fp contract(off)
+  static_assert(!(GROUPED && SPLIT > 1), "the grouped float fold is never split");
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
   extern __shared__ __align__(16) unsigned char smem8[];
 
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int tile_id = blockIdx.x / SPLIT;
+  const int split = blockIdx.x % SPLIT;
   int tm, tn;
   {
     const int ntiles = tiles_m * tiles_n;
-    int id = blockIdx.x;
+    int id = tile_id;
     if (ntiles % kXcds == 0) {
       const int per = ntiles / kXcds;
       id = (id % kXcds) * per + id / kXcds;
@@ -74,6 +104,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
     tn = r / gm;
   }
   const int m0 = tm * BM, n0 = tn * BN;
+  const int kc = g.K / SPLIT, kbeg = split * kc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
@@ -82,8 +113,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
   constexpr int ROW_BLOCKS = (BM + BN) / 8;
   constexpr int LOADS = ROW_BLOCKS / NW;
   static_assert(ROW_BLOCKS % NW == 0 && BM % 8 == 0, "row blocks must split evenly over waves");
-  const unsigned char *abase = reinterpret_cast<const unsigned char *>(QA);
-  const unsigned char *bbase = reinterpret_cast<const unsigned char *>(QW);
+  const unsigned char *abase = reinterpret_cast<const unsigned char *>(g.QA);
+  const unsigned char *bbase = reinterpret_cast<const unsigned char *>(g.QW);
   uint32_t goff[LOADS];
   {
     const int lrow = lane >> 3;
@@ -93,12 +124,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
       const int chunk = (lane & 7) ^ ((R >> 1) & 7);
       if (R < BM) {
         int r = m0 + R;
-        r = r < M ? r : M - 1;
-        goff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * K + chunk * 16);
+        r = r < g.M ? r : g.M - 1;
+        goff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * g.K + kbeg + chunk * 16);
       } else {
         int r = n0 + R - BM;
-        r = r < N ? r : N - 1;
-        goff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * K + chunk * 16);
+        r = r < g.N ? r : g.N - 1;
+        goff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * g.K + kbeg + chunk * 16);
       }
     }
   }
@@ -120,21 +151,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
 #pragma unroll
   for (int j = 0; j < TN; ++j) b_row[j] = (wn * TN + j) * 32 + fr;
 
-  const int row_l = fh * 4;
+  // lane holds C[m_l][n_l + 8q + e], e = 0..3, in accumulator registers 4q + e of each block
+  const int m_l = lane & 31, n_l = (lane >> 5) * 4;
   i32x16_t acc[TM][TN];
-  float tot[TM][TN][16];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      acc[i][j] = i32x16_t{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = i32x16_t{};
+  float tot[GROUPED ? TM : 1][GROUPED ? TN : 1][GROUPED ? 16 : 1];
+  if constexpr (GROUPED) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
-    }
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
+  }
 
-  const int KT = K / BK;
-  const int slices_per_group = group / BK;
-  const int ngroups = K / group;
+  const int KT = kc / BK;
+  const int slices_per_group = g.group / BK;
+  const int ngroups = g.K / g.group;
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < KT) issue_slice(p, p);
@@ -168,7 +204,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
       if (ks + 1 < BK / 32) {
 #pragma unroll
         for (int q = 0; q < TM + TN; ++q) {
@@ -178,26 +214,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
         if (TM * TN > TM + TN) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
       }
     }
-    // group end: tot += float(acc) * SA[m, g], then clear acc
-    if ((kt + 1) % slices_per_group == 0) {
-      const int g = (kt + 1) / slices_per_group - 1;
+    if constexpr (GROUPED) {
+      // group end: tot += float(acc) * SA[m, g], then clear acc (one scale per lane row)
+      if ((kt + 1) % slices_per_group == 0) {
+        const int gi = (kt + 1) / slices_per_group - 1;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int m = m0 + (wm * TM + i) * 32 + (r / 4) * 8 + row_l + (r % 4);
-          m = m < M ? m : M - 1;
-          const float sa = SA[static_cast<int64_t>(m) * ngroups + g];
+        for (int i = 0; i < TM; ++i) {
+          int m = m0 + (wm * TM + i) * 32 + m_l;
+          m = m < g.M ? m : g.M - 1;
+          const float sa = g.SA[static_cast<int64_t>(m) * ngroups + gi];
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            const float t = static_cast<float>(acc[i][j][r]) * sa;
-            tot[i][j][r] = tot[i][j][r] + t;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float t = static_cast<float>(acc[i][j][r]) * sa;
+              tot[i][j][r] = tot[i][j][r] + t;
+            }
+            acc[i][j] = i32x16_t{};
           }
         }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = i32x16_t{};
+      }
     }
     if (more)
       lds_dma_barrier<LOADS * (NS - 2)>();
@@ -205,33 +241,141 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(
       lds_dma_barrier<0>();
   }
 
-  const int col_l = lane & 31;
+  if constexpr (SPLIT > 1) {
+    // row-mode split: store this K piece's int32 partial tile, row-major [piece][M][N] (N % 4 == 0)
+    int32_t *part = g.part + static_cast<int64_t>(split) * g.M * g.N;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + (wn * TN + j) * 32 + col_l;
-    if (n >= N) continue;
-    const float sw = SW[n];
-    const float b = bf2f(bias[n]);
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + (wm * TM + i) * 32 + m_l;
+      if (m >= g.M) continue;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + (wm * TM + i) * 32 + (r / 4) * 8 + row_l + (r % 4);
-        if (m >= M) continue;
-        const float v = tot[i][j][r] * sw;
-        const float o = v + b;
-        C[static_cast<int64_t>(m) * ldc + n] = static_cast<bf16_t>(f2bf(o));
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (wn * TN + j) * 32 + q * 8 + n_l;
+          if (n < g.N)
+            *reinterpret_cast<int4 *>(part + static_cast<int64_t>(m) * g.N + n) =
+                make_int4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+    }
+    return;
+  }
+
+  // Epilogue through LDS: per-column weight scale and bias staged once; per 32-row block index
+  // i every wave writes its float32 activation-scaled sums (row mode: float(acc) * SA[m]) to a
+  // band of WM * 32 rows x BN columns, then all threads dequantise 4-column chunks of the band
+  // in a rolled loop: bf16((v * SW[n]) + bias[n]), 8-byte stores along the rows.
+  constexpr int LD = Cfg::EPI_LD;
+  float *band = reinterpret_cast<float *>(smem8);
+  float *ssw = band + Cfg::EPI_BAND;
+  float *sbias = ssw + BN;
+  __syncthreads();
+  for (int c = tid; c < BN; c += NT) {
+    const int n = n0 + c;
+    ssw[c] = n < g.N ? g.SW[n] : 0.f;
+    sbias[c] = n < g.N ? bf2f(g.bias[n]) : 0.f;
+  }
+  const bool vec = (g.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(g.C) % 8 == 0);
+  constexpr int CHUNKS_PER_ROW = BN / 4;
+  constexpr int BAND_CHUNKS = WM * 32 * CHUNKS_PER_ROW;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i > 0) __syncthreads();  // previous band fully read
+    float sa = 0.f;
+    if constexpr (!GROUPED) {
+      int m = m0 + (wm * TM + i) * 32 + m_l;
+      m = m < g.M ? m : g.M - 1;
+      sa = g.SA[m];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (GROUPED)
+            v[e] = tot[i][j][4 * q + e];
+          else
+            v[e] = static_cast<float>(acc[i][j][4 * q + e]) * sa;
+        }
+        *reinterpret_cast<float4 *>(band + (wm * 32 + m_l) * LD + (wn * TN + j) * 32 + q * 8 + n_l) =
+            make_float4(v[0], v[1], v[2], v[3]);
       }
+    __syncthreads();
+#pragma unroll 2
+    for (int c4 = tid; c4 < BAND_CHUNKS; c4 += NT) {
+      const int row = c4 / CHUNKS_PER_ROW, col = (c4 - row * CHUNKS_PER_ROW) * 4;
+      const int m = m0 + ((row >> 5) * TM + i) * 32 + (row & 31);
+      const int n = n0 + col;
+      if (m >= g.M || n >= g.N) continue;
+      const float4 a4 = *reinterpret_cast<const float4 *>(band + row * LD + col);
+      const float4 w4 = *reinterpret_cast<const float4 *>(ssw + col);
+      const float4 b4 = *reinterpret_cast<const float4 *>(sbias + col);
+      const float t0 = a4.x * w4.x, t1 = a4.y * w4.y, t2 = a4.z * w4.z, t3 = a4.w * w4.w;
+      const float o[4] = {t0 + b4.x, t1 + b4.y, t2 + b4.z, t3 + b4.w};
+      const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
+      if (vec && n + 3 < g.N) {
+        uint2 pk;
+        pk.x = pack_bf2(o[0], o[1]);
+        pk.y = pack_bf2(o[2], o[3]);
+        *reinterpret_cast<uint2 *>(g.C + off) = pk;
+      } else {
+        for (int e = 0; e < 4 && n + e < g.N; ++e) g.C[off + e] = static_cast<bf16_t>(f2bf(o[e]));
+      }
+    }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
-void run_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
-                 const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
-                 hipStream_t s) {
+// Adds the S int32 partials (exact) and dequantises: bf16(((float(sum) * SA[m]) * SW[n]) + b[n]).
+template <int S>
+__global__ __launch_bounds__(256) void splitk_i8_reduce_kernel(const int32_t *__restrict__ part,
+                                                               int M, int N,
+                                                               const float *__restrict__ SA,
+                                                               const float *__restrict__ SW,
+                                                               const bf16_t *__restrict__ bias,
+                                                               bf16_t *__restrict__ C, int64_t ldc) {
+#pragma clang fp contract(off)
+  const int64_t total4 = static_cast<int64_t>(M) * N / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total4) return;
+  const int64_t e0 = idx * 4;
+  const int m = static_cast<int>(e0 / N), n = static_cast<int>(e0 - static_cast<int64_t>(m) * N);
+  int4 s = *reinterpret_cast<const int4 *>(part + e0);
+#pragma unroll
+  for (int p = 1; p < S; ++p) {
+    const int4 t = *reinterpret_cast<const int4 *>(part + static_cast<int64_t>(p) * M * N + e0);
+    s.x += t.x;
+    s.y += t.y;
+    s.z += t.z;
+    s.w += t.w;
+  }
+  const float sa = SA[m];
+  const int sv[4] = {s.x, s.y, s.z, s.w};
+  float o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = static_cast<float>(sv[e]) * sa;
+    const float t = v * SW[n + e];
+    o[e] = t + bf2f(bias[n + e]);
+  }
+  bf16_t *dst = C + static_cast<int64_t>(m) * ldc + n;
+  if (ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) % 8) == 0) {
+    uint2 pk;
+    pk.x = pack_bf2(o[0], o[1]);
+    pk.y = pack_bf2(o[2], o[3]);
+    *reinterpret_cast<uint2 *>(dst) = pk;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = static_cast<bf16_t>(f2bf(o[e]));
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT>
+void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS>;
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS, GROUPED, SPLIT>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -239,15 +383,54 @@ void run_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const floa
                               static_cast<int>(Cfg::LDS_BYTES));
     attr_set = true;
   }
-  kern<<<tiles, Cfg::NT, Cfg::LDS_BYTES, s>>>(QA, SA, QW, SW, bias, C, ldc, M, N, K, group);
+  kern<<<tiles * SPLIT, Cfg::NT, Cfg::LDS_BYTES, s>>>(a);
+  if constexpr (SPLIT > 1) {
+    const int64_t total4 = static_cast<int64_t>(a.M) * a.N / 4;
+    splitk_i8_reduce_kernel<SPLIT><<<static_cast<int>((total4 + 255) / 256), 256, 0, s>>>(
+        a.part, a.M, a.N, a.SA, a.SW, a.bias, a.C, a.ldc);
+  }
 }
 
 }  // namespace
 
+// Tile choice (cfg * 8 + split), measured on the MI355X with random int8 operands:
+//   grouped                              128x128, 4 waves, three LDS stages (unsplit)
+//   row, M >= 4096                       384x192, 8 waves, two LDS stages
+//   row, 1024 <= M < 4096, N % 4 == 0    384x192, 8 waves, K split in 4
+//   row, otherwise                       128x128, 4 waves, three LDS stages
+// A split needs K % (128 * split) == 0 and N % 4 == 0.
+GemmPlan plan_gemm_i8(int M, int N, int K, int group) {
+  GemmPlan p{};
+  p.cfg = 0;
+  p.split = 1;
+  if (group == K) {
+    if (M >= 4096) {
+      p.cfg = 4;
+    } else if (M >= 1024) {
+      p.cfg = 4;
+      p.split = 4;
+    }
+  }
+  if (p.split > 1 && (K % (128 * p.split) != 0 || N % 4 != 0)) p.split = 1;
+  if (p.split > 1) p.part_bytes = static_cast<size_t>(p.split) * M * N * sizeof(int32_t);
+  return p;
+}
+
 void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
-                    hipStream_t s) {
-  run_gemm_i8<128, 128, 2, 2, 3>(QA, SA, QW, SW, bias, C, ldc, M, N, K, group, s);
+                    hipStream_t s, const SplitScratch &sc) {
+  GemmPlan p = plan_gemm_i8(M, N, K, group);
+  if (p.split > 1 && (!sc.part || p.part_bytes > sc.part_bytes)) p.split = 1;
+  GemmI8Args a{QA, SA, QW, SW, bias, C, ldc, M, N, K, group, reinterpret_cast<int32_t *>(sc.part)};
+  if (group != K) {
+    run_gemm_i8<128, 128, 2, 2, 3, true, 1>(a, s);
+    return;
+  }
+  switch (p.cfg * 8 + p.split) {
+    case 4 * 8 + 1: run_gemm_i8<384, 192, 4, 2, 2, false, 1>(a, s); break;
+    case 4 * 8 + 4: run_gemm_i8<384, 192, 4, 2, 2, false, 4>(a, s); break;
+    default: run_gemm_i8<128, 128, 2, 2, 3, false, 1>(a, s); break;
+  }
 }
 
 }  // namespace h3
