@@ -28,10 +28,12 @@ pytestmark = pytest.mark.gpu
 _MODELS = {}
 
 
-def gpu_model(name, n_blocks=2, fc2_mode="bf16"):
-    key = (name, n_blocks)
+def gpu_model(name, n_blocks=2, fc2_mode="bf16", frames=None):
+    key = (name, n_blocks, frames)
     if key not in _MODELS:
         w = dataclasses.replace(S.WORKLOADS[name], n_blocks=n_blocks, layers=0, fc2_mode=fc2_mode)
+        if frames is not None:
+            w = dataclasses.replace(w, frames=frames)
         _MODELS[key] = (w, DiTModel(w, with_int8=True), oracle_model(w))
     return _MODELS[key]
 
@@ -146,11 +148,13 @@ def test_block_rejects_bad_arguments():
                            model.ctx_kv[0], ws)
 
 
-def test_int8_row_split_k_bit_identical_to_unsplit():
-    # inside the block the 1536-row int8 FC2 splits K over four workgroups per tile and adds
-    # the int32 partials in a second launch; the standalone product runs unsplit.  Integer
-    # partial sums are exact, so both must give the same bf16 bits from the same quantised input.
-    w, model, om = gpu_model("512sq_22f")
+@pytest.mark.parametrize("frames", [22, 5])
+def test_int8_row_split_k_bit_identical_to_unsplit(frames):
+    # inside the block the int8 FC2 at 1536 rows (22 frames: 384x192 tiles) or 512 rows (5
+    # frames: 192x192 tiles) splits K over four workgroups per tile and adds the int32 partials
+    # in a second launch; the standalone product runs unsplit.  Integer partial sums are exact,
+    # so both must give the same bf16 bits from the same quantised input.
+    w, model, om = gpu_model("512sq_22f", frames=frames)
     n, d, F = model.geo.n_tokens, w.d_model, w.ffn_dim
     mod, _ = dit.modulation(om["global"], 0.75)
     mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
@@ -167,7 +171,7 @@ def test_int8_row_split_k_bit_identical_to_unsplit():
     torch.cuda.synchronize()
     assert np.array_equal(bits(out), bits(m_blk))
     # and both equal the exact integer product dequantised by the oracle's rule, on sampled rows
-    rows = np.array([0, 1, 517, 1024, n - 1])
+    rows = np.array([0, 1, 317, n // 2 + 5, n - 1])
     qa = hq[torch.as_tensor(rows, device=DEV)].cpu().numpy()
     sa = hs[torch.as_tensor(rows, device=DEV)].cpu().numpy()
     acc = dit.int8_accumulate(qa, blk["fc2_q"].cpu().numpy(), None)

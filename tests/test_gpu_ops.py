@@ -228,7 +228,10 @@ def test_quant_rows_bit_exact(rows, K, group):
 
 
 @pytest.mark.parametrize("M,N,K,group", [(300, 256, 2048, 2048), (300, 256, 2048, 1024),
-                                         (1536, 3072, 12288, 12288), (130, 640, 4096, 1024)])
+                                         (1536, 3072, 12288, 12288), (130, 640, 4096, 1024),
+                                         (4100, 700, 2048, 2048),    # 256x256 row tiles, ragged
+                                         (4100, 400, 2048, 1024),    # 192x192 grouped tiles, ragged
+                                         (700, 520, 4096, 4096)])    # 192x192 row tiles (unsplit)
 def test_gemm_i8_bit_exact(M, N, K, group):
     rng = np.random.default_rng(M + N + K + group)
     qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)

@@ -182,6 +182,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
   for (int kt = 0; kt < KT; ++kt) {
     const unsigned char *st = smem8 + (kt % NS) * Cfg::STAGE;
     const bool more = kt + NS - 1 < KT;
+    // grouped: this slice ends a group -> fetch the group's activation scales now (before this
+    // iteration's slice loads, so waiting for them never waits for those) and use them after
+    // the MFMAs
+    const bool fold = GROUPED && (kt + 1) % slices_per_group == 0;
+    float sa_g[GROUPED ? TM : 1];
+    if constexpr (GROUPED) {
+      if (fold) {
+        const int gi = (kt + 1) / slices_per_group - 1;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          int m = m0 + (wm * TM + i) * 32 + m_l;
+          m = m < g.M ? m : g.M - 1;
+          sa_g[i] = g.SA[static_cast<int64_t>(m) * ngroups + gi];
+        }
+      }
+    }
     if (more) issue_slice((kt + NS - 1) % NS, kt + NS - 1);
     i32x4_t af[2][TM], bfr[2][TN];
 #pragma unroll
@@ -216,13 +232,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
     }
     if constexpr (GROUPED) {
       // group end: tot += float(acc) * SA[m, g], then clear acc (one scale per lane row)
-      if ((kt + 1) % slices_per_group == 0) {
-        const int gi = (kt + 1) / slices_per_group - 1;
+      if (fold) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          int m = m0 + (wm * TM + i) * 32 + m_l;
-          m = m < g.M ? m : g.M - 1;
-          const float sa = g.SA[static_cast<int64_t>(m) * ngroups + gi];
+          const float sa = sa_g[i];
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -394,22 +407,27 @@ void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
 }  // namespace
 
 // Tile choice (cfg * 8 + split), measured on the MI355X with random int8 operands:
-//   grouped                              128x128, 4 waves, three LDS stages (unsplit)
-//   row, M >= 4096                       384x192, 8 waves, two LDS stages
-//   row, 1024 <= M < 4096, N % 4 == 0    384x192, 8 waves, K split in 4
-//   row, otherwise                       128x128, 4 waves, three LDS stages
+//   grouped, M >= 4096                   192x192, 4 waves, three LDS stages (never split)
+//   grouped, otherwise                   128x256, 4 waves, three LDS stages
+//   row, M >= 4096                       256x256, 8 waves, two LDS stages
+//   row, 1024 <= M < 4096                384x192, 8 waves, K split in 4
+//   row, 192 <= M < 1024                 192x192, 4 waves, K split in 4
+//   row, otherwise                       128x128, 4 waves
 // A split needs K % (128 * split) == 0 and N % 4 == 0.
 GemmPlan plan_gemm_i8(int M, int N, int K, int group) {
   GemmPlan p{};
   p.cfg = 0;
   p.split = 1;
-  if (group == K) {
-    if (M >= 4096) {
-      p.cfg = 4;
-    } else if (M >= 1024) {
-      p.cfg = 4;
-      p.split = 4;
-    }
+  if (group != K) {
+    p.cfg = M >= 4096 ? 1 : 3;
+  } else if (M >= 4096) {
+    p.cfg = 2;
+  } else if (M >= 1024) {
+    p.cfg = 4;
+    p.split = 4;
+  } else if (M >= 192) {
+    p.cfg = 1;
+    p.split = 4;
   }
   if (p.split > 1 && (K % (128 * p.split) != 0 || N % 4 != 0)) p.split = 1;
   if (p.split > 1) p.part_bytes = static_cast<size_t>(p.split) * M * N * sizeof(int32_t);
@@ -423,12 +441,18 @@ void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const f
   if (p.split > 1 && (!sc.part || p.part_bytes > sc.part_bytes)) p.split = 1;
   GemmI8Args a{QA, SA, QW, SW, bias, C, ldc, M, N, K, group, reinterpret_cast<int32_t *>(sc.part)};
   if (group != K) {
-    run_gemm_i8<128, 128, 2, 2, 3, true, 1>(a, s);
+    if (p.cfg == 1)
+      run_gemm_i8<192, 192, 2, 2, 3, true, 1>(a, s);
+    else
+      run_gemm_i8<128, 256, 2, 2, 3, true, 1>(a, s);
     return;
   }
   switch (p.cfg * 8 + p.split) {
+    case 2 * 8 + 1: run_gemm_i8<256, 256, 2, 4, 2, false, 1>(a, s); break;
     case 4 * 8 + 1: run_gemm_i8<384, 192, 4, 2, 2, false, 1>(a, s); break;
     case 4 * 8 + 4: run_gemm_i8<384, 192, 4, 2, 2, false, 4>(a, s); break;
+    case 1 * 8 + 1: run_gemm_i8<192, 192, 2, 2, 3, false, 1>(a, s); break;
+    case 1 * 8 + 4: run_gemm_i8<192, 192, 2, 2, 3, false, 4>(a, s); break;
     default: run_gemm_i8<128, 128, 2, 2, 3, false, 1>(a, s); break;
   }
 }
