@@ -212,7 +212,8 @@ def test_token_merge_restore_exact(f, gh, gw, d):
 
 # ------------------------------------------------------------------ int8 FC2
 @pytest.mark.parametrize("rows,K,group", [(300, 2048, 2048), (300, 2048, 1024), (1536, 12288, 12288),
-                                          (64, 20480, 1024)])
+                                          (64, 20480, 1024), (33, 20480, 20480),
+                                          (70, 7168, 7168)])   # K / 1024 = 7: the generic row kernel
 def test_quant_rows_bit_exact(rows, K, group):
     rng = np.random.default_rng(rows + K + group)
     X = randn_bf16(rng, (rows, K), 0.7)

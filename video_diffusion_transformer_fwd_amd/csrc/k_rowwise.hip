@@ -296,54 +296,102 @@ __device__ __forceinline__ uint32_t quant4(const float *x, float s) {
   return w;
 }
 
-__global__ __launch_bounds__(256) void quant_rows_kernel(const bf16_t *__restrict__ X,
-                                                         int8_t *__restrict__ Q,
-                                                         float *__restrict__ S, int rows,
-                                                         int K, int group) {
+// group == 1024: one wave per (row, group), 16 channels per lane.
+__global__ __launch_bounds__(256) void quant_groups_kernel(const bf16_t *__restrict__ X,
+                                                           int8_t *__restrict__ Q,
+                                                           float *__restrict__ S, int rows, int K) {
+  const int lane = threadIdx.x & 63;
+  const int ng = K / 1024;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);  // row * ng + g
+  if (item >= static_cast<int64_t>(rows) * ng) return;
+  const int64_t row = item / ng;
+  const int g = static_cast<int>(item - row * ng);
+  const bf16_t *xr = X + row * K;
+  int8_t *qr = Q + row * K;
+  float a[16];
+  const int e0 = g * 1024 + lane * 8, e1 = e0 + 512;
+  unpack8(*reinterpret_cast<const uint4 *>(xr + e0), a);
+  unpack8(*reinterpret_cast<const uint4 *>(xr + e1), a + 8);
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(a[k]));
+  m = wave_max(m);
+  const float s = m / 127.0f;
+  uint2 w0, w1;
+  w0.x = quant4(a, s); w0.y = quant4(a + 4, s);
+  w1.x = quant4(a + 8, s); w1.y = quant4(a + 12, s);
+  *reinterpret_cast<uint2 *>(qr + e0) = w0;
+  *reinterpret_cast<uint2 *>(qr + e1) = w1;
+  if (lane == 0) S[item] = s;
+}
+
+// Row mode with K = 1024 V: 128 threads (two waves) per row, the row held in registers (V
+// 16-byte vectors per thread, consecutive threads on consecutive vectors), one pass over HBM.
+template <int V>
+__global__ __launch_bounds__(128) void quant_row_kernel(const bf16_t *__restrict__ X,
+                                                        int8_t *__restrict__ Q,
+                                                        float *__restrict__ S) {
+  constexpr int K = V * 1024;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const bf16_t *xr = X + row * K;
+  int8_t *qr = Q + row * K;
+  uint4 raw[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) raw[v] = *reinterpret_cast<const uint4 *>(xr + (v * 128 + tid) * 8);
+  float m = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float a[8];
+    unpack8(raw[v], a);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(a[k]));
+  }
+  m = wave_max(m);
+  __shared__ float red[2];
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(red[0], red[1]);
+  const float s = m / 127.0f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float a[8];
+    unpack8(raw[v], a);
+    uint2 w;
+    w.x = quant4(a, s);
+    w.y = quant4(a + 4, s);
+    *reinterpret_cast<uint2 *>(qr + (v * 128 + tid) * 8) = w;
+  }
+  if (tid == 0) S[row] = s;
+}
+
+// Row mode, any K (multiple of 512): one wave per row, two passes over the row.
+__global__ __launch_bounds__(256) void quant_row_any_kernel(const bf16_t *__restrict__ X,
+                                                            int8_t *__restrict__ Q,
+                                                            float *__restrict__ S, int rows, int K) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const bf16_t *xr = X + static_cast<size_t>(row) * K;
   int8_t *qr = Q + static_cast<size_t>(row) * K;
-  if (group == 1024) {
-    const int ng = K / 1024;
-    for (int g = 0; g < ng; ++g) {
-      float a[16];
-      const int e0 = g * 1024 + lane * 8, e1 = e0 + 512;
-      unpack8(*reinterpret_cast<const uint4 *>(xr + e0), a);
-      unpack8(*reinterpret_cast<const uint4 *>(xr + e1), a + 8);
-      float m = 0.f;
+  float m = 0.f;
+  for (int e = lane * 8; e < K; e += 512) {
+    float a[8];
+    unpack8(*reinterpret_cast<const uint4 *>(xr + e), a);
 #pragma unroll
-      for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(a[k]));
-      m = wave_max(m);
-      const float s = m / 127.0f;
-      uint2 w0, w1;
-      w0.x = quant4(a, s); w0.y = quant4(a + 4, s);
-      w1.x = quant4(a + 8, s); w1.y = quant4(a + 12, s);
-      *reinterpret_cast<uint2 *>(qr + e0) = w0;
-      *reinterpret_cast<uint2 *>(qr + e1) = w1;
-      if (lane == 0) S[static_cast<size_t>(row) * ng + g] = s;
-    }
-  } else {
-    float m = 0.f;
-    for (int e = lane * 8; e < K; e += 512) {
-      float a[8];
-      unpack8(*reinterpret_cast<const uint4 *>(xr + e), a);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(a[k]));
-    }
-    m = wave_max(m);
-    const float s = m / 127.0f;
-    for (int e = lane * 8; e < K; e += 512) {
-      float a[8];
-      unpack8(*reinterpret_cast<const uint4 *>(xr + e), a);
-      uint2 w;
-      w.x = quant4(a, s);
-      w.y = quant4(a + 4, s);
-      *reinterpret_cast<uint2 *>(qr + e) = w;
-    }
-    if (lane == 0) S[row] = s;
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(a[k]));
   }
+  m = wave_max(m);
+  const float s = m / 127.0f;
+  for (int e = lane * 8; e < K; e += 512) {
+    float a[8];
+    unpack8(*reinterpret_cast<const uint4 *>(xr + e), a);
+    uint2 w;
+    w.x = quant4(a, s);
+    w.y = quant4(a + 4, s);
+    *reinterpret_cast<uint2 *>(qr + e) = w;
+  }
+  if (lane == 0) S[row] = s;
 }
 
 // ------------------------------------------------------------------ small kernels
@@ -453,7 +501,19 @@ void launch_euler(float *x, const float *v, float dt, int64_t n, hipStream_t s) 
 
 void launch_quant_rows(const bf16_t *X, int8_t *Q, float *S, int rows, int K, int group,
                        hipStream_t s) {
-  quant_rows_kernel<<<(rows + 3) / 4, 256, 0, s>>>(X, Q, S, rows, K, group);
+  if (group == 1024) {
+    const int64_t items = static_cast<int64_t>(rows) * (K / 1024);
+    quant_groups_kernel<<<static_cast<int>((items + 3) / 4), 256, 0, s>>>(X, Q, S, rows, K);
+    return;
+  }
+  switch (K % 1024 == 0 ? K / 1024 : 0) {
+#define H3_QROW(V) \
+  case V: quant_row_kernel<V><<<rows, 128, 0, s>>>(X, Q, S); return;
+    H3_QROW(1) H3_QROW(2) H3_QROW(3) H3_QROW(4) H3_QROW(5) H3_QROW(6) H3_QROW(8) H3_QROW(10)
+    H3_QROW(12) H3_QROW(16) H3_QROW(20)
+#undef H3_QROW
+    default: quant_row_any_kernel<<<(rows + 3) / 4, 256, 0, s>>>(X, Q, S, rows, K);
+  }
 }
 
 void launch_f32_to_bf16(const float *src, bf16_t *dst, int64_t n, hipStream_t s) {
