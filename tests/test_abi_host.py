@@ -166,3 +166,18 @@ def test_entry_points_reject_bad_arguments_without_launching(lib):
     assert L.h3_token_reduce(2, ctypes.byref(g), 512, 16, 16, 32, None) == B.H3_EINVAL
     assert L.h3_token_reduce(0, ctypes.byref(g), 512, 16, None, 16, None) == B.H3_EINVAL
     assert b"alias" in L.h3_last_error()
+
+
+def test_864x480_geometry_and_odd_width_pairing(lib):
+    # 864x480 output at 22 frames: a 15 x 27 token grid (odd width) of 6 latent frames
+    from video_diffusion_transformer_fwd_amd.runtime import Geometry
+    w = S.WORKLOADS["864x480_22f"]
+    geo = Geometry(w)
+    assert (geo.f_lat, geo.grid_h, geo.grid_w, geo.scale, geo.n_tokens) == (6, 15, 27, 1.0, 2430)
+    assert host.token_grid(864, 480) == (15, 27, 1.0)
+    plan = B.h3_token_plan(geo.f_lat, geo.grid_h, geo.grid_w, 0, 45)
+    assert plan["n_reduced"] == 6 * 15 * 14 == 1260
+    # the 14th reduced token of every grid row is the last column paired with itself
+    last = plan["pairs"].reshape(6 * 15, 14, 2)[:, 13]
+    np.testing.assert_array_equal(last[:, 0], last[:, 1])
+    np.testing.assert_array_equal(last[:, 0] % 27, 26)

@@ -140,3 +140,21 @@ def test_512sq_token_reduction_loop_reduced_depth():
     model = DiTModel(w)
     om = oracle_model(w)
     loop_parity(w, model, om, {"token_reduction": True}, 2, 1, [0, 1, 2, 3, 4])
+
+
+def test_864x480_loop_reduced_depth():
+    # the 864x480x22 shape (2430 tokens: ragged tiles in every product and attention) with 2
+    # blocks, --steps 4 --reuse 1
+    w = dataclasses.replace(S.WORKLOADS["864x480_22f"], n_blocks=2)
+    model = DiTModel(w)
+    assert model.geo.n_tokens == 2430
+    om = oracle_model(w)
+    loop_parity(w, model, om, {}, 4, 1, [0, 1])
+
+
+def test_864x480_token_reduction_loop_reduced_depth():
+    # odd grid width 27: token pairing leaves the last column of every row alone (2430 -> 1260)
+    w = dataclasses.replace(S.WORKLOADS["864x480_22f_tr"], n_blocks=5, layers=0, steps=2, reuse=1)
+    model = DiTModel(w)
+    om = oracle_model(w)
+    loop_parity(w, model, om, {"token_reduction": True}, 2, 1, [0, 1, 2, 3, 4])

@@ -98,6 +98,11 @@ WORKLOADS = {
     # 768x1344, 243 frames, one forward
     "768x1344_243f": Workload("768x1344_243f", 1344, 768, 243, 5120, 40, 20480, 512, 50,
                               steps=1),
+    # 864x480 (15 x 27 token grid: odd width), 22 frames, --steps 4 --reuse 1
+    "864x480_22f": Workload("864x480_22f", 864, 480, 22, 3072, 24, 12288, 256, 50, steps=4),
+    # same shape with --steps 20 --layers 45 --reuse 2 --token-reduction (singleton last column)
+    "864x480_22f_tr": Workload("864x480_22f_tr", 864, 480, 22, 3072, 24, 12288, 256, 50,
+                               steps=20, reuse=2, layers=45, token_reduction=True),
 }
 
 STD = 0.02
