@@ -25,6 +25,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -174,6 +175,7 @@ def main():
     fwd_flops_total = sum(2 * r * d_ * 4 * d_ + 4 * r * r * d_ + 4 * r * L_ * d_ + 4 * r * d_ * d_
                           + 4 * r * d_ * F_ for r in timed_rows)
     actual_tok_blocks = sum(timed_rows) / elapsed
+    peak = PEAK_INT8_TOPS if w.int8_linear else PEAK_BF16_TFLOPS
     out = {
         "metric": "DiT denoise-step ms & tokens·blocks/s at 512²×22f; % bf16 MFMA peak",
         "value": round(tok_blocks, 1),
@@ -185,20 +187,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16+int8" if (w.int8_linear or w.fc2_mode != "bf16") else "bf16",
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) latent)",
         "config": {"workload": w.name, "width": w.width, "height": w.height, "frames": w.frames,
                    "tokens": n, "blocks": nb_act, "d_model": w.d_model, "heads": w.n_heads,
                    "ffn": w.ffn_dim, "ctx_len": w.ctx_len, "steps": w.steps, "reuse": w.reuse,
-                   "fc2": w.fc2_mode, "token_reduction": w.token_reduction},
+                   "fc2": w.fc2_mode, "int8_qkv_fc1": w.int8_linear,
+                   "token_reduction": w.token_reduction},
         "ms_per_fresh_eval": round(elapsed * 1e3 / max(n_evals, 1), 3),
         "actual_tokens_blocks_per_s": round(actual_tok_blocks, 1),
         "mfma_frac_forward": round(fwd_flops_total / elapsed / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "fc1_gemm (bf16 GEMM + GELU epilogue)",
-                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma",
+                     "kernel": ("fc1_gemm (int8 GEMM + dequant + GELU epilogue)" if w.int8_linear
+                                else "fc1_gemm (bf16 GEMM + GELU epilogue)"),
+                     "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "TOP/s" if w.int8_linear else "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
                      "flops_per_launch": fc1_flops, "avg_launch_ms": round(fc1_avg_ms, 5),
-                     "launches": fc1_launches, "traffic": traffic_for("k_gemm.hip")},
+                     "launches": fc1_launches,
+                     "traffic": None if w.int8_linear else traffic_for("k_gemm.hip")},
     }
     if not args.no_cpu:
         del model

@@ -156,6 +156,12 @@ typedef struct h3_block_weights {
   const void *fc2_w, *fc2_b;  /* [d, F], [d] */
   void *fc2_q;   /* int8 [d, F] or NULL: written by h3_quantize_fc2_weights */
   void *fc2_s;   /* float [d] or NULL: per-output-channel scales, same */
+  /* int8 copies for the int8 QKV / FC1 path (h3_run_opts.int8_linear), or NULL; written by
+   * h3_quantize_linear_weights with the same per-output-channel rule */
+  void *qkvq_q;  /* int8 [4d, d] */
+  void *qkvq_s;  /* float [4d] */
+  void *fc1_q;   /* int8 [F, d] */
+  void *fc1_s;   /* float [F] */
 } h3_block_weights;
 
 typedef struct h3_model h3_model;
@@ -183,6 +189,12 @@ typedef struct h3_run_opts {
   int32_t fused_cross_block;  /* 1: MLP gate + next block's AdaLN in one kernel; 0: two kernels, bit-identical */
   int32_t qk_norm;            /* 1: per-head RMSNorm of Q and K before RoPE (P3 "the int8 path") */
   int32_t token_reduction;    /* 1: horizontal token pairing per h3_token_plan (forward only) */
+  int32_t int8_linear;        /* 1: int8 QKV and FC1 products (P3 "the int8 path": quantised QKV
+                               * projections and the int8 MLP, with the activation quantisation
+                               * fused into the gated-AdaLN kernel).  The AdaLN rows n1, n2 are
+                               * rounded to bf16 and quantised with one scale per token row
+                               * (absmax / 127, the rule of h3_quant_rows); the weights need the
+                               * copies of h3_quantize_linear_weights. */
 } h3_run_opts;
 
 /* Tokens of a geometry (validates it). */
@@ -197,7 +209,8 @@ int32_t h3_workspace_size(const h3_model *m, int32_t n_tokens, const h3_run_opts
  * h3_dit_block_fwd, for inspection.  Each is [n_tokens, width] bf16 unless noted:
  * n1 [N,d], qkvq [N,4d] (q,k after RMSNorm+RoPE), attn [N,2d] (self | cross outputs),
  * y [N,d] (summed output projection), n2 [N,d], h [N,F] (GELU output), m [N,d] (FC2
- * output), hq int8 [N,F], hs float [N, F/1024 or 1]. */
+ * output), hq int8 [N,F], hs float [N, F/1024 or 1].  With int8_linear, n1 and n2 hold the
+ * row-quantised AdaLN outputs: int8 [N,d] followed by float [N]. */
 typedef struct h3_ws_layout {
   size_t n1, qkvq, attn, y, n2, h, m, hq, hs, rope, total;
 } h3_ws_layout;
@@ -214,6 +227,11 @@ int32_t h3_prepare_context(const h3_model *m, const void *ctx, void *ctx_kv, voi
  * division, ties to even, s = 0 -> q = 0.  Writes blocks[b].fc2_q / fc2_s (must be set). */
 int32_t h3_quantize_fc2_weights(const h3_model *m, void *stream);
 
+/* Same rule for the QKV(+cross Q) and FC1 weights of every block: writes
+ * blocks[b].qkvq_q / qkvq_s ([4d, d] int8, [4d] float) and fc1_q / fc1_s ([F, d], [F]) (all
+ * must be set); needed by h3_run_opts.int8_linear. */
+int32_t h3_quantize_linear_weights(const h3_model *m, void *stream);
+
 /* AdaLN parameters of every block for one timestep sigma (reading of P3 "DiT fusions").
  * mod (device, float [n_blocks, 6, d]) rows sh1 sc1 g1 sh2 sc2 g2; mod_final (device,
  * float [2, d]) rows shift, scale.  ws: at least h3_workspace_size bytes. */
@@ -229,7 +247,10 @@ int32_t h3_modulation(const h3_model *m, float sigma, float *mod, float *mod_fin
  * x (device, bf16 [N, d], in/out) with N = h3_geom_tokens(geom); n1_in (device, bf16 [N,d]
  * or NULL); n1_next (device, bf16 [N,d] or NULL, then mod_next != NULL: float [6,d] or
  * [2,d] rows shift, scale -- the next AdaLN's parameters); mod (device, float [6, d]);
- * ctx_kv (device, bf16 [2, ctx_len, d]: this block's K then V).  block in [0, n_blocks). */
+ * ctx_kv (device, bf16 [2, ctx_len, d]: this block's K then V).  block in [0, n_blocks).
+ * With o->int8_linear, n1_in and n1_next hold the quantised AdaLN row instead: int8 [N, d]
+ * followed (at byte N*d) by the float32 row scales [N] -- N*d + 4N bytes; QKV and FC1 run as
+ * int8 products with the block's qkvq_q / fc1_q copies. */
 int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
                          const h3_run_opts *o, void *x, const void *n1_in, void *n1_next,
                          const float *mod, const float *mod_next, const void *ctx_kv,
@@ -287,7 +308,7 @@ int32_t h3_attention(const void *Q, int64_t ldq, const void *K, int64_t ldk, con
 /* Dynamic int8 quantisation of rows (P2 §4 per-row scale; P3 "the int8 path" one scale per
  * 1024 channels): X (device, bf16 [rows, K]) -> Q (device, int8 [rows, K]) and S (device,
  * float [rows, K / group]); s = absmax / 127 in float32, q = clamp(rint(x / s), +-127),
- * ties to even, s = 0 -> q = 0.  group = K (per row) or 1024; K % 1024 == 0. */
+ * ties to even, s = 0 -> q = 0.  group = K (per row; K % 512 == 0) or 1024 (K % 1024 == 0). */
 int32_t h3_quant_rows(const void *X, void *Q, float *S, int32_t rows, int32_t K,
                       int32_t group, void *stream);
 
@@ -295,10 +316,12 @@ int32_t h3_quant_rows(const void *X, void *Q, float *S, int32_t rows, int32_t K,
  * acc_g = sum_{k in group g} QA[r,k] QW[n,k] (exact int32), out = bf16(((sum_g
  * float(acc_g) * SA[r,g]) * SW[n]) + bias[n]), groups ascending, each float operation
  * rounded (no fused multiply-add).  QA int8 [M, K], QW int8 [N, K], SA float [M, K/group],
- * SW float [N], bias bf16 [N], C bf16 [M, ldc].  group = K or 1024; K % 1024 == 0. */
+ * SW float [N], bias bf16 [N], C bf16 [M, ldc].  group = K (K % 128 == 0) or 1024
+ * (K % 1024 == 0).  epilogue: H3_EPI_NONE, or H3_EPI_GELU (exact-erf GELU of the dequantised value before the
+ * bf16 rounding: the int8 FC1 of P3 "the int8 path"). */
 int32_t h3_gemm_i8(const void *QA, const float *SA, const void *QW, const float *SW,
                    const void *bias, void *C, int64_t ldc, int32_t M, int32_t N, int32_t K,
-                   int32_t group, void *stream);
+                   int32_t group, int32_t epilogue, void *stream);
 
 /* Gated residual and/or AdaLN on rows of width d_model (P3 "DiT fusions and memory"):
  *   if y != NULL:     x_out = bf16(x + gate * y)                      (gate: device float [d])
@@ -310,6 +333,16 @@ int32_t h3_gemm_i8(const void *QA, const float *SA, const void *QW, const float 
 int32_t h3_gate_adaln(const void *x, const void *y, const float *gate, void *x_out,
                       const float *shift, const float *scale, void *n_out, int32_t rows,
                       int32_t d_model, void *stream);
+
+/* The same with the AdaLN output quantised instead of stored (P3 "the int8 path": the
+ * activation quantisation fused into the gated-AdaLN kernel): the bf16-rounded AdaLN row is
+ * written as q_out (device int8 [rows, d_model]) and s_out (device float [rows]) by the rule
+ * of h3_quant_rows with group = d_model -- bit-identical to h3_gate_adaln into n_out followed
+ * by h3_quant_rows(n_out).  shift, scale, q_out, s_out must be set; y / gate / x_out as in
+ * h3_gate_adaln. */
+int32_t h3_gate_adaln_quant(const void *x, const void *y, const float *gate, void *x_out,
+                            const float *shift, const float *scale, void *q_out, float *s_out,
+                            int32_t rows, int32_t d_model, void *stream);
 
 /* RoPE table of a geometry: table (device, float2 [n_tokens, head_dim/2]) = (cos, sin) of
  * coord * 10000^(-2j/D_axis) for the [t | h | w] channel slices of D - 4 floor(D/6),

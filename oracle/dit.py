@@ -256,6 +256,23 @@ def dequant(acc, sa, sw, bias):
     return (out + np.asarray(bias, np.float32)[None, :]).astype(np.float32)
 
 
+def linear_int8(a, w, b):
+    """int8 product of a row-quantised activation and per-output-channel int8 weights.
+
+    P3 "the int8 path": the QKV projections and the MLP run as int8 products, activations
+    quantised dynamically with per-output-channel weight scales, the quantisation fused into
+    the gated-AdaLN kernel, which reads the rows as bf16 and writes int8.
+    Reading: the activation is the bf16-rounded value the bf16 path would store; one scale
+    per token row; quantisation, integer sums and dequantisation as in ``quantize_rows``,
+    ``int8_accumulate`` and ``dequant`` (one group).  Returns the float32 result as float64.
+    """
+    ab = f32_to_bf16(np.asarray(a, dtype=np.float32))
+    qa, sa = quantize_rows(ab, None)
+    qw, sw = quantize_weight(np.asarray(w, dtype=np.float32))
+    acc = int8_accumulate(qa, qw, None)
+    return dequant(acc, sa, sw[:, 0], np.asarray(b, np.float32)).astype(np.float64)
+
+
 def fc2(h, blk, mode="bf16", group=1024):
     """FC2 of the MLP in one of three modes: 'bf16' (float64 product), 'row', 'grouped'.
 
@@ -299,7 +316,7 @@ def context_kv(ctx, blk):
 
 
 def block_forward(x, blk, mod_b, ctx, coords, n_heads, qk_norm=True, fc2_mode="bf16",
-                  trace=None):
+                  trace=None, int8_linear=False):
     """One DiT block on the residual stream x [N, d].
 
     P3 "DiT fusions": each active block has an attention residual gate followed by the MLP
@@ -313,13 +330,15 @@ def block_forward(x, blk, mod_b, ctx, coords, n_heads, qk_norm=True, fc2_mode="b
       y  = O Wo^T + bo + Oc Woc^T + boc;  x <- x + g1 y
       n2 = AdaLN(x; sh2, sc2);  h = GELU(n2 W1^T + b1);  m = FC2(h);  x <- x + g2 m
     ``mod_b`` is [6, d] (sh1, sc1, g1, sh2, sc2, g2).  ``trace`` (a dict) receives the
-    intermediates when given.
+    intermediates when given.  ``int8_linear``: the QKV, cross-attention Q and FC1 products
+    run as ``linear_int8`` (P3 "the int8 path").
     """
+    lin = linear_int8 if int8_linear else linear
     n, d = x.shape
     dh = d // n_heads
     sh1, sc1, g1, sh2, sc2, g2 = mod_b
     n1 = adaln(x, sh1, sc1)
-    qkv = linear(n1, blk["qkv_w"], blk["qkv_b"])
+    qkv = lin(n1, blk["qkv_w"], blk["qkv_b"])
     q = qkv[:, :d].reshape(n, n_heads, dh)
     k = qkv[:, d:2 * d].reshape(n, n_heads, dh)
     v = qkv[:, 2 * d:].reshape(n, n_heads, dh)
@@ -330,14 +349,14 @@ def block_forward(x, blk, mod_b, ctx, coords, n_heads, qk_norm=True, fc2_mode="b
     k = rope_apply(k, coords)
     o = attention(q, k, v).reshape(n, d)
     kc, vc = context_kv(ctx, blk)
-    qc = linear(n1, blk["qc_w"], blk["qc_b"])
+    qc = lin(n1, blk["qc_w"], blk["qc_b"])
     lc = ctx.shape[0]
     oc = attention(qc.reshape(n, n_heads, dh), kc.reshape(lc, n_heads, dh),
                    vc.reshape(lc, n_heads, dh)).reshape(n, d)
     y = linear(o, blk["o_w"], blk["o_b"]) + linear(oc, blk["oc_w"], blk["oc_b"])
     x1 = gated_residual(x, g1, y)
     n2 = adaln(x1, sh2, sc2)
-    h = gelu(linear(n2, blk["fc1_w"], blk["fc1_b"]))
+    h = gelu(lin(n2, blk["fc1_w"], blk["fc1_b"]))
     m = fc2(h, blk, fc2_mode)
     x2 = gated_residual(x1, g2, m)
     if trace is not None:
@@ -358,7 +377,7 @@ def patch_embed(latent, g):
 
 # --------------------------------------------------------------------------- forward / loop
 def dit_forward(latent, model, sigma, active, geom, n_heads, eval_index=0, qk_norm=True,
-                fc2_mode="bf16", token_reduction=False, trace=None):
+                fc2_mode="bf16", token_reduction=False, trace=None, int8_linear=False):
     """One fresh denoiser evaluation: latent [N, C] -> velocity [N, C].
 
     ``geom`` = dict(f_lat, grid_h, grid_w, scale).  ``active`` = ascending block indices.
@@ -380,7 +399,8 @@ def dit_forward(latent, model, sigma, active, geom, n_heads, eval_index=0, qk_no
         if plan is not None and saved is not None and pos == plan["restore_before"] - 1:
             x = token_restore(saved, x, plan["pairs"])
             saved, coords = None, full
-        x = block_forward(x, blocks[b], mod[b], ctx, coords, n_heads, qk_norm, fc2_mode)
+        x = block_forward(x, blocks[b], mod[b], ctx, coords, n_heads, qk_norm, fc2_mode,
+                          int8_linear=int8_linear)
         if trace is not None:
             trace.setdefault("x_after", []).append(x)
     if saved is not None:
@@ -394,7 +414,7 @@ def euler_step(x, v, sigma_cur, sigma_next):
 
 
 def denoise(latent0, model, steps, reuse, active, geom, n_heads, qk_norm=True,
-            fc2_mode="bf16", token_reduction=False):
+            fc2_mode="bf16", token_reduction=False, int8_linear=False):
     """The Euler loop: ``steps`` transitions, fresh evaluations per ``host.schedule``.
 
     Skipped steps reuse the last fresh velocity (P3 "aggressive levers": reuse extrapolates
@@ -406,7 +426,7 @@ def denoise(latent0, model, steps, reuse, active, geom, n_heads, qk_norm=True,
     for i in range(steps):
         if fresh[i]:
             v = dit_forward(x, model, float(sig[i]), active, geom, n_heads, ev, qk_norm,
-                            fc2_mode, token_reduction)
+                            fc2_mode, token_reduction, int8_linear=int8_linear)
             ev += 1
         x = euler_step(x, v, sig[i], sig[i + 1])
     return x, ev

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
     for s in syms:
         assert hasattr(raw, s), f"{s} declared in h3dit.h but not exported"
     assert set(syms) == set(B.SIGNATURES), "binding signatures out of sync with the header"
-    assert lib.h3_abi_version() == 100
+    assert lib.h3_abi_version() == 101
 
 
 def test_align_frames_matches_oracle(lib):
@@ -161,7 +161,10 @@ def test_entry_points_reject_bad_arguments_without_launching(lib):
     assert L.h3_gemm_bf16(16, 64, 16, 64, 16, 64, 4, 4, 60, None, None, 0, 0, None) == B.H3_ESHAPE
     assert L.h3_attention(16, 128, 16, 128, 16, 128, 16, 128, 1, 1, 1, 96, None) == B.H3_EUNSUPPORTED
     assert L.h3_quant_rows(16, 16, 16, 1, 1000, 1000, None) == B.H3_ESHAPE
-    assert L.h3_gemm_i8(16, 16, 16, 16, 16, 16, 8, 1, 8, 2048, 512, None) == B.H3_EINVAL
+    assert L.h3_gemm_i8(16, 16, 16, 16, 16, 16, 8, 1, 8, 2048, 512, 0, None) == B.H3_EINVAL
+    assert L.h3_gemm_i8(16, 16, 16, 16, 16, 16, 8, 1, 8, 2048, 2048, 7, None) == B.H3_EINVAL
+    assert L.h3_gate_adaln_quant(16, None, None, None, 16, 16, None, 16, 4, 512, None) == B.H3_EINVAL
+    assert L.h3_gate_adaln_quant(16, None, None, None, 16, 16, 16, 16, 4, 500, None) == B.H3_ESHAPE
     g = B.make_geom(2, 8, 8, 1.0)
     assert L.h3_token_reduce(2, ctypes.byref(g), 512, 16, 16, 32, None) == B.H3_EINVAL
     assert L.h3_token_reduce(0, ctypes.byref(g), 512, 16, None, 16, None) == B.H3_EINVAL

@@ -34,7 +34,7 @@ def gpu_model(name, n_blocks=2, fc2_mode="bf16", frames=None):
         w = dataclasses.replace(S.WORKLOADS[name], n_blocks=n_blocks, layers=0, fc2_mode=fc2_mode)
         if frames is not None:
             w = dataclasses.replace(w, frames=frames)
-        _MODELS[key] = (w, DiTModel(w, with_int8=True), oracle_model(w))
+        _MODELS[key] = (w, DiTModel(w, with_int8=True, with_int8_linear=True), oracle_model(w))
     return _MODELS[key]
 
 
@@ -52,8 +52,9 @@ def run_block(model, w, b, x, mod_dev, opts, n1_next=None, mod_next=None):
 
 
 @pytest.mark.parametrize("name", ["tiny_256sq_5f", "512sq_22f"])
-@pytest.mark.parametrize("fc2_mode", ["bf16", "row", "grouped"])
-def test_block_parity(name, fc2_mode):
+@pytest.mark.parametrize("fc2_mode,int8_linear", [("bf16", False), ("row", False), ("grouped", False),
+                                                  ("bf16", True), ("grouped", True)])
+def test_block_parity(name, fc2_mode, int8_linear):
     w, model, om = gpu_model(name)
     n, d = model.geo.n_tokens, w.d_model
     sigma = 0.75
@@ -61,16 +62,16 @@ def test_block_parity(name, fc2_mode):
     mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
     coords = dit.rope_coords(model.geo.f_lat, model.geo.grid_h, model.geo.grid_w, model.geo.scale)
     x0 = S.normal("test.block.x", (n, d), 1.0)
-    opts = B.make_opts(fc2_mode=fc2_mode)
+    opts = B.make_opts(fc2_mode=fc2_mode, int8_linear=int8_linear)
     for b in range(w.n_blocks):
         x = x0.to(DEV)
         ws = run_block(model, w, b, x, mod_dev, opts)
         lay = B.h3_workspace_layout(model.handle, n, opts)
         tr = {}
         ref = dit.block_forward(f64(x0), om["blocks"][b], mod[b], om["ctx"], coords, w.n_heads,
-                                fc2_mode=fc2_mode, trace=tr)
+                                fc2_mode=fc2_mode, trace=tr, int8_linear=int8_linear)
         got = f64(x)
-        tag = f"{name} {fc2_mode} block {b}"
+        tag = f"{name} {fc2_mode} int8_linear={int8_linear} block {b}"
         assert_close(got, ref, rel=2e-2, elem=6e-2, what=f"{tag} out")
         # block delta: the stored output is bf16, whose rounding (at most 2^-8 relative per
         # element) is a floor under any comparison of a delta that is small next to x
@@ -89,8 +90,15 @@ def test_block_parity(name, fc2_mode):
         assert rel_l2(attn[:, d:], tr["oc"]) < 2e-2, f"{tag} cross-attention"
 
 
+def valid_bytes(t, n, d, int8_linear):
+    """The defined part of an AdaLN output buffer: bf16 [n, d], or int8 [n, d] + float [n]."""
+    b = t.detach().contiguous().view(torch.uint8).reshape(-1)
+    return (b[:n * d + 4 * n] if int8_linear else b).cpu().numpy()
+
+
 @pytest.mark.parametrize("name", ["tiny_256sq_5f", "512sq_22f"])
-def test_fused_and_unfused_bit_identical(name):
+@pytest.mark.parametrize("int8_linear", [False, True])
+def test_fused_and_unfused_bit_identical(name, int8_linear):
     w, model, om = gpu_model(name)
     n, d = model.geo.n_tokens, w.d_model
     mod, fin = dit.modulation(om["global"], 0.5)
@@ -98,19 +106,26 @@ def test_fused_and_unfused_bit_identical(name):
     x0 = S.normal("test.block.x2", (n, d), 1.0).to(DEV)
     outs = {}
     for fg, fc in [(1, 1), (0, 0), (1, 0), (0, 1)]:
-        opts = B.make_opts(fused_gate_adaln=fg, fused_cross_block=fc)
+        opts = B.make_opts(fused_gate_adaln=fg, fused_cross_block=fc, int8_linear=int8_linear)
         x = x0.clone()
         n1n = torch.empty_like(x)
         ws = run_block(model, w, 0, x, mod_dev, opts, n1n, mod_dev[1])
         lay = B.h3_workspace_layout(model.handle, n, opts)
-        outs[(fg, fc)] = (x, n1n, ws_view(ws, lay.n2, (n, d)).clone())
+        outs[(fg, fc)] = (bits(x), valid_bytes(n1n, n, d, int8_linear),
+                          valid_bytes(ws_view(ws, lay.n2, (n, d)), n, d, int8_linear), x.clone(), n1n.clone())
     ref = outs[(1, 1)]
     for k, v in outs.items():
-        for a, b_, what in zip(v, ref, ("x", "n1_next", "n2")):
-            assert np.array_equal(bits(a), bits(b_)), f"{name} {what} differs for fused={k}"
-    # n1_next is the next block's AdaLN-1 of the output stream
-    want = dit.adaln(f64(ref[0]), mod[1][0], mod[1][1])
-    assert_close(f64(ref[1]), want, rel=1e-2, elem=3e-2, what="n1_next")
+        for a, b_, what in zip(v[:3], ref[:3], ("x", "n1_next", "n2")):
+            assert np.array_equal(a, b_), f"{name} {what} differs for fused={k}"
+    # n1_next is the next block's AdaLN-1 of the output stream (dequantised in int8 mode)
+    want = dit.adaln(f64(ref[3]), mod[1][0], mod[1][1])
+    if int8_linear:
+        raw = ref[4].view(torch.uint8).reshape(-1)
+        q = raw[:n * d].view(torch.int8).reshape(n, d).cpu().numpy().astype(np.float64)
+        sc = raw[n * d:n * d + 4 * n].view(torch.float32).cpu().numpy().astype(np.float64)
+        assert rel_l2(q * sc[:, None], want) < 2e-2
+    else:
+        assert_close(f64(ref[4]), want, rel=1e-2, elem=3e-2, what="n1_next")
 
 
 def test_block_deterministic_run_to_run():

@@ -35,7 +35,8 @@ def loop_parity(w, model, om, opts_kw, steps, reuse, active):
     torch.cuda.synchronize()
     ref, ev_ref = dit.denoise(f64(lat0), om, steps, reuse, active, geo.as_dict(), w.n_heads,
                               fc2_mode=opts_kw.get("fc2_mode", "bf16"),
-                              token_reduction=opts_kw.get("token_reduction", False))
+                              token_reduction=opts_kw.get("token_reduction", False),
+                              int8_linear=opts_kw.get("int8_linear", False))
     assert ev == ev_ref
     got = f64(x)
     assert np.isfinite(got).all()
@@ -158,3 +159,21 @@ def test_864x480_token_reduction_loop_reduced_depth():
     model = DiTModel(w)
     om = oracle_model(w)
     loop_parity(w, model, om, {"token_reduction": True}, 2, 1, [0, 1, 2, 3, 4])
+
+
+def test_int8_path_forward_and_loop():
+    # the whole int8 path: int8 QKV and FC1 with the fused row quantisation, grouped int8 FC2,
+    # through the forward with token pairing and the Euler loop
+    w = dataclasses.replace(TR_SMALL, fc2_mode="grouped", int8_linear=True, steps=6)
+    model = DiTModel(w)
+    om = oracle_model(w)
+    active = model.active()
+    lat = model.initial_latent()
+    for tr in (False, True):
+        v = model.forward(lat, 0.6, active, eval_index=3, opts=model.opts(token_reduction=tr))
+        torch.cuda.synchronize()
+        ref = dit.dit_forward(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads, eval_index=3,
+                              fc2_mode="grouped", token_reduction=tr, int8_linear=True)
+        assert_close(f64(v), ref, rel=2e-2, elem=8e-2, what=f"int8 velocity token_reduction={tr}")
+    loop_parity(w, model, om, {"fc2_mode": "grouped", "int8_linear": True, "token_reduction": True},
+                6, 2, active)

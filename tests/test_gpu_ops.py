@@ -228,6 +228,33 @@ def test_quant_rows_bit_exact(rows, K, group):
     assert np.array_equal(Sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("group", [2048, 1024])
+def test_quant_rows_exact_half_way_quotients(group):
+    # every group holds its absmax 127 c (c a power of two, so s = c exactly) and values
+    # (k + 1/2) c: their quotients sit exactly half-way between codes and must round to even,
+    # which the quantiser decides with the exact division
+    K, rows = 2048, 4
+    X = np.zeros((rows, K))
+    k = (np.arange(K) % 253) - 126                      # -126 .. 126
+    for r, c in enumerate([2.0 ** -3, 2.0 ** 5, 2.0 ** -20, 1.0]):
+        X[r] = (k + 0.5) * c
+        X[r, ::group] = 127 * c
+        X[r, 1::7] = ((k[1::7] % 63) - 31 + 0.25) * c   # and some values off the half-way points
+    Xd = torch.tensor(X, dtype=torch.float32).to(torch.bfloat16)
+    assert np.array_equal(Xd.double().numpy(), X)      # the values are bf16-exact
+    Q = torch.empty((rows, K), dtype=torch.int8, device=DEV)
+    Sc = torch.empty((rows, K // group), dtype=torch.float32, device=DEV)
+    B.h3_quant_rows(Xd.to(DEV), Q, Sc, group)
+    sync()
+    q_ref, s_ref = dit.quantize_rows(X.astype(np.float32), None if group == K else group)
+    assert np.array_equal(Q.cpu().numpy(), q_ref)
+    assert np.array_equal(Sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    half = np.zeros(K, bool)
+    half[2::7] = True
+    half[::group] = False                               # (not the absmax positions)
+    assert (np.abs(q_ref[:, half]) % 2 == 0).all()      # the half-way values went to even codes
+
+
 @pytest.mark.parametrize("M,N,K,group", [(300, 256, 2048, 2048), (300, 256, 2048, 1024),
                                          (1536, 3072, 12288, 12288), (130, 640, 4096, 1024),
                                          (4100, 700, 2048, 2048),    # 256x256 row tiles, ragged
@@ -279,6 +306,60 @@ def test_int8_fc2_pipeline_bit_exact_on_seeded_input():
         # and the int8 product stays close to the float64 bf16 product
         ref_f = dit.linear(f64(h), f64(W2), f64(b2))
         assert rel_l2(f64(out), ref_f) < 2e-2
+
+
+@pytest.mark.parametrize("rows,d,gated", [(5, 512, True), (1536, 3072, True), (130, 5120, False),
+                                          (64, 1024, True)])
+def test_gate_adaln_quant_bit_identical_to_adaln_then_quant_rows(rows, d, gated):
+    rng = np.random.default_rng(rows * 3 + d)
+    x = randn_bf16(rng, (rows, d))
+    y = randn_bf16(rng, (rows, d)) if gated else None
+    vec = lambda: torch.tensor(rng.standard_normal(d) * 0.2, dtype=torch.float32, device=DEV)
+    g, sh, sc = vec(), vec(), vec()
+    # fused: gate, AdaLN and int8 row quantisation in one kernel
+    xf = x.clone()
+    qf = torch.empty((rows, d), dtype=torch.int8, device=DEV)
+    sf = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    B.h3_gate_adaln_quant(xf, y, g if gated else None, xf if gated else None, sh, sc, qf, sf)
+    # reference sequence: gate + AdaLN into bf16, then the row quantiser
+    xu, nu = x.clone(), torch.empty_like(x)
+    B.h3_gate_adaln(xu, y, g if gated else None, xu if gated else None, sh, sc, nu)
+    qu = torch.empty_like(qf)
+    su = torch.empty((rows, 1), dtype=torch.float32, device=DEV)
+    B.h3_quant_rows(nu, qu, su, d)
+    sync()
+    assert torch.equal(xf.view(torch.int16), xu.view(torch.int16))
+    assert torch.equal(qf, qu)
+    assert torch.equal(sf.view(torch.int32), su.view(-1).view(torch.int32))
+    # and the quantiser's output is the oracle's on the same bf16 rows
+    q_ref, s_ref = dit.quantize_rows(f64(nu).astype(np.float32), None)
+    assert np.array_equal(qf.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("M,N,K,sample", [(300, 640, 2048, False), (1536, 12288, 3072, True)])
+def test_gemm_i8_gelu_epilogue(M, N, K, sample):
+    # int8 FC1: dequantisation bit-exact, then GELU before the bf16 rounding; the exact-erf
+    # GELU of the oracle and the kernel's may land on the two sides of a bf16 rounding
+    # boundary, so the bar is one bf16 unit
+    rng = np.random.default_rng(M + N)
+    qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    # |acc| ~ sqrt(K) 127^2 / 3: scales of a few 1e-3 give dequantised values of order 1-10
+    sa = (1e-3 + rng.random((M, 1)) * 4e-3).astype(np.float32)
+    sw = (1e-3 + rng.random(N) * 4e-3).astype(np.float32)
+    bias = bf16_dev(rng.standard_normal(N) * 0.5)
+    Cm = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    B.h3_gemm_i8(torch.from_numpy(qa).to(DEV), torch.from_numpy(sa).to(DEV), torch.from_numpy(qw).to(DEV),
+                 torch.from_numpy(sw).to(DEV), bias, Cm, K, epilogue=1)
+    sync()
+    rows = np.sort(rng.choice(M, 12, replace=False)) if sample else np.arange(M)
+    cols = np.sort(rng.choice(N, 96, replace=False)) if sample else np.arange(N)
+    acc = dit.int8_accumulate(qa[rows], qw[cols], None)
+    v = dit.dequant(acc, sa[rows], sw[cols], f64(bias).astype(np.float32)[cols])
+    ref = dit.gelu(v.astype(np.float64))
+    got = Cm.cpu().to(torch.float32).numpy()[np.ix_(rows, cols)].astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 2e-6)
+    assert np.abs(v).max() > 3 and (v < -1).any()   # both GELU regimes are exercised
 
 
 # ------------------------------------------------------------------ Euler

@@ -333,6 +333,48 @@ def test_int8_fc2_close_to_bf16_product():
         assert (np.abs(got - ref) <= bound * 1.01 + 1e-6).all()
 
 
+def test_linear_int8_exact_when_quantisation_is_lossless():
+    # activations on the grid s_a * k (|k| <= 127, 127 reached, s_a a power of two so the bf16
+    # rounding and the division are exact) and weights on s_w * j: the int8 product is then
+    # the exact product, up to the float32 rounding of the dequantisation
+    qa = RNG.integers(-127, 128, size=(4, 96))
+    qa[:, 0] = 127
+    qw = RNG.integers(-127, 128, size=(6, 96))
+    qw[:, 5] = -127
+    sa = 2.0 ** -RNG.integers(3, 9, size=(4, 1))
+    sw = 2.0 ** -RNG.integers(6, 12, size=(6, 1))
+    a, w = qa * sa, qw * sw
+    b = RNG.normal(size=6) * 0.01
+    b = b.astype(np.float32).astype(np.float64)
+    got = dit.linear_int8(a, w, b)
+    want = tF.linear(t64(a), t64(w), t64(b)).numpy()
+    np.testing.assert_allclose(got, want, rtol=2e-7, atol=1e-9)
+
+
+def test_linear_int8_rounds_the_activation_to_bf16_first():
+    a = RNG.normal(size=(3, 64))
+    w = RNG.normal(size=(5, 64)) * 0.02
+    b = np.zeros(5)
+    ab = torch.from_numpy(a).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(dit.linear_int8(a, w, b), dit.linear_int8(ab, w, b))
+
+
+def test_linear_int8_within_quantisation_bound_of_the_float64_product():
+    a = RNG.normal(size=(5, 512))
+    w = RNG.normal(size=(12, 512)) * 0.02
+    b = RNG.normal(size=12) * 0.02
+    ab = torch.from_numpy(a).to(torch.bfloat16).double().numpy()
+    ref = tF.linear(t64(ab), t64(w), t64(b)).numpy()
+    got = dit.linear_int8(a, w, b)
+    _, sa = dit.quantize_rows(ab.astype(np.float32))
+    _, sw = dit.quantize_weight(w.astype(np.float32))
+    bound = (np.abs(w)[None] * sa[:, None, :] / 2).sum(-1) + \
+            (np.abs(ab)[:, None, :] * sw[None, :, 0:1] / 2).sum(-1) + \
+            (sa[:, None, :] * sw[None, :, 0:1] / 4).sum(-1)
+    assert (np.abs(got - ref) <= bound * 1.01 + 1e-6).all()
+    assert np.abs(got - ref).max() > 0   # it is a different product
+
+
 # ----------------------------------------------------------------- token pairing
 def test_merge_restore_identity_and_delta():
     plan = host.token_plan(2, 3, 5, 0, 10)

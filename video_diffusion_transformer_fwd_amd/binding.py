@@ -34,7 +34,8 @@ class h3_dims(C.Structure):
 GLOBAL_FIELDS = ("t1_w", "t1_b", "t2_w", "t2_b", "mod_w", "mod_b", "fin_w", "fin_b", "fin_t",
                  "mod_table", "patch_w", "patch_b", "head_w", "head_b")
 BLOCK_FIELDS = ("qkvq_w", "qkvq_b", "kc_w", "kc_b", "vc_w", "vc_b", "out_w", "out_b", "outc_b",
-                "q_gamma", "k_gamma", "fc1_w", "fc1_b", "fc2_w", "fc2_b", "fc2_q", "fc2_s")
+                "q_gamma", "k_gamma", "fc1_w", "fc1_b", "fc2_w", "fc2_b", "fc2_q", "fc2_s",
+                "qkvq_q", "qkvq_s", "fc1_q", "fc1_s")
 
 
 class h3_global_weights(C.Structure):
@@ -52,7 +53,8 @@ class h3_geom(C.Structure):
 
 class h3_run_opts(C.Structure):
     _fields_ = [(n, C.c_int32) for n in
-                ("fc2_mode", "fused_gate_adaln", "fused_cross_block", "qk_norm", "token_reduction")]
+                ("fc2_mode", "fused_gate_adaln", "fused_cross_block", "qk_norm", "token_reduction",
+                 "int8_linear")]
 
 
 class h3_ws_layout(C.Structure):
@@ -82,6 +84,7 @@ SIGNATURES = {
     "h3_workspace_layout": (_I32, [_VP, _I32, C.POINTER(h3_run_opts), C.POINTER(h3_ws_layout)]),
     "h3_prepare_context": (_I32, [_VP, _VP, _VP, _VP]),
     "h3_quantize_fc2_weights": (_I32, [_VP, _VP]),
+    "h3_quantize_linear_weights": (_I32, [_VP, _VP]),
     "h3_modulation": (_I32, [_VP, _F, _VP, _VP, _VP, _SZ, _VP]),
     "h3_dit_block_fwd": (_I32, [_VP, _I32, C.POINTER(h3_geom), C.POINTER(h3_run_opts), _VP, _VP,
                                 _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -94,8 +97,9 @@ SIGNATURES = {
     "h3_attention": (_I32, [_VP, _I64, _VP, _I64, _VP, _I64, _VP, _I64, _I32, _I32, _I32, _I32,
                             _VP]),
     "h3_quant_rows": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
-    "h3_gemm_i8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _VP]),
+    "h3_gemm_i8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP]),
     "h3_gate_adaln": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
+    "h3_gate_adaln_quant": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
     "h3_rope_table": (_I32, [C.POINTER(h3_geom), _I32, _VP, _VP]),
     "h3_qk_norm_rope": (_I32, [_VP, _I64, _I32, _I32, _I32, _VP, _VP, _I32, _VP, _VP]),
     "h3_profile_begin": (_I32, [C.c_uint32, _I32]),
@@ -207,10 +211,10 @@ def h3_geom_tokens(geom: h3_geom) -> int:
 
 
 def make_opts(fc2_mode="bf16", fused_gate_adaln=True, fused_cross_block=True, qk_norm=True,
-              token_reduction=False):
+              token_reduction=False, int8_linear=False):
     return h3_run_opts(FC2_MODES[fc2_mode] if isinstance(fc2_mode, str) else fc2_mode,
                        int(fused_gate_adaln), int(fused_cross_block), int(qk_norm),
-                       int(token_reduction))
+                       int(token_reduction), int(int8_linear))
 
 
 # ------------------------------------------------------------------ model
@@ -243,6 +247,10 @@ def h3_prepare_context(m, ctx, ctx_kv, stream=None):
 
 def h3_quantize_fc2_weights(m, stream=None):
     _check(lib().h3_quantize_fc2_weights(m, stream_handle(stream)))
+
+
+def h3_quantize_linear_weights(m, stream=None):
+    _check(lib().h3_quantize_linear_weights(m, stream_handle(stream)))
 
 
 def h3_modulation(m, sigma, mod, mod_final, ws, stream=None):
@@ -296,17 +304,23 @@ def h3_quant_rows(X, Q, S, group, stream=None):
     _check(lib().h3_quant_rows(ptr(X), ptr(Q), ptr(S), rows, K, group, stream_handle(stream)))
 
 
-def h3_gemm_i8(QA, SA, QW, SW, bias, C_out, group, stream=None):
+def h3_gemm_i8(QA, SA, QW, SW, bias, C_out, group, epilogue=0, stream=None):
     M, K = QA.shape
     N = QW.shape[0]
     _check(lib().h3_gemm_i8(ptr(QA), ptr(SA), ptr(QW), ptr(SW), ptr(bias), ptr(C_out),
-                            C_out.stride(0), M, N, K, group, stream_handle(stream)))
+                            C_out.stride(0), M, N, K, group, epilogue, stream_handle(stream)))
 
 
 def h3_gate_adaln(x, y, gate, x_out, shift, scale, n_out, stream=None):
     rows, d = x.shape
     _check(lib().h3_gate_adaln(ptr(x), ptr(y), ptr(gate), ptr(x_out), ptr(shift), ptr(scale),
                                ptr(n_out), rows, d, stream_handle(stream)))
+
+
+def h3_gate_adaln_quant(x, y, gate, x_out, shift, scale, q_out, s_out, stream=None):
+    rows, d = x.shape
+    _check(lib().h3_gate_adaln_quant(ptr(x), ptr(y), ptr(gate), ptr(x_out), ptr(shift), ptr(scale),
+                                     ptr(q_out), ptr(s_out), rows, d, stream_handle(stream)))
 
 
 def h3_rope_table(geom, head_dim, table, stream=None):

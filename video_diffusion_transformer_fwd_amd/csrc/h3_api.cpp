@@ -28,6 +28,16 @@ int32_t check_opts(const h3_run_opts *o) {
   if (!o) return fail(H3_EINVAL, "run options are NULL");
   if (o->fc2_mode < H3_FC2_BF16 || o->fc2_mode > H3_FC2_INT8_GROUPED)
     return fail(H3_EINVAL, "fc2_mode must be 0, 1 or 2");
+  if (o->int8_linear != 0 && o->int8_linear != 1) return fail(H3_EINVAL, "int8_linear must be 0 or 1");
+  return H3_OK;
+}
+
+// The int8 weight copies a block needs under these options.
+int32_t check_block_int8(const h3_block_weights &w, const h3_run_opts &o, const char *who) {
+  if (o.fc2_mode != H3_FC2_BF16 && (!w.fc2_q || !w.fc2_s))
+    return fail(H3_EINVAL, std::string(who) + ": int8 FC2 needs quantised weights");
+  if (o.int8_linear && (!w.qkvq_q || !w.qkvq_s || !w.fc1_q || !w.fc1_s))
+    return fail(H3_EINVAL, std::string(who) + ": int8_linear needs quantised QKV and FC1 weights");
   return H3_OK;
 }
 
@@ -65,6 +75,10 @@ WsPlan plan_workspace(const Model &m, int32_t n, const h3_run_opts &o) {
                            plan_gemm(r, d, F)};
     for (const GemmPlan &g : gp) part = std::max(part, g.part_bytes);
     if (i8) part = std::max(part, plan_gemm_i8(r, d, F, o.fc2_mode == H3_FC2_INT8_ROW ? F : 1024).part_bytes);
+    if (o.int8_linear) {
+      part = std::max(part, plan_gemm_i8(r, 4 * d, d, d).part_bytes);
+      part = std::max(part, plan_gemm_i8(r, F, d, d).part_bytes);
+    }
   }
   p.gpart = take(part);
   p.gpart_bytes = part;
@@ -92,19 +106,48 @@ int32_t validate_model(const h3_model *m) {
   return H3_OK;
 }
 
-// Launches the block on validated arguments.  rows = tokens of this geometry.
+// A row-quantised AdaLN output: int8 [rows, d] followed by the float32 row scales [rows].
+struct QRows {
+  int8_t *q;
+  float *s;
+};
+QRows qrows(const void *buf, int rows, int d) {
+  char *b = reinterpret_cast<char *>(const_cast<void *>(buf));
+  return {reinterpret_cast<int8_t *>(b), reinterpret_cast<float *>(b + static_cast<size_t>(rows) * d)};
+}
+
+// AdaLN (after the optional gate x <- x + g y) into dst: bf16 [rows, d], or row-quantised
+// (QRows layout) when quant.  fused = gate and AdaLN in one kernel (bit-identical either way).
+void gate_then_adaln(bf16_t *x, const bf16_t *y, const float *g, const float *sh, const float *sc,
+                     void *dst, bool quant, bool fused, int rows, int d, hipStream_t s) {
+  if (y && !fused) {
+    launch_gate_adaln(x, y, g, x, nullptr, nullptr, nullptr, rows, d, s);
+    y = nullptr;
+  }
+  if (quant) {
+    const QRows r = qrows(dst, rows, d);
+    launch_gate_adaln(x, y, g, y ? x : nullptr, sh, sc, nullptr, rows, d, s, r.q, r.s);
+  } else {
+    launch_gate_adaln(x, y, g, y ? x : nullptr, sh, sc, reinterpret_cast<bf16_t *>(dst), rows, d, s);
+  }
+}
+
+// Launches the block on validated arguments.  rows = tokens of this geometry.  With
+// o.int8_linear the block's n1 (given or computed) is row-quantised; n1_next is row-quantised
+// when n1_next_q, else bf16.
 int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t rows,
-                  const h3_run_opts &o, bf16_t *x, const bf16_t *n1_in, bf16_t *n1_next,
-                  const float *mod, const float *mod_next, const bf16_t *ctx_kv, char *ws,
-                  const WsPlan &p, hipStream_t s, const float2 *rope_table) {
+                  const h3_run_opts &o, bf16_t *x, const void *n1_in, void *n1_next,
+                  bool n1_next_q, const float *mod, const float *mod_next, const bf16_t *ctx_kv,
+                  char *ws, const WsPlan &p, hipStream_t s, const float2 *rope_table) {
+  const bool q8 = o.int8_linear != 0;
   const int d = m->dims.d_model, F = m->dims.ffn_dim, H = m->dims.n_heads, D = m->head_dim;
   const int L = m->dims.ctx_len;
   const h3_block_weights &w = m->blocks[b];
-  bf16_t *n1 = reinterpret_cast<bf16_t *>(ws + p.n1);
+  void *n1 = ws + p.n1;
   bf16_t *qkvq = reinterpret_cast<bf16_t *>(ws + p.qkvq);
   bf16_t *attn = reinterpret_cast<bf16_t *>(ws + p.attn);
   bf16_t *y = reinterpret_cast<bf16_t *>(ws + p.y);
-  bf16_t *n2 = reinterpret_cast<bf16_t *>(ws + p.n2);
+  void *n2 = ws + p.n2;
   bf16_t *h = reinterpret_cast<bf16_t *>(ws + p.h);
   bf16_t *mo = reinterpret_cast<bf16_t *>(ws + p.m);
   const float *sh1 = mod, *sc1 = mod + d, *g1 = mod + 2 * d;
@@ -116,15 +159,23 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
   // AdaLN-1 (unless the caller already has it, e.g. from the previous block's fused gate)
   if (!n1_in) {
     ProfScope ps(H3_ST_ADALN, s);
-    launch_gate_adaln(x, nullptr, nullptr, nullptr, sh1, sc1, n1, rows, d, s);
+    gate_then_adaln(x, nullptr, nullptr, sh1, sc1, n1, q8, true, rows, d, s);
     n1_in = n1;
   }
   // [q | k | v | qc] = n1 W_qkvq^T + b
   {
     ProfScope ps(H3_ST_QKV_GEMM, s);
-    launch_gemm_bf16(n1_in, d, reinterpret_cast<const bf16_t *>(w.qkvq_w), d, qkvq, 4 * d, rows,
-                     4 * d, d, reinterpret_cast<const bf16_t *>(w.qkvq_b), nullptr, H3_EPI_NONE,
-                     0, s, sk);
+    if (q8) {
+      const QRows r = qrows(n1_in, rows, d);
+      launch_gemm_i8(r.q, r.s, reinterpret_cast<const int8_t *>(w.qkvq_q),
+                     reinterpret_cast<const float *>(w.qkvq_s),
+                     reinterpret_cast<const bf16_t *>(w.qkvq_b), qkvq, 4 * d, rows, 4 * d, d, d,
+                     s, sk, H3_EPI_NONE);
+    } else {
+      launch_gemm_bf16(reinterpret_cast<const bf16_t *>(n1_in), d,
+                       reinterpret_cast<const bf16_t *>(w.qkvq_w), d, qkvq, 4 * d, rows, 4 * d, d,
+                       reinterpret_cast<const bf16_t *>(w.qkvq_b), nullptr, H3_EPI_NONE, 0, s, sk);
+    }
   }
   // Q/K RMSNorm + 3D RoPE, in place
   {
@@ -151,19 +202,24 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
                      reinterpret_cast<const bf16_t *>(w.outc_b), H3_EPI_NONE, 0, s, sk);
   }
   // x <- x + g1 y ; n2 = AdaLN(x; sh2, sc2)
-  if (o.fused_gate_adaln) {
+  {
     ProfScope ps(H3_ST_GATE_ADALN, s);
-    launch_gate_adaln(x, y, g1, x, sh2, sc2, n2, rows, d, s);
-  } else {
-    ProfScope ps(H3_ST_GATE_ADALN, s);
-    launch_gate_adaln(x, y, g1, x, nullptr, nullptr, nullptr, rows, d, s);
-    launch_gate_adaln(x, nullptr, nullptr, nullptr, sh2, sc2, n2, rows, d, s);
+    gate_then_adaln(x, y, g1, sh2, sc2, n2, q8, o.fused_gate_adaln != 0, rows, d, s);
   }
   // h = GELU(n2 W1^T + b1)
   {
     ProfScope ps(H3_ST_FC1_GEMM, s);
-    launch_gemm_bf16(n2, d, reinterpret_cast<const bf16_t *>(w.fc1_w), d, h, F, rows, F, d,
-                     reinterpret_cast<const bf16_t *>(w.fc1_b), nullptr, H3_EPI_GELU, 0, s, sk);
+    if (q8) {
+      const QRows r = qrows(n2, rows, d);
+      launch_gemm_i8(r.q, r.s, reinterpret_cast<const int8_t *>(w.fc1_q),
+                     reinterpret_cast<const float *>(w.fc1_s),
+                     reinterpret_cast<const bf16_t *>(w.fc1_b), h, F, rows, F, d, d, s, sk,
+                     H3_EPI_GELU);
+    } else {
+      launch_gemm_bf16(reinterpret_cast<const bf16_t *>(n2), d,
+                       reinterpret_cast<const bf16_t *>(w.fc1_w), d, h, F, rows, F, d,
+                       reinterpret_cast<const bf16_t *>(w.fc1_b), nullptr, H3_EPI_GELU, 0, s, sk);
+    }
   }
   // m = FC2(h)
   if (o.fc2_mode == H3_FC2_BF16) {
@@ -184,13 +240,13 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
                    reinterpret_cast<const bf16_t *>(w.fc2_b), mo, d, rows, d, F, group, s, sk);
   }
   // x <- x + g2 m ; optionally n1_next = AdaLN(x; next shift, scale)
-  if (n1_next && o.fused_cross_block) {
+  {
     ProfScope ps(H3_ST_GATE_ADALN, s);
-    launch_gate_adaln(x, mo, g2, x, mod_next, mod_next + d, n1_next, rows, d, s);
-  } else {
-    ProfScope ps(H3_ST_GATE_ADALN, s);
-    launch_gate_adaln(x, mo, g2, x, nullptr, nullptr, nullptr, rows, d, s);
-    if (n1_next) launch_gate_adaln(x, nullptr, nullptr, nullptr, mod_next, mod_next + d, n1_next, rows, d, s);
+    if (n1_next)
+      gate_then_adaln(x, mo, g2, mod_next, mod_next + d, n1_next, n1_next_q,
+                      o.fused_cross_block != 0, rows, d, s);
+    else
+      launch_gate_adaln(x, mo, g2, x, nullptr, nullptr, nullptr, rows, d, s);
   }
   (void)geom;
   return check_launch("h3_dit_block_fwd");
@@ -328,6 +384,26 @@ int32_t h3_quantize_fc2_weights(const h3_model *m, void *stream) {
   return check_launch("h3_quantize_fc2_weights");
 }
 
+int32_t h3_quantize_linear_weights(const h3_model *m, void *stream) {
+  if (int32_t e = validate_model(m)) return e;
+  for (int b = 0; b < m->dims.n_blocks; ++b) {
+    const h3_block_weights &w = m->blocks[b];
+    if (!w.qkvq_q || !w.qkvq_s || !w.fc1_q || !w.fc1_s)
+      return fail(H3_EINVAL, "h3_quantize_linear_weights: qkvq_q/qkvq_s/fc1_q/fc1_s not set in block " +
+                                 std::to_string(b));
+  }
+  hipStream_t s = as_stream(stream);
+  const int d = m->dims.d_model, F = m->dims.ffn_dim;
+  for (int b = 0; b < m->dims.n_blocks; ++b) {
+    const h3_block_weights &w = m->blocks[b];
+    launch_quant_rows(reinterpret_cast<const bf16_t *>(w.qkvq_w), reinterpret_cast<int8_t *>(w.qkvq_q),
+                      reinterpret_cast<float *>(w.qkvq_s), 4 * d, d, d, s);
+    launch_quant_rows(reinterpret_cast<const bf16_t *>(w.fc1_w), reinterpret_cast<int8_t *>(w.fc1_q),
+                      reinterpret_cast<float *>(w.fc1_s), F, d, d, s);
+  }
+  return check_launch("h3_quantize_linear_weights");
+}
+
 int32_t h3_modulation(const h3_model *m, float sigma, float *mod, float *mod_final, void *ws,
                       size_t ws_bytes, void *stream) {
   if (int32_t e = validate_model(m)) return e;
@@ -350,17 +426,16 @@ int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
   if (int32_t e = h3_geom_tokens(geom, &n)) return e;
   if (!x || !mod || !ctx_kv) return fail(H3_EINVAL, "h3_dit_block_fwd: NULL x, mod or ctx_kv");
   if (n1_next && !mod_next) return fail(H3_EINVAL, "h3_dit_block_fwd: n1_next needs mod_next");
-  if (o->fc2_mode != H3_FC2_BF16 && (!m->blocks[block].fc2_q || !m->blocks[block].fc2_s))
-    return fail(H3_EINVAL, "h3_dit_block_fwd: int8 FC2 needs quantised weights");
+  if (int32_t e = check_block_int8(m->blocks[block], *o, "h3_dit_block_fwd")) return e;
   const WsPlan p = plan_workspace(*m, n, *o);
   if (!ws || ws_bytes < p.total) return fail(H3_EWORKSPACE, "h3_dit_block_fwd: workspace too small");
   hipStream_t s = as_stream(stream);
   char *w = reinterpret_cast<char *>(ws);
   float2 *rope = reinterpret_cast<float2 *>(w + p.rope);
   launch_rope_table(rope, *geom, n, m->head_dim, s);
-  return run_block(m, block, *geom, n, *o, reinterpret_cast<bf16_t *>(x),
-                   reinterpret_cast<const bf16_t *>(n1_in), reinterpret_cast<bf16_t *>(n1_next),
-                   mod, mod_next, reinterpret_cast<const bf16_t *>(ctx_kv), w, p, s, rope);
+  return run_block(m, block, *geom, n, *o, reinterpret_cast<bf16_t *>(x), n1_in, n1_next,
+                   o->int8_linear != 0, mod, mod_next, reinterpret_cast<const bf16_t *>(ctx_kv), w,
+                   p, s, rope);
 }
 
 int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts *o,
@@ -379,8 +454,7 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
   for (int i = 0; i < n_active; ++i) {
     if (active[i] < 0 || active[i] >= nb) return fail(H3_EINVAL, "h3_dit_forward: active index out of range");
     if (i && active[i] <= active[i - 1]) return fail(H3_EINVAL, "h3_dit_forward: active must ascend");
-    if (o->fc2_mode != H3_FC2_BF16 && (!m->blocks[active[i]].fc2_q || !m->blocks[active[i]].fc2_s))
-      return fail(H3_EINVAL, "h3_dit_forward: int8 FC2 needs quantised weights");
+    if (int32_t e = check_block_int8(m->blocks[active[i]], *o, "h3_dit_forward")) return e;
   }
   if (eval_index < 0) return fail(H3_EINVAL, "h3_dit_forward: eval_index must be >= 0");
   int32_t merge_after = 0, restore_before = 0, n_red = 0;
@@ -399,8 +473,9 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
   float *fin = reinterpret_cast<float *>(w + p.fin);
   bf16_t *x = reinterpret_cast<bf16_t *>(w + p.x);
   bf16_t *xr = reinterpret_cast<bf16_t *>(w + p.xr);
-  bf16_t *na = reinterpret_cast<bf16_t *>(w + p.n1b);
-  bf16_t *nb_ = reinterpret_cast<bf16_t *>(w + p.n1);
+  void *na = w + p.n1b;
+  void *nb_ = w + p.n1;
+  const bool q8 = o->int8_linear != 0;
   bf16_t *lat16 = reinterpret_cast<bf16_t *>(w + p.lat16);
   float2 *rope_full = reinterpret_cast<float2 *>(w + p.rope);
   float2 *rope_red = reinterpret_cast<float2 *>(w + p.rope_r);
@@ -427,7 +502,7 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
   int rows = n;
   const float2 *rope = rope_full;
   const h3_geom *g_cur = geom;
-  bf16_t *n1 = na, *n1_other = nb_;
+  void *n1 = na, *n1_other = nb_;
   bool n1_valid = false;
   for (int pos = 0; pos < n_active; ++pos) {
     const int b = active[pos];
@@ -444,7 +519,7 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
     }
     if (!n1_valid) {
       ProfScope ps(H3_ST_ADALN, s);
-      launch_gate_adaln(cur, nullptr, nullptr, nullptr, mb, mb + d, n1, rows, d, s);
+      gate_then_adaln(cur, nullptr, nullptr, mb, mb + d, n1, q8, true, rows, d, s);
     }
     // the next AdaLN can be fused into this block's MLP gate when no token op sits between
     const bool last = pos + 1 == n_active;
@@ -453,7 +528,7 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
     const bool restore_before_head = o->token_reduction && last && restore_before == n_active + 1 &&
                                      merge_after < n_active;
     const float *mnext = nullptr;
-    bf16_t *n1n = nullptr;
+    void *n1n = nullptr;
     if (!last && !token_op_next) {
       mnext = mod + static_cast<size_t>(active[pos + 1]) * 6 * d;
       n1n = n1_other;
@@ -463,7 +538,8 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
     }
     // n1 is always supplied, so the block never writes its own n1 slot (p.n1), which serves
     // here as the second of the two alternating n1 buffers
-    int32_t e = run_block(m, b, *g_cur, rows, *o, cur, n1, n1n, mb, mnext,
+    // the final AdaLN (mnext == fin) feeds the bf16 head, so it is never quantised
+    int32_t e = run_block(m, b, *g_cur, rows, *o, cur, n1, n1n, q8 && mnext != fin, mb, mnext,
                           kv + static_cast<size_t>(b) * 2 * L * d, w, p, s, rope);
     if (e) return e;
     if (n1n) {
@@ -479,15 +555,17 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
       }
       cur = x; rows = n;
       ProfScope ps(H3_ST_ADALN, s);
-      launch_gate_adaln(x, nullptr, nullptr, nullptr, fin, fin + d, n1, rows, d, s);
+      launch_gate_adaln(x, nullptr, nullptr, nullptr, fin, fin + d, reinterpret_cast<bf16_t *>(n1),
+                        rows, d, s);
       n1_valid = true;
     }
   }
   // head: velocity = AdaLN_final(x) W_h^T + b_h, float32
   {
     ProfScope ps(H3_ST_HEAD, s);
-    launch_gemm_bf16(n1, d, reinterpret_cast<const bf16_t *>(m->g.head_w), d, velocity, C, n, C,
-                     d, reinterpret_cast<const bf16_t *>(m->g.head_b), nullptr, H3_EPI_NONE, 1, s);
+    launch_gemm_bf16(reinterpret_cast<const bf16_t *>(n1), d,
+                     reinterpret_cast<const bf16_t *>(m->g.head_w), d, velocity, C, n, C, d,
+                     reinterpret_cast<const bf16_t *>(m->g.head_b), nullptr, H3_EPI_NONE, 1, s);
   }
   return check_launch("h3_dit_forward");
 }
@@ -556,8 +634,9 @@ int32_t h3_attention(const void *Q, int64_t ldq, const void *K, int64_t ldk, con
 int32_t h3_quant_rows(const void *X, void *Q, float *S, int32_t rows, int32_t K, int32_t group,
                       void *stream) {
   if (!X || !Q || !S) return fail(H3_EINVAL, "h3_quant_rows: NULL pointer");
-  if (rows < 1 || K < 1024 || K % 1024) return fail(H3_ESHAPE, "h3_quant_rows: K must be a multiple of 1024");
   if (group != K && group != 1024) return fail(H3_EINVAL, "h3_quant_rows: group must be K or 1024");
+  if (rows < 1 || K < 512 || K % 512 || (group == 1024 && K % 1024))
+    return fail(H3_ESHAPE, "h3_quant_rows: K must be a multiple of 512 (of 1024 with groups)");
   launch_quant_rows(reinterpret_cast<const bf16_t *>(X), reinterpret_cast<int8_t *>(Q), S, rows, K,
                     group, as_stream(stream));
   return check_launch("h3_quant_rows");
@@ -565,14 +644,16 @@ int32_t h3_quant_rows(const void *X, void *Q, float *S, int32_t rows, int32_t K,
 
 int32_t h3_gemm_i8(const void *QA, const float *SA, const void *QW, const float *SW,
                    const void *bias, void *C, int64_t ldc, int32_t M, int32_t N, int32_t K,
-                   int32_t group, void *stream) {
+                   int32_t group, int32_t epilogue, void *stream) {
   if (!QA || !SA || !QW || !SW || !bias || !C) return fail(H3_EINVAL, "h3_gemm_i8: NULL pointer");
-  if (M < 1 || N < 1 || K < 1024 || K % 1024) return fail(H3_ESHAPE, "h3_gemm_i8: K must be a multiple of 1024");
   if (group != K && group != 1024) return fail(H3_EINVAL, "h3_gemm_i8: group must be K or 1024");
+  if (M < 1 || N < 1 || K < 128 || K % 128 || (group == 1024 && K % 1024))
+    return fail(H3_ESHAPE, "h3_gemm_i8: K must be a multiple of 128 (of 1024 with groups)");
   if (ldc < N) return fail(H3_ESHAPE, "h3_gemm_i8: ldc < N");
+  if (epilogue != H3_EPI_NONE && epilogue != H3_EPI_GELU) return fail(H3_EINVAL, "h3_gemm_i8: bad epilogue");
   launch_gemm_i8(reinterpret_cast<const int8_t *>(QA), SA, reinterpret_cast<const int8_t *>(QW), SW,
                  reinterpret_cast<const bf16_t *>(bias), reinterpret_cast<bf16_t *>(C), ldc, M, N, K,
-                 group, as_stream(stream));
+                 group, as_stream(stream), SplitScratch(), epilogue);
   return check_launch("h3_gemm_i8");
 }
 
@@ -589,6 +670,19 @@ int32_t h3_gate_adaln(const void *x, const void *y, const float *gate, void *x_o
                     reinterpret_cast<bf16_t *>(x_out), shift, scale, reinterpret_cast<bf16_t *>(n_out),
                     rows, d_model, as_stream(stream));
   return check_launch("h3_gate_adaln");
+}
+
+int32_t h3_gate_adaln_quant(const void *x, const void *y, const float *gate, void *x_out,
+                            const float *shift, const float *scale, void *q_out, float *s_out,
+                            int32_t rows, int32_t d_model, void *stream) {
+  if (!x || !shift || !scale || !q_out || !s_out) return fail(H3_EINVAL, "h3_gate_adaln_quant: NULL pointer");
+  if (y && (!gate || !x_out)) return fail(H3_EINVAL, "h3_gate_adaln_quant: gate needs gate and x_out");
+  if (rows < 1) return fail(H3_ESHAPE, "h3_gate_adaln_quant: rows must be >= 1");
+  if (!supported_width(d_model)) return fail(H3_ESHAPE, "h3_gate_adaln_quant: unsupported d_model");
+  launch_gate_adaln(reinterpret_cast<const bf16_t *>(x), reinterpret_cast<const bf16_t *>(y), gate,
+                    reinterpret_cast<bf16_t *>(x_out), shift, scale, nullptr, rows, d_model,
+                    as_stream(stream), reinterpret_cast<int8_t *>(q_out), s_out);
+  return check_launch("h3_gate_adaln_quant");
 }
 
 int32_t h3_rope_table(const h3_geom *geom, int32_t head_dim, void *table, void *stream) {

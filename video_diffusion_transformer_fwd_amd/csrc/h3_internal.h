@@ -36,6 +36,26 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// GELU(x) = x Phi(x) with Phi the standard normal CDF.  erfc by Abramowitz & Stegun, Handbook
+// of Mathematical Functions, formula 7.1.26: erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2) with
+// t = 1 / (1 + p z), z >= 0, absolute error <= 1.5e-7.  With z = |x| / sqrt 2 and
+// q = erfc(z) / 2 = Phi(-|x|), x Phi(x) = x / 2 + |x| (1/2 - q) holds for either sign of x, so
+// the product needs no branch or select: one reciprocal, one exponential, eight FMA/multiplies.
+// The factor 1/2 of q is folded into the coefficients, 1/sqrt 2 into p and the exponent.
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + (0.3275911f * 0.70710678118654752f) * ax);
+  float h = 0.5f * 1.061405429f;
+  h = h * t - 0.5f * 1.453152027f;
+  h = h * t + 0.5f * 1.421413741f;
+  h = h * t - 0.5f * 0.284496736f;
+  h = h * t + 0.5f * 0.254829592f;
+  h = h * t;
+  const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // exp(-x^2 / 2)
+  const float q = h * e;
+  return __builtin_fmaf(ax, 0.5f - q, 0.5f * x);
+}
+
 // ---------------------------------------------------------------- model
 struct Model {
   h3_dims dims;
@@ -80,15 +100,19 @@ void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb
 GemmPlan plan_gemm_i8(int M, int N, int K, int group);
 void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
-                    hipStream_t s, const SplitScratch &scratch = SplitScratch());
+                    hipStream_t s, const SplitScratch &scratch = SplitScratch(),
+                    int epilogue = H3_EPI_NONE);
 void launch_attention(const bf16_t *Q, int64_t ldq, const bf16_t *K, int64_t ldk,
                       const bf16_t *V, int64_t ldv, bf16_t *O, int64_t ldo, int nq, int nk,
                       int heads, int head_dim, hipStream_t s);
 // x_out = bf16(x + gate*y) (if y != nullptr), then n_out = bf16(LN(x_out)(1+scale)+shift)
 // (if n_out != nullptr).  With y == nullptr the row is read from x.  x_out may equal x.
+// With q_out != nullptr the normalised row is not stored as bf16 but quantised: q_out int8
+// [rows, d] and s_out float32 [rows] (one scale per row), bit-identical to storing n_out and
+// quantising it with launch_quant_rows(group = d).
 void launch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
                        const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
-                       hipStream_t s);
+                       hipStream_t s, int8_t *q_out = nullptr, float *s_out = nullptr);
 void launch_rope_table(float2 *table, const h3_geom &geom, int n_tokens, int head_dim,
                        hipStream_t s);
 void launch_qk_norm_rope(bf16_t *qkvq, int64_t ld, int n_tokens, int d, int head_dim,

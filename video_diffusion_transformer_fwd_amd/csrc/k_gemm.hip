@@ -46,26 +46,6 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
-// GELU(x) = x Phi(x) with Phi the standard normal CDF.  erfc by Abramowitz & Stegun, Handbook
-// of Mathematical Functions, formula 7.1.26: erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2) with
-// t = 1 / (1 + p z), z >= 0, absolute error <= 1.5e-7.  With z = |x| / sqrt 2 and
-// q = erfc(z) / 2 = Phi(-|x|), x Phi(x) = x / 2 + |x| (1/2 - q) holds for either sign of x, so
-// the product needs no branch or select: one reciprocal, one exponential, eight FMA/multiplies.
-// The factor 1/2 of q is folded into the coefficients, 1/sqrt 2 into p and the exponent.
-__device__ __forceinline__ float gelu_erf(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.0f + (0.3275911f * 0.70710678118654752f) * ax);
-  float h = 0.5f * 1.061405429f;
-  h = h * t - 0.5f * 1.453152027f;
-  h = h * t + 0.5f * 1.421413741f;
-  h = h * t - 0.5f * 0.284496736f;
-  h = h * t + 0.5f * 0.254829592f;
-  h = h * t;
-  const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // exp(-x^2 / 2)
-  const float q = h * e;
-  return __builtin_fmaf(ax, 0.5f - q, 0.5f * x);
-}
-
 // LDS holds 64 banks of 4 bytes; a 16-byte-per-lane read is served 16 lanes per cycle.  Tile
 // rows are 128 bytes, so two rows share one 256-byte bank line: chunk c of row r is stored in
 // slot c ^ ((r >> 1) & 7), which puts the 16 rows an MFMA-operand read touches at one chunk

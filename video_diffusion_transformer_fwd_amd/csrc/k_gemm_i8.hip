@@ -19,8 +19,8 @@
 // second launch adds the S partials (integer addition: exact in any order) and dequantises, so
 // the result equals the unsplit product bit for bit.  Grouped mode folds each group's int32
 // sums into a float32 total in group order inside the kernel and is never split (the float
-// fold order is fixed).  The dequantising epilogue runs from an LDS band in a rolled loop, as
-// in the bf16 product.
+// fold order is fixed).  The dequantising epilogue (optionally followed by the exact-erf GELU
+// of the bf16 product) runs from an LDS band in a rolled loop, as in the bf16 product.
 #include <hip/hip_runtime.h>
 
 #include "h3_internal.h"
@@ -76,7 +76,7 @@ struct GemmI8Args {
   int32_t *part;  // split-K int32 partials [S][M][N] (row mode)
 };
 
-template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT>
+template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT, int EPI>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
 #pragma clang fp contract(off)
   static_assert(!(GROUPED && SPLIT > 1), "the grouped float fold is never split");
@@ -326,7 +326,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
       const float4 w4 = *reinterpret_cast<const float4 *>(ssw + col);
       const float4 b4 = *reinterpret_cast<const float4 *>(sbias + col);
       const float t0 = a4.x * w4.x, t1 = a4.y * w4.y, t2 = a4.z * w4.z, t3 = a4.w * w4.w;
-      const float o[4] = {t0 + b4.x, t1 + b4.y, t2 + b4.z, t3 + b4.w};
+      float o[4] = {t0 + b4.x, t1 + b4.y, t2 + b4.z, t3 + b4.w};
+      if constexpr (EPI == H3_EPI_GELU) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = gelu_erf(o[e]);
+      }
       const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
       if (vec && n + 3 < g.N) {
         uint2 pk;
@@ -340,8 +344,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
   }
 }
 
-// Adds the S int32 partials (exact) and dequantises: bf16(((float(sum) * SA[m]) * SW[n]) + b[n]).
-template <int S>
+// Adds the S int32 partials (exact) and dequantises: bf16(((float(sum) * SA[m]) * SW[n]) + b[n]),
+// then GELU when EPI says so.
+template <int S, int EPI>
 __global__ __launch_bounds__(256) void splitk_i8_reduce_kernel(const int32_t *__restrict__ part,
                                                                int M, int N,
                                                                const float *__restrict__ SA,
@@ -371,6 +376,7 @@ __global__ __launch_bounds__(256) void splitk_i8_reduce_kernel(const int32_t *__
     const float v = static_cast<float>(sv[e]) * sa;
     const float t = v * SW[n + e];
     o[e] = t + bf2f(bias[n + e]);
+    if constexpr (EPI == H3_EPI_GELU) o[e] = gelu_erf(o[e]);
   }
   bf16_t *dst = C + static_cast<int64_t>(m) * ldc + n;
   if (ldc % 4 == 0 && (reinterpret_cast<uintptr_t>(C) % 8) == 0) {
@@ -384,11 +390,11 @@ __global__ __launch_bounds__(256) void splitk_i8_reduce_kernel(const int32_t *__
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT>
+template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT, int EPI>
 void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS, GROUPED, SPLIT>;
+  auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS, GROUPED, SPLIT, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -399,7 +405,7 @@ void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
   kern<<<tiles * SPLIT, Cfg::NT, Cfg::LDS_BYTES, s>>>(a);
   if constexpr (SPLIT > 1) {
     const int64_t total4 = static_cast<int64_t>(a.M) * a.N / 4;
-    splitk_i8_reduce_kernel<SPLIT><<<static_cast<int>((total4 + 255) / 256), 256, 0, s>>>(
+    splitk_i8_reduce_kernel<SPLIT, EPI><<<static_cast<int>((total4 + 255) / 256), 256, 0, s>>>(
         a.part, a.M, a.N, a.SA, a.SW, a.bias, a.C, a.ldc);
   }
 }
@@ -410,51 +416,62 @@ void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
 //   grouped, M >= 4096                   192x192, 4 waves, three LDS stages (never split)
 //   grouped, otherwise                   128x256, 4 waves, three LDS stages
 //   row, M >= 4096                       256x256, 8 waves, two LDS stages
-//   row, 1024 <= M < 4096                384x192, 8 waves, K split in 4
-//   row, 192 <= M < 1024                 192x192, 4 waves, K split in 4
+//   row, 1024 <= M < 4096                384x192, 8 waves; K split in 4 when N < 8192
+//   row, 192 <= M < 1024                 192x192, 4 waves; K split in 4 when N < 8192
 //   row, otherwise                       128x128, 4 waves
 // A split needs K % (128 * split) == 0 and N % 4 == 0.
 GemmPlan plan_gemm_i8(int M, int N, int K, int group) {
   GemmPlan p{};
   p.cfg = 0;
   p.split = 1;
+  const int wide_split = N >= 8192 ? 1 : 4;
   if (group != K) {
     p.cfg = M >= 4096 ? 1 : 3;
   } else if (M >= 4096) {
     p.cfg = 2;
   } else if (M >= 1024) {
     p.cfg = 4;
-    p.split = 4;
+    p.split = wide_split;
   } else if (M >= 192) {
     p.cfg = 1;
-    p.split = 4;
+    p.split = wide_split;
   }
   if (p.split > 1 && (K % (128 * p.split) != 0 || N % 4 != 0)) p.split = 1;
   if (p.split > 1) p.part_bytes = static_cast<size_t>(p.split) * M * N * sizeof(int32_t);
   return p;
 }
 
-void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
-                    const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
-                    hipStream_t s, const SplitScratch &sc) {
-  GemmPlan p = plan_gemm_i8(M, N, K, group);
-  if (p.split > 1 && (!sc.part || p.part_bytes > sc.part_bytes)) p.split = 1;
-  GemmI8Args a{QA, SA, QW, SW, bias, C, ldc, M, N, K, group, reinterpret_cast<int32_t *>(sc.part)};
-  if (group != K) {
+namespace {
+template <int EPI>
+void dispatch_i8(const GemmPlan &p, const GemmI8Args &a, bool grouped, hipStream_t s) {
+  if (grouped) {
     if (p.cfg == 1)
-      run_gemm_i8<192, 192, 2, 2, 3, true, 1>(a, s);
+      run_gemm_i8<192, 192, 2, 2, 3, true, 1, EPI>(a, s);
     else
-      run_gemm_i8<128, 256, 2, 2, 3, true, 1>(a, s);
+      run_gemm_i8<128, 256, 2, 2, 3, true, 1, EPI>(a, s);
     return;
   }
   switch (p.cfg * 8 + p.split) {
-    case 2 * 8 + 1: run_gemm_i8<256, 256, 2, 4, 2, false, 1>(a, s); break;
-    case 4 * 8 + 1: run_gemm_i8<384, 192, 4, 2, 2, false, 1>(a, s); break;
-    case 4 * 8 + 4: run_gemm_i8<384, 192, 4, 2, 2, false, 4>(a, s); break;
-    case 1 * 8 + 1: run_gemm_i8<192, 192, 2, 2, 3, false, 1>(a, s); break;
-    case 1 * 8 + 4: run_gemm_i8<192, 192, 2, 2, 3, false, 4>(a, s); break;
-    default: run_gemm_i8<128, 128, 2, 2, 3, false, 1>(a, s); break;
+    case 2 * 8 + 1: run_gemm_i8<256, 256, 2, 4, 2, false, 1, EPI>(a, s); break;
+    case 4 * 8 + 1: run_gemm_i8<384, 192, 4, 2, 2, false, 1, EPI>(a, s); break;
+    case 4 * 8 + 4: run_gemm_i8<384, 192, 4, 2, 2, false, 4, EPI>(a, s); break;
+    case 1 * 8 + 1: run_gemm_i8<192, 192, 2, 2, 3, false, 1, EPI>(a, s); break;
+    case 1 * 8 + 4: run_gemm_i8<192, 192, 2, 2, 3, false, 4, EPI>(a, s); break;
+    default: run_gemm_i8<128, 128, 2, 2, 3, false, 1, EPI>(a, s); break;
   }
+}
+}  // namespace
+
+void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
+                    const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
+                    hipStream_t s, const SplitScratch &sc, int epilogue) {
+  GemmPlan p = plan_gemm_i8(M, N, K, group);
+  if (p.split > 1 && (!sc.part || p.part_bytes > sc.part_bytes)) p.split = 1;
+  GemmI8Args a{QA, SA, QW, SW, bias, C, ldc, M, N, K, group, reinterpret_cast<int32_t *>(sc.part)};
+  if (epilogue == H3_EPI_GELU)
+    dispatch_i8<H3_EPI_GELU>(p, a, group != K, s);
+  else
+    dispatch_i8<H3_EPI_NONE>(p, a, group != K, s);
 }
 
 }  // namespace h3

@@ -48,17 +48,57 @@ __device__ __forceinline__ void load8f(const float *p, float *f) {
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
+// ------------------------------------------------------------------ int8 row quantisation
+// Per group of channels: s = absmax / 127 (IEEE float32 division), q = clamp(rint(x / s),
+// -127, 127) with x / s the correctly rounded float32 quotient and ties to even; s == 0 gives
+// q = 0.  The quotient is formed as x * r with r = rcp(s) (within 1 ulp): for |x / s| <= 127
+// that differs from the correctly rounded quotient by at most 3.1e-5, so both round to the
+// same integer unless the value lies within that distance of a half-integer; those rare
+// elements (|frac - 1/2| < 4e-5) take the exact division.  The result is the exact rule's.
+__device__ __forceinline__ uint32_t quant4(const float *x, float s, float r) {
+  float t[4];
+  int near = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    t[k] = x[k] * r;
+    const float f = t[k] - floorf(t[k]);
+    if (fabsf(f - 0.5f) < 4e-5f) near |= 1 << k;
+  }
+  // a reciprocal that is not a finite positive number (s tiny) sends every element to the
+  // exact division; s == 0 is handled below
+  if (s > 0.f && !(r > 0.f && r < 3.0e38f)) near = 0xF;
+  // wave-uniform branch: the divisions run only when some lane of the wave needs one
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(near != 0) != 0, 0)) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (near & (1 << k)) t[k] = x[k] / s;
+  }
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float u = fminf(fmaxf(rintf(t[k]), -127.f), 127.f);
+    const int q = s > 0.f ? static_cast<int>(u) : 0;
+    w |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * k);
+  }
+  return w;
+}
+__device__ __forceinline__ float quant_rcp(float s) { return s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f; }
+
 // ------------------------------------------------------------------ gate + AdaLN
 // GATE: x' = bf16(x + g*y) stored to x_out.  NORM: n = bf16((v - mean) * rstd * (1 + sc) + sh)
 // over the row v (= x' when GATE, else the row of x).  The fused variant (GATE && NORM)
 // normalises the bf16-rounded x' held in registers; the unfused pair writes x' and reads it
 // back.  Both run the identical NORM code below (same lane mapping, order and operations),
 // so their outputs are bit-identical.
-template <int VPL, bool GATE, bool NORM>
+// QUANT (with NORM): instead of n, the row of bf16-rounded n is quantised to int8 with one
+// scale per row by the quant4 rule above and written as q_out (int8) and s_out (float32), the
+// same bits as storing n and quantising it with the row quantiser.
+template <int VPL, bool GATE, bool NORM, bool QUANT>
 __global__ __launch_bounds__(256) void gate_adaln_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ y, const float *__restrict__ gate,
     bf16_t *x_out, const float *__restrict__ shift, const float *__restrict__ scale,
-    bf16_t *__restrict__ n_out, int rows, int d) {
+    bf16_t *__restrict__ n_out, int8_t *__restrict__ q_out, float *__restrict__ s_out, int rows,
+    int d) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -105,21 +145,46 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
       load8f(scale + e, sc);
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = ((v[i][k] - mean) * rstd) * (1.0f + sc[k]) + sh[k];
-      *reinterpret_cast<uint4 *>(n_out + base + e) = pack8(o);
+      if constexpr (QUANT) {
+        // keep the bf16-rounded output in place of the (no longer needed) input vector
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[i][k] = bf2f(f2bf(o[k]));
+      } else {
+        *reinterpret_cast<uint4 *>(n_out + base + e) = pack8(o);
+      }
+    }
+    if constexpr (QUANT) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[i][k]));
+      m = wave_max(m);
+      const float sq = m / 127.0f, rq = quant_rcp(sq);
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int e = (i * 64 + lane) * 8;
+        uint2 w;
+        w.x = quant4(v[i], sq, rq);
+        w.y = quant4(v[i] + 4, sq, rq);
+        *reinterpret_cast<uint2 *>(q_out + base + e) = w;
+      }
+      if (lane == 0) s_out[row] = sq;
     }
   }
 }
 
-template <bool GATE, bool NORM>
+template <bool GATE, bool NORM, bool QUANT>
 void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
-                         const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
-                         hipStream_t s) {
+                         const float *shift, const float *scale, bf16_t *n_out, int8_t *q_out,
+                         float *s_out, int rows, int d, hipStream_t s) {
   dim3 grid((rows + 3) / 4), block(256);
   switch (d / 512) {
-#define H3_CASE(V)                                                                      \
-  case V:                                                                               \
-    gate_adaln_kernel<V, GATE, NORM><<<grid, block, 0, s>>>(x, y, gate, x_out, shift, scale, \
-                                                            n_out, rows, d);           \
+#define H3_CASE(V)                                                                          \
+  case V:                                                                                   \
+    gate_adaln_kernel<V, GATE, NORM, QUANT><<<grid, block, 0, s>>>(x, y, gate, x_out, shift,  \
+                                                                   scale, n_out, q_out, s_out, \
+                                                                   rows, d);                \
     break;
     H3_CASE(1) H3_CASE(2) H3_CASE(3) H3_CASE(4) H3_CASE(5) H3_CASE(6) H3_CASE(8) H3_CASE(10)
     H3_CASE(12) H3_CASE(16)
@@ -276,26 +341,6 @@ __global__ void euler_kernel(float *__restrict__ x, const float *__restrict__ v,
   }
 }
 
-// ------------------------------------------------------------------ int8 row quantisation
-// One wave per row.  Per group of `group` channels: s = absmax / 127 (IEEE float32 division),
-// q = clamp(rint(x / s), -127, 127) with ties to even; s == 0 gives q = 0.  With
-// group == 1024 a group is two 8-channel vectors per lane and stays in registers; with one
-// group per row the row is read twice (the second read hits the cache).
-__device__ __forceinline__ uint32_t quant4(const float *x, float s) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    int q = 0;
-    if (s > 0.f) {
-      float t = rintf(x[k] / s);
-      t = fminf(fmaxf(t, -127.f), 127.f);
-      q = static_cast<int>(t);
-    }
-    w |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * k);
-  }
-  return w;
-}
-
 // group == 1024: one wave per (row, group), 16 channels per lane.
 __global__ __launch_bounds__(256) void quant_groups_kernel(const bf16_t *__restrict__ X,
                                                            int8_t *__restrict__ Q,
@@ -316,10 +361,10 @@ __global__ __launch_bounds__(256) void quant_groups_kernel(const bf16_t *__restr
 #pragma unroll
   for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(a[k]));
   m = wave_max(m);
-  const float s = m / 127.0f;
+  const float s = m / 127.0f, r = quant_rcp(s);
   uint2 w0, w1;
-  w0.x = quant4(a, s); w0.y = quant4(a + 4, s);
-  w1.x = quant4(a + 8, s); w1.y = quant4(a + 12, s);
+  w0.x = quant4(a, s, r); w0.y = quant4(a + 4, s, r);
+  w1.x = quant4(a + 8, s, r); w1.y = quant4(a + 12, s, r);
   *reinterpret_cast<uint2 *>(qr + e0) = w0;
   *reinterpret_cast<uint2 *>(qr + e1) = w1;
   if (lane == 0) S[item] = s;
@@ -352,14 +397,14 @@ __global__ __launch_bounds__(128) void quant_row_kernel(const bf16_t *__restrict
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   m = fmaxf(red[0], red[1]);
-  const float s = m / 127.0f;
+  const float s = m / 127.0f, r = quant_rcp(s);
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     float a[8];
     unpack8(raw[v], a);
     uint2 w;
-    w.x = quant4(a, s);
-    w.y = quant4(a + 4, s);
+    w.x = quant4(a, s, r);
+    w.y = quant4(a + 4, s, r);
     *reinterpret_cast<uint2 *>(qr + (v * 128 + tid) * 8) = w;
   }
   if (tid == 0) S[row] = s;
@@ -382,13 +427,13 @@ __global__ __launch_bounds__(256) void quant_row_any_kernel(const bf16_t *__rest
     for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(a[k]));
   }
   m = wave_max(m);
-  const float s = m / 127.0f;
+  const float s = m / 127.0f, r = quant_rcp(s);
   for (int e = lane * 8; e < K; e += 512) {
     float a[8];
     unpack8(*reinterpret_cast<const uint4 *>(xr + e), a);
     uint2 w;
-    w.x = quant4(a, s);
-    w.y = quant4(a + 4, s);
+    w.x = quant4(a, s, r);
+    w.y = quant4(a + 4, s, r);
     *reinterpret_cast<uint2 *>(qr + e) = w;
   }
   if (lane == 0) S[row] = s;
@@ -450,14 +495,20 @@ __global__ void add_table_kernel(const float *__restrict__ Mv, const bf16_t *__r
 
 void launch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
                        const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
-                       hipStream_t s) {
+                       hipStream_t s, int8_t *q_out, float *s_out) {
   if (rows <= 0) return;
-  if (y && n_out)
-    dispatch_gate_adaln<true, true>(x, y, gate, x_out, shift, scale, n_out, rows, d, s);
-  else if (y)
-    dispatch_gate_adaln<true, false>(x, y, gate, x_out, shift, scale, n_out, rows, d, s);
-  else
-    dispatch_gate_adaln<false, true>(x, y, gate, x_out, shift, scale, n_out, rows, d, s);
+  if (q_out) {
+    if (y)
+      dispatch_gate_adaln<true, true, true>(x, y, gate, x_out, shift, scale, nullptr, q_out, s_out, rows, d, s);
+    else
+      dispatch_gate_adaln<false, true, true>(x, y, gate, x_out, shift, scale, nullptr, q_out, s_out, rows, d, s);
+  } else if (y && n_out) {
+    dispatch_gate_adaln<true, true, false>(x, y, gate, x_out, shift, scale, n_out, nullptr, nullptr, rows, d, s);
+  } else if (y) {
+    dispatch_gate_adaln<true, false, false>(x, y, gate, x_out, shift, scale, n_out, nullptr, nullptr, rows, d, s);
+  } else {
+    dispatch_gate_adaln<false, true, false>(x, y, gate, x_out, shift, scale, n_out, nullptr, nullptr, rows, d, s);
+  }
 }
 
 void launch_rope_table(float2 *table, const h3_geom &geom, int n_tokens, int head_dim,

@@ -30,7 +30,8 @@ class Geometry:
         return dict(f_lat=self.f_lat, grid_h=self.grid_h, grid_w=self.grid_w, scale=self.scale)
 
 
-def _upload_block(w: S.Workload, b: int, seed: int, device, with_int8: bool) -> dict:
+def _upload_block(w: S.Workload, b: int, seed: int, device, with_int8: bool,
+                  with_int8_linear: bool = False) -> dict:
     t = S.block_weights(w, b, seed)
     d, F = w.d_model, w.ffn_dim
     dev = {
@@ -46,6 +47,11 @@ def _upload_block(w: S.Workload, b: int, seed: int, device, with_int8: bool) -> 
     if with_int8:
         out["fc2_q"] = torch.empty((d, F), dtype=torch.int8, device=device)
         out["fc2_s"] = torch.empty((d,), dtype=torch.float32, device=device)
+    if with_int8_linear:
+        out["qkvq_q"] = torch.empty((4 * d, d), dtype=torch.int8, device=device)
+        out["qkvq_s"] = torch.empty((4 * d,), dtype=torch.float32, device=device)
+        out["fc1_q"] = torch.empty((F, d), dtype=torch.int8, device=device)
+        out["fc1_s"] = torch.empty((F,), dtype=torch.float32, device=device)
     return out
 
 
@@ -53,9 +59,10 @@ class DiTModel:
     """A synthetic MiniMax-H3-shaped DiT resident in HBM, bound to the C ABI."""
 
     def __init__(self, w: S.Workload, seed: int = 0, device="cuda:0", with_int8=None,
-                 workers=None, blocks=None):
+                 workers=None, blocks=None, with_int8_linear=None):
         self.w, self.seed, self.device = w, seed, torch.device(device)
         self.with_int8 = (w.fc2_mode != "bf16") if with_int8 is None else with_int8
+        self.with_int8_linear = w.int8_linear if with_int8_linear is None else with_int8_linear
         self.geo = Geometry(w)
         g = S.global_weights(w, seed)
         self.gw = {k: v.contiguous().to(self.device) for k, v in g.items()}
@@ -67,8 +74,8 @@ class DiTModel:
         torch.set_num_threads(1)
         try:
             with cf.ThreadPoolExecutor(workers) as ex:
-                futs = {ex.submit(_upload_block, w, b, seed, self.device, self.with_int8): b
-                        for b in range(nb)}
+                futs = {ex.submit(_upload_block, w, b, seed, self.device, self.with_int8,
+                                  self.with_int8_linear): b for b in range(nb)}
                 for f in cf.as_completed(futs):
                     self.blocks[futs[f]] = f.result()
         finally:
@@ -83,6 +90,8 @@ class DiTModel:
         self.handle = B.h3_model_create(self.dims, self.g_struct, self.b_structs)
         if self.with_int8:
             B.h3_quantize_fc2_weights(self.handle)
+        if self.with_int8_linear:
+            B.h3_quantize_linear_weights(self.handle)
         self.ctx = S.context(w, seed).to(self.device)
         self.ctx_kv = torch.empty((nb, 2, w.ctx_len, w.d_model), dtype=torch.bfloat16, device=self.device)
         B.h3_prepare_context(self.handle, self.ctx, self.ctx_kv)
@@ -103,7 +112,8 @@ class DiTModel:
         return B.h3_select_layers(self.mod_table_bits, n_active)
 
     def opts(self, **kw):
-        base = dict(fc2_mode=self.w.fc2_mode, token_reduction=self.w.token_reduction)
+        base = dict(fc2_mode=self.w.fc2_mode, token_reduction=self.w.token_reduction,
+                    int8_linear=self.w.int8_linear)
         base.update(kw)
         return B.make_opts(**base)
 

@@ -73,6 +73,7 @@ class Workload:
     layers: int = 0            # 0 = all blocks
     token_reduction: bool = False
     fc2_mode: str = "bf16"
+    int8_linear: bool = False  # int8 QKV and FC1 with row-quantised AdaLN outputs
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -95,6 +96,10 @@ WORKLOADS = {
     # same shape, 50 blocks, per-row int8 FC2
     "512sq_22f_int8": Workload("512sq_22f_int8", 512, 512, 22, 3072, 24, 12288, 256, 50,
                                steps=4, fc2_mode="row"),
+    # same shape with the whole int8 path: int8 QKV and FC1 (quantisation fused into the gated
+    # AdaLN) and the per-row int8 FC2
+    "512sq_22f_int8_all": Workload("512sq_22f_int8_all", 512, 512, 22, 3072, 24, 12288, 256, 50,
+                                   steps=4, fc2_mode="row", int8_linear=True),
     # 768x1344, 243 frames, one forward
     "768x1344_243f": Workload("768x1344_243f", 1344, 768, 243, 5120, 40, 20480, 512, 50,
                               steps=1),
