@@ -25,6 +25,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kBlockM = 128;  // queries per workgroup
 constexpr int kBlockN = 64;   // keys per tile
+constexpr float kLazy = 8.0f; // log2 headroom of the lazily moved softmax reference
 
 template <int D>
 struct AttnCfg {
@@ -69,7 +70,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
   f32x16_t o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_ref: running reference maximum (raw score units) of this lane's query; -inf until the
+  // first tile, whose maximum always raises it (alpha = 2^-inf = 0 clears nothing yet stored)
+  float m_ref = -INFINITY, l_run = 0.f;
 
   // staging registers for the next K/V tile
   uint4 kreg[Cfg::K_PASSES];
@@ -136,36 +139,47 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     }
-    // scale, mask, tile max (lane's 32 scores + partner lane)
+    // Online softmax with the scale folded into the exponent: p = 2^(s c - m c) with the raw
+    // score s, c = log2(e) / sqrt(D) and m a running reference maximum in raw units.  The
+    // reference only moves up when some lane's tile maximum exceeds it by more than
+    // kLazy / c (p stays <= 2^kLazy); O and l are rescaled then, which leaves O / l exact.
+    if (kv0 + kBlockN > nk) {  // keys beyond n_k (last tile only)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kv0 + kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
+          if (key >= nk) s[kb][i] = -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kv0 + kb * 32 + 8 * (i / 4) + 4 * g + (i % 4);
-        float v = s[kb][i] * scale_log2;
-        v = key < nk ? v : -INFINITY;
-        s[kb][i] = v;
-        mt = fmaxf(mt, v);
-      }
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const bool raise = mt * scale_log2 > m_ref * scale_log2 + kLazy;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform: rare after the first tiles
+      const float m_new = raise ? mt : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m_ref = m_new;
+    }
+    const float mc = m_ref * scale_log2;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], scale_log2, -mc));
         s[kb][i] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    l_run += psum;
 
     // O^T += V^T P^T over 4 steps of 16 keys
 #pragma unroll
