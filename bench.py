@@ -123,7 +123,10 @@ def main():
     n, nb_act = geo.n_tokens, w.n_active
     active = model.active()
     opts = model.opts()
-    sig, fresh, n_fresh = B.h3_schedule(w.steps, w.reuse, 1)
+    sig, fresh, n_fresh = B.h3_schedule(w.steps, w.reuse, w.core_reuse)
+    # core-residual reuse: every step runs the patch and the head; the marked steps the core
+    core_delta = (torch.empty((n, w.d_model), dtype=torch.float32, device=model.device)
+                  if w.core_reuse > 1 else None)
     lat = model.initial_latent()
     v = torch.empty((n, w.latent_ch), dtype=torch.float32, device=model.device)
     ev_count = [0]
@@ -141,7 +144,14 @@ def main():
 
     def step(k, timed=False):
         i = k % w.steps
-        if fresh[i]:
+        if core_delta is not None:
+            e = ev_count[0] % max(n_fresh, 1)
+            model.forward_cached(lat, float(sig[i]), bool(fresh[i]), core_delta, active, e, opts, v)
+            if fresh[i]:
+                ev_count[0] += 1
+                if timed:
+                    timed_rows.extend(rows_per_block(e))
+        elif fresh[i]:
             e = ev_count[0] % max(n_fresh, 1)
             model.forward(lat, float(sig[i]), active, e, opts, v)
             ev_count[0] += 1
@@ -192,7 +202,7 @@ def main():
         "config": {"workload": w.name, "width": w.width, "height": w.height, "frames": w.frames,
                    "tokens": n, "blocks": nb_act, "d_model": w.d_model, "heads": w.n_heads,
                    "ffn": w.ffn_dim, "ctx_len": w.ctx_len, "steps": w.steps, "reuse": w.reuse,
-                   "fc2": w.fc2_mode, "int8_qkv_fc1": w.int8_linear,
+                   "core_reuse": w.core_reuse, "fc2": w.fc2_mode, "int8_qkv_fc1": w.int8_linear,
                    "token_reduction": w.token_reduction},
         "ms_per_fresh_eval": round(elapsed * 1e3 / max(n_evals, 1), 3),
         "actual_tokens_blocks_per_s": round(actual_tok_blocks, 1),

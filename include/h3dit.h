@@ -85,12 +85,14 @@ int32_t h3_token_grid(int32_t width, int32_t height, int32_t reference_rope,
  * exactly N denoising passes on a linear grid with one endpoint; P3 "aggressive levers"
  * and P4 table: `--reuse r` evaluates the denoiser at 20/11/8 of 20 steps for r = 1/2/3
  * and extrapolates the skipped transitions; P2 §4: --reuse and --core-reuse exclude each
- * other.
+ * other, and --core-reuse k (k <= 6) runs the core less often while the patch and the
+ * timestep-dependent head stay fresh (h3_dit_forward_cached).
  *   sigmas (host, float[steps + 1]): sigma_i = (float)(steps - i) / (float)steps.
- *   fresh  (host, uint8[steps]): 1 iff i % reuse == 0 or i == steps - 1.
- *   n_fresh: number of fresh evaluations.
- * steps >= 1, reuse >= 1, core_reuse >= 1 (H3_EINVAL); reuse > 1 with core_reuse > 1 is
- * H3_EINVAL; core_reuse > 1 alone is H3_EUNSUPPORTED (not part of this path). */
+ *   fresh  (host, uint8[steps]): 1 iff i % r == 0 or i == steps - 1, r = reuse, or
+ *          core_reuse when that is > 1 (then: the steps whose core runs fresh).
+ *   n_fresh: number of fresh evaluations (of the core, with core_reuse > 1).
+ * steps >= 1, reuse >= 1, 1 <= core_reuse <= 6 (H3_EINVAL); reuse > 1 with core_reuse > 1
+ * is H3_EINVAL. */
 int32_t h3_schedule(int32_t steps, int32_t reuse, int32_t core_reuse, float *sigmas,
                     uint8_t *fresh, int32_t *n_fresh);
 
@@ -265,6 +267,22 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
                        const float *latent, float sigma, const int32_t *active,
                        int32_t n_active, int32_t eval_index, const void *ctx_kv,
                        float *velocity, void *ws, size_t ws_bytes, void *stream);
+
+/* One evaluation under core-residual reuse (P2 §4, P3 "aggressive levers": --core-reuse k
+ * runs the expensive core less often while the patch and the timestep-dependent head stay
+ * fresh on every step; h3_schedule(.., core_reuse = k, ..) marks the core steps).
+ *   refresh_core = 1: exactly h3_dit_forward, and core_delta (device, float [N, d]) receives
+ *     x_L - x_0: the bf16 stream after the last active block (full resolution, after any
+ *     bypass restore) minus the bf16 patch embedding, subtracted in float32.
+ *   refresh_core = 0: the blocks are skipped: x = bf16(patch(latent) + core_delta) goes through
+ *     the final AdaLN of sigma and the head (active, eval_index and the token reduction
+ *     option are then unused).
+ * Other arguments as h3_dit_forward. */
+int32_t h3_dit_forward_cached(const h3_model *m, const h3_geom *geom, const h3_run_opts *o,
+                              const float *latent, float sigma, const int32_t *active,
+                              int32_t n_active, int32_t eval_index, const void *ctx_kv,
+                              int32_t refresh_core, float *core_delta, float *velocity, void *ws,
+                              size_t ws_bytes, void *stream);
 
 /* Euler transition (P4 §2): latent[i] += (sigma_next - sigma_cur) * velocity[i], float32,
  * the step computed on the host in float32.  latent, velocity: device float [n_elems]. */

@@ -405,7 +405,32 @@ def dit_forward(latent, model, sigma, active, geom, n_heads, eval_index=0, qk_no
             trace.setdefault("x_after", []).append(x)
     if saved is not None:
         x = token_restore(saved, x, plan["pairs"])
+    if trace is not None:
+        trace["x_core_out"] = x
     return final_head(x, g, fin)
+
+
+def dit_forward_cached(latent, model, sigma, active, geom, n_heads, core_delta=None,
+                       eval_index=0, qk_norm=True, fc2_mode="bf16", token_reduction=False,
+                       int8_linear=False):
+    """One evaluation under core-residual reuse: returns (velocity, core delta).
+
+    P2 §4 / P3 "aggressive levers": ``--core-reuse`` runs the expensive core less often while
+    the patch and the timestep-dependent head stay fresh on every step.
+    Reading: the core is the stack of active blocks; its residual delta is
+    x_L - x_0, x_0 = patch(latent) and x_L the full-resolution stream after the last active
+    block (after any bypass restore).  ``core_delta`` None: a fresh evaluation, which
+    returns its velocity and its delta; otherwise the blocks are skipped and the stream
+    patch(latent) + core_delta goes through the final AdaLN of this sigma and the head.
+    """
+    g = model["global"]
+    if core_delta is None:
+        tr = {}
+        v = dit_forward(latent, model, sigma, active, geom, n_heads, eval_index, qk_norm,
+                        fc2_mode, token_reduction, trace=tr, int8_linear=int8_linear)
+        return v, tr["x_core_out"] - patch_embed(latent, g)
+    _, fin = modulation(g, sigma)
+    return final_head(patch_embed(latent, g) + core_delta, g, fin), core_delta
 
 
 def euler_step(x, v, sigma_cur, sigma_next):
@@ -414,17 +439,24 @@ def euler_step(x, v, sigma_cur, sigma_next):
 
 
 def denoise(latent0, model, steps, reuse, active, geom, n_heads, qk_norm=True,
-            fc2_mode="bf16", token_reduction=False, int8_linear=False):
+            fc2_mode="bf16", token_reduction=False, int8_linear=False, core_reuse=1):
     """The Euler loop: ``steps`` transitions, fresh evaluations per ``host.schedule``.
 
     Skipped steps reuse the last fresh velocity (P3 "aggressive levers": reuse extrapolates
-    the skipped transitions).  Returns (x_N, number of fresh evaluations).
+    the skipped transitions).  With ``core_reuse`` > 1 every step evaluates the patch and the
+    head and only the marked steps run the core (``dit_forward_cached``).  Returns (x_N,
+    number of fresh (core) evaluations).
     """
-    sig, fresh = host.schedule(steps, reuse)
+    sig, fresh = host.schedule(steps, reuse, core_reuse)
     x = np.asarray(latent0, dtype=np.float64)
-    v, ev = None, 0
+    v, ev, delta = None, 0, None
     for i in range(steps):
-        if fresh[i]:
+        if core_reuse > 1:
+            v, delta = dit_forward_cached(x, model, float(sig[i]), active, geom, n_heads,
+                                          None if fresh[i] else delta, ev, qk_norm, fc2_mode,
+                                          token_reduction, int8_linear)
+            ev += int(fresh[i])
+        elif fresh[i]:
             v = dit_forward(x, model, float(sig[i]), active, geom, n_heads, ev, qk_norm,
                             fc2_mode, token_reduction, int8_linear=int8_linear)
             ev += 1

@@ -80,18 +80,22 @@ def schedule(steps: int, reuse: int = 1, core_reuse: int = 1):
     P2 §4: ``--reuse`` and ``--core-reuse`` are mutually exclusive.
     Reading: sigma_i = (N - i) / N in float32, i = 0..N (so sigma_N = 0); step i is fresh
     iff i mod r == 0 or i == N - 1; a skipped step reuses the last fresh velocity.
-    Core-residual reuse is not part of this path (only core_reuse == 1 is accepted).
+    P2 §4 / P3 "aggressive levers": ``--core-reuse k`` runs the heavy core less often while
+    the patch and the timestep-dependent head stay fresh every step; values above 6 are not
+    offered.  Reading: the same rule with r = k marks the steps whose core runs fresh
+    (``fresh`` then means "core fresh"); 1 <= k <= 6.
     Returns (sigmas float32[N+1], fresh uint8[N]).
     """
     if steps < 1 or reuse < 1 or core_reuse < 1:
         raise ValueError("steps, reuse, core_reuse must be >= 1")
     if reuse > 1 and core_reuse > 1:
         raise ValueError("--reuse and --core-reuse are mutually exclusive")
-    if core_reuse > 1:
-        raise NotImplementedError("core-residual reuse is outside this path")
+    if core_reuse > 6:
+        raise ValueError("core_reuse must be at most 6")
+    r = reuse if reuse > 1 else core_reuse
     n = np.float32(steps)
     sig = np.array([np.float32(steps - i) / n for i in range(steps + 1)], dtype=np.float32)
-    fresh = np.array([1 if (i % reuse == 0 or i == steps - 1) else 0 for i in range(steps)],
+    fresh = np.array([1 if (i % r == 0 or i == steps - 1) else 0 for i in range(steps)],
                      dtype=np.uint8)
     return sig, fresh
 

@@ -82,9 +82,15 @@ def test_schedule_matches_oracle_bit_exact(lib):
     with pytest.raises(B.H3Error) as e:
         B.h3_schedule(20, 2, 4)
     assert e.value.code == B.H3_EINVAL
+    for steps in (1, 4, 6, 20):
+        for k in range(2, 7):
+            sig, fresh, nf = B.h3_schedule(steps, 1, k)
+            osig, ofresh = host.schedule(steps, 1, k)
+            np.testing.assert_array_equal(fresh, ofresh)
+            assert nf == int(ofresh.sum())
     with pytest.raises(B.H3Error) as e:
-        B.h3_schedule(20, 1, 4)
-    assert e.value.code == B.H3_EUNSUPPORTED
+        B.h3_schedule(20, 1, 7)
+    assert e.value.code == B.H3_EINVAL
 
 
 def test_select_layers_matches_oracle_on_synthetic_tables(lib):

@@ -177,3 +177,59 @@ def test_int8_path_forward_and_loop():
         assert_close(f64(v), ref, rel=2e-2, elem=8e-2, what=f"int8 velocity token_reduction={tr}")
     loop_parity(w, model, om, {"fc2_mode": "grouped", "int8_linear": True, "token_reduction": True},
                 6, 2, active)
+
+
+@pytest.mark.parametrize("tr", [False, True])
+def test_core_reuse_cached_forward(tr):
+    w = TR_SMALL
+    model = DiTModel(w)
+    om = oracle_model(w)
+    active = model.active()
+    lat = model.initial_latent()
+    n, d = model.geo.n_tokens, w.d_model
+    opts = model.opts(token_reduction=tr)
+    v_plain = model.forward(lat, 0.6, active, 2, opts).clone()
+    delta = torch.empty((n, d), dtype=torch.float32, device=DEV)
+    v_fresh = model.forward_cached(lat, 0.6, True, delta, active, 2, opts).clone()
+    torch.cuda.synchronize()
+    # the fresh cached evaluation is the forward, bit for bit
+    assert np.array_equal(bits(v_fresh), bits(v_plain))
+    tr_ref = {}
+    v_ref = dit.dit_forward(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads,
+                            eval_index=2, token_reduction=tr, trace=tr_ref)
+    _, d_ref = dit.dit_forward_cached(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads,
+                                      eval_index=2, token_reduction=tr)
+    # the delta is a small difference of two bf16 streams: besides 2e-2 of its own norm it
+    # carries the bf16 rounding of every residual update of the stream, about sqrt(blocks)
+    # units of 2^-9 relative to the stream (a wrong sign or a missed restore is far above)
+    err = np.linalg.norm(f64(delta) - d_ref)
+    floor = 2.0 ** -8 * np.sqrt(len(active)) * np.linalg.norm(tr_ref["x_core_out"])
+    assert err <= 2e-2 * np.linalg.norm(d_ref) + floor, (err, np.linalg.norm(d_ref), floor)
+    assert np.linalg.norm(d_ref) > 4 * floor   # the bar still resolves the delta itself
+    # reused at the same latent and sigma: x_0 + delta is the core output again
+    v_reuse = model.forward_cached(lat, 0.6, False, delta, active, 2, opts)
+    torch.cuda.synchronize()
+    assert rel_l2(f64(v_reuse), f64(v_fresh)) < 1e-3
+    # reused at another point: the oracle's patch + cached delta + head of that sigma
+    lat2 = lat * 0.8
+    v2 = model.forward_cached(lat2, 0.35, False, delta, active, 2, opts)
+    torch.cuda.synchronize()
+    ref2, _ = dit.dit_forward_cached(f64(lat2), om, 0.35, active, model.geo.as_dict(), w.n_heads,
+                                     core_delta=f64(delta))
+    assert_close(f64(v2), ref2, rel=2e-2, elem=8e-2, what="reused velocity")
+
+
+def test_core_reuse_loop():
+    w = dataclasses.replace(S.WORKLOADS["tiny_256sq_5f"], steps=7, core_reuse=3)
+    model = DiTModel(w)
+    om = oracle_model(w)
+    lat0 = model.initial_latent()
+    x = lat0.clone()
+    ev = model.denoise(x, 7, 1, [0, 1], model.opts(), core_reuse=3)
+    torch.cuda.synchronize()
+    ref, ev_ref = dit.denoise(f64(lat0), om, 7, 1, [0, 1], model.geo.as_dict(), w.n_heads,
+                              core_reuse=3)
+    assert ev == ev_ref == 3
+    r1 = rel_l2(f64(x), ref)
+    r2 = rel_l2(f64(x) - f64(lat0), ref - f64(lat0))
+    assert r1 < 5e-2 and r2 < 5e-2, (r1, r2)

@@ -182,3 +182,53 @@ def test_denoise_counts_and_reuse_hold():
     v2 = dit.dit_forward(xb, mdl, float(sig[2]), [0, 1], geom, 2, 1)
     np.testing.assert_allclose(x2, dit.euler_step(xb, v2, sig[2], sig[3]), rtol=1e-13, atol=1e-13)
     assert ev == 2
+
+
+def test_core_reuse_cached_evaluation_at_the_fresh_point_is_the_fresh_velocity():
+    # x_0 + (x_L - x_0) = x_L: a reused evaluation at the same latent and sigma reproduces
+    # the fresh velocity; with token pairing the delta is taken after the bypass restore
+    mdl = tiny_model(nb=5)
+    geom = dict(f_lat=1, grid_h=2, grid_w=3, scale=1.0)
+    lat = RNG.normal(size=(6, 6))
+    for tr in (False, True):
+        v, delta = dit.dit_forward_cached(lat, mdl, 0.6, [0, 1, 2, 3, 4], geom, 2,
+                                          token_reduction=tr)
+        np.testing.assert_allclose(v, dit.dit_forward(lat, mdl, 0.6, [0, 1, 2, 3, 4], geom, 2,
+                                                      token_reduction=tr), rtol=1e-13, atol=1e-13)
+        v2, d2 = dit.dit_forward_cached(lat, mdl, 0.6, [0, 1, 2, 3, 4], geom, 2, core_delta=delta)
+        assert d2 is delta
+        np.testing.assert_allclose(v2, v, rtol=1e-12, atol=1e-12)
+        assert np.abs(delta).max() > 1e-3
+
+
+def test_core_reuse_with_zero_gates_has_zero_delta():
+    mdl = _zero_gate_model(tiny_model(nb=3))
+    geom = dict(f_lat=1, grid_h=2, grid_w=2, scale=1.0)
+    lat = RNG.normal(size=(4, 6))
+    _, delta = dit.dit_forward_cached(lat, mdl, 0.7, [0, 1, 2], geom, 2)
+    np.testing.assert_allclose(delta, 0.0, atol=1e-13)
+
+
+def test_core_reuse_loop_refreshes_patch_and_head_only():
+    # --core-reuse 2 over 3 steps: steps 0 and 2 run the core; step 1 reuses step 0's delta
+    # with its own latent and its own sigma in the head
+    mdl = tiny_model(nb=2)
+    geom = dict(f_lat=1, grid_h=2, grid_w=2, scale=1.0)
+    lat = RNG.normal(size=(4, 6))
+    g = mdl["global"]
+    x3, ev = dit.denoise(lat, mdl, 3, 1, [0, 1], geom, 2, core_reuse=2)
+    assert ev == 2
+    sig, fresh = host.schedule(3, 1, 2)
+    assert list(fresh) == [1, 0, 1]
+    tr = {}
+    v0 = dit.dit_forward(lat, mdl, float(sig[0]), [0, 1], geom, 2, trace=tr)
+    delta = tr["x_core_out"] - dit.patch_embed(lat, g)
+    xa = dit.euler_step(lat, v0, sig[0], sig[1])
+    _, fin1 = dit.modulation(g, float(sig[1]))
+    v1 = dit.final_head(dit.patch_embed(xa, g) + delta, g, fin1)
+    xb = dit.euler_step(xa, v1, sig[1], sig[2])
+    v2 = dit.dit_forward(xb, mdl, float(sig[2]), [0, 1], geom, 2, 1)
+    np.testing.assert_allclose(x3, dit.euler_step(xb, v2, sig[2], sig[3]), rtol=1e-12, atol=1e-12)
+    # and it differs from whole-velocity reuse, which would keep v0 on step 1
+    x3r, _ = dit.denoise(lat, mdl, 3, 2, [0, 1], geom, 2)
+    assert not np.allclose(x3, x3r)

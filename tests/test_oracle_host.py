@@ -96,10 +96,20 @@ def test_reuse_fresh_positions_and_last_step():
 def test_reuse_and_core_reuse_exclusive():
     with pytest.raises(ValueError):
         host.schedule(20, 2, 4)
-    with pytest.raises(NotImplementedError):
-        host.schedule(20, 1, 4)
+    with pytest.raises(ValueError):
+        host.schedule(20, 1, 7)   # core-reuse values above 6 are not offered
     with pytest.raises(ValueError):
         host.schedule(0)
+
+
+def test_core_reuse_marks_core_fresh_steps_like_reuse():
+    # the same rule as --reuse: step i runs the core iff i mod k == 0 or it is the last step
+    for k in range(2, 7):
+        _, fresh_c = host.schedule(20, 1, k)
+        _, fresh_r = host.schedule(20, k, 1)
+        np.testing.assert_array_equal(fresh_c, fresh_r)
+    _, fresh = host.schedule(20, 1, 4)
+    assert list(np.nonzero(fresh)[0]) == [0, 4, 8, 12, 16, 19]
 
 
 def _table_with_scores(scores, d=3):

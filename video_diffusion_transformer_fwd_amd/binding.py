@@ -90,6 +90,8 @@ SIGNATURES = {
                                 _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "h3_dit_forward": (_I32, [_VP, C.POINTER(h3_geom), C.POINTER(h3_run_opts), _VP, _F, _PI32,
                               _I32, _I32, _VP, _VP, _VP, _SZ, _VP]),
+    "h3_dit_forward_cached": (_I32, [_VP, C.POINTER(h3_geom), C.POINTER(h3_run_opts), _VP, _F, _PI32,
+                                     _I32, _I32, _VP, _I32, _VP, _VP, _VP, _SZ, _VP]),
     "h3_euler_step": (_I32, [_VP, _VP, _F, _F, _I64, _VP]),
     "h3_token_reduce": (_I32, [_I32, C.POINTER(h3_geom), _I32, _VP, _VP, _VP, _VP]),
     "h3_gemm_bf16": (_I32, [_VP, _I64, _VP, _I64, _VP, _I64, _I32, _I32, _I32, _VP, _VP, _I32,
@@ -270,6 +272,15 @@ def h3_dit_forward(m, geom, opts, latent, sigma, active, eval_index, ctx_kv, vel
                                 act.ctypes.data_as(_PI32), len(act), eval_index, ptr(ctx_kv),
                                 ptr(velocity), ptr(ws), ws.numel() * ws.element_size(),
                                 stream_handle(stream)))
+
+
+def h3_dit_forward_cached(m, geom, opts, latent, sigma, active, eval_index, ctx_kv, refresh_core,
+                          core_delta, velocity, ws, stream=None):
+    act = np.ascontiguousarray(active, dtype=np.int32)
+    _check(lib().h3_dit_forward_cached(m, C.byref(geom), C.byref(opts), ptr(latent), sigma,
+                                       act.ctypes.data_as(_PI32), len(act), eval_index, ptr(ctx_kv),
+                                       int(refresh_core), ptr(core_delta), ptr(velocity), ptr(ws),
+                                       ws.numel() * ws.element_size(), stream_handle(stream)))
 
 
 def h3_euler_step(latent, velocity, sigma_cur, sigma_next, stream=None):

@@ -91,6 +91,7 @@ WsPlan plan_workspace(const Model &m, int32_t n, const h3_run_opts &o) {
   p.n1b = take(bytes_bf16(n * d));
   p.lat16 = take(bytes_bf16(n * C));
   p.rope_r = take(static_cast<size_t>(n * half) * sizeof(float2));
+  p.x0 = take(bytes_bf16(n * d));  // patch embedding kept for the core-residual delta
   p.total = off;
   return p;
 }
@@ -438,10 +439,19 @@ int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
                    p, s, rope);
 }
 
-int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts *o,
-                       const float *latent, float sigma, const int32_t *active, int32_t n_active,
-                       int32_t eval_index, const void *ctx_kv, float *velocity, void *ws,
-                       size_t ws_bytes, void *stream) {
+namespace {
+enum CoreMode { kCorePlain = 0, kCoreFresh = 1, kCoreReuse = 2 };
+}
+
+// One evaluation.  kCorePlain: the forward.  kCoreFresh: the forward, and core_delta =
+// x_L - x_0 (stream after the last active block minus the patch embedding).  kCoreReuse:
+// x = bf16(x_0 + core_delta), then the final AdaLN of sigma and the head; the blocks are
+// skipped.
+static int32_t forward_impl(const h3_model *m, const h3_geom *geom, const h3_run_opts *o,
+                            const float *latent, float sigma, const int32_t *active,
+                            int32_t n_active, int32_t eval_index, const void *ctx_kv,
+                            float *velocity, void *ws, size_t ws_bytes, void *stream,
+                            int core_mode, float *core_delta) {
   if (int32_t e = validate_model(m)) return e;
   if (int32_t e = check_opts(o)) return e;
   if (!geom || geom->paired) return fail(H3_EINVAL, "h3_dit_forward: geom must be the full grid");
@@ -491,6 +501,26 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
     launch_f32_to_bf16(latent, lat16, static_cast<int64_t>(n) * C, s);
     launch_gemm_bf16(lat16, C, reinterpret_cast<const bf16_t *>(m->g.patch_w), C, x, d, n, d, C,
                      reinterpret_cast<const bf16_t *>(m->g.patch_b), nullptr, H3_EPI_NONE, 0, s);
+  }
+  const int64_t nd = static_cast<int64_t>(n) * d;
+  bf16_t *x0 = reinterpret_cast<bf16_t *>(w + p.x0);
+  if (core_mode == kCoreReuse) {
+    // cached core: x = bf16(x_0 + delta); final AdaLN of this sigma; head
+    launch_core_apply(x, core_delta, x, nd, s);
+    bf16_t *nh = reinterpret_cast<bf16_t *>(w + p.n1b);
+    {
+      ProfScope ps(H3_ST_ADALN, s);
+      launch_gate_adaln(x, nullptr, nullptr, nullptr, fin, fin + d, nh, n, d, s);
+    }
+    ProfScope ps(H3_ST_HEAD, s);
+    launch_gemm_bf16(nh, d, reinterpret_cast<const bf16_t *>(m->g.head_w), d, velocity, C, n, C, d,
+                     reinterpret_cast<const bf16_t *>(m->g.head_b), nullptr, H3_EPI_NONE, 1, s);
+    return check_launch("h3_dit_forward_cached");
+  }
+  if (core_mode == kCoreFresh) {
+    if (hipMemcpyAsync(x0, x, static_cast<size_t>(nd) * sizeof(bf16_t), hipMemcpyDeviceToDevice, s) !=
+        hipSuccess)
+      return fail(H3_EHIP, "h3_dit_forward_cached: copy of the patch embedding failed");
   }
   launch_rope_table(rope_full, *geom, n, m->head_dim, s);
   h3_geom red = *geom;
@@ -560,6 +590,7 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
       n1_valid = true;
     }
   }
+  if (core_mode == kCoreFresh) launch_core_delta(x, x0, core_delta, nd, s);
   // head: velocity = AdaLN_final(x) W_h^T + b_h, float32
   {
     ProfScope ps(H3_ST_HEAD, s);
@@ -568,6 +599,26 @@ int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts
                      reinterpret_cast<const bf16_t *>(m->g.head_b), nullptr, H3_EPI_NONE, 1, s);
   }
   return check_launch("h3_dit_forward");
+}
+
+int32_t h3_dit_forward(const h3_model *m, const h3_geom *geom, const h3_run_opts *o,
+                       const float *latent, float sigma, const int32_t *active, int32_t n_active,
+                       int32_t eval_index, const void *ctx_kv, float *velocity, void *ws,
+                       size_t ws_bytes, void *stream) {
+  return forward_impl(m, geom, o, latent, sigma, active, n_active, eval_index, ctx_kv, velocity,
+                      ws, ws_bytes, stream, kCorePlain, nullptr);
+}
+
+int32_t h3_dit_forward_cached(const h3_model *m, const h3_geom *geom, const h3_run_opts *o,
+                              const float *latent, float sigma, const int32_t *active,
+                              int32_t n_active, int32_t eval_index, const void *ctx_kv,
+                              int32_t refresh_core, float *core_delta, float *velocity, void *ws,
+                              size_t ws_bytes, void *stream) {
+  if (!core_delta) return fail(H3_EINVAL, "h3_dit_forward_cached: core_delta is NULL");
+  if (refresh_core != 0 && refresh_core != 1)
+    return fail(H3_EINVAL, "h3_dit_forward_cached: refresh_core must be 0 or 1");
+  return forward_impl(m, geom, o, latent, sigma, active, n_active, eval_index, ctx_kv, velocity,
+                      ws, ws_bytes, stream, refresh_core ? kCoreFresh : kCoreReuse, core_delta);
 }
 
 int32_t h3_euler_step(float *latent, const float *velocity, float sigma_cur, float sigma_next,

@@ -85,13 +85,15 @@ int32_t h3_schedule(int32_t steps, int32_t reuse, int32_t core_reuse, float *sig
     return fail(H3_EINVAL, "h3_schedule: steps, reuse, core_reuse must be >= 1");
   if (reuse > 1 && core_reuse > 1)
     return fail(H3_EINVAL, "h3_schedule: --reuse and --core-reuse are mutually exclusive");
-  if (core_reuse > 1)
-    return fail(H3_EUNSUPPORTED, "h3_schedule: core-residual reuse is not part of this path");
+  if (core_reuse > 6) return fail(H3_EINVAL, "h3_schedule: core_reuse must be at most 6");
   const float n = static_cast<float>(steps);
   for (int32_t i = 0; i <= steps; ++i) sigmas[i] = static_cast<float>(steps - i) / n;
+  // whole-velocity reuse (reuse > 1) or core-residual reuse (core_reuse > 1): the same rule
+  // marks the steps whose core runs fresh
+  const int32_t r = reuse > 1 ? reuse : core_reuse;
   int32_t cnt = 0;
   for (int32_t i = 0; i < steps; ++i) {
-    fresh[i] = (i % reuse == 0 || i == steps - 1) ? 1 : 0;
+    fresh[i] = (i % r == 0 || i == steps - 1) ? 1 : 0;
     cnt += fresh[i];
   }
   *n_fresh = cnt;

@@ -70,7 +70,7 @@ struct WsPlan {
   size_t n1, qkvq, attn, y, n2, h, m, hq, hs, rope, gpart;
   size_t gpart_bytes;
   // forward / modulation part
-  size_t mod, fin, tmp, x, xr, n1b, lat16, rope_r;
+  size_t mod, fin, tmp, x, xr, n1b, lat16, rope_r, x0;
   size_t total;
 };
 WsPlan plan_workspace(const Model &m, int32_t n_tokens, const h3_run_opts &o);
@@ -121,6 +121,11 @@ void launch_qk_norm_rope(bf16_t *qkvq, int64_t ld, int n_tokens, int d, int head
 void launch_token_reduce(int direction, const h3_geom &geom, int d, const bf16_t *src,
                          const bf16_t *bypass, bf16_t *dst, hipStream_t s);
 void launch_euler(float *x, const float *v, float dt, int64_t n, hipStream_t s);
+// Core-residual reuse (n % 8 == 0): delta = float(x_core) - float(x_patch); x = bf16(float(x_patch)
+// + delta) (x may equal x_patch).
+void launch_core_delta(const bf16_t *x_core, const bf16_t *x_patch, float *delta, int64_t n,
+                       hipStream_t s);
+void launch_core_apply(const bf16_t *x_patch, const float *delta, bf16_t *x, int64_t n, hipStream_t s);
 void launch_quant_rows(const bf16_t *X, int8_t *Q, float *S, int rows, int K, int group,
                        hipStream_t s);
 void launch_f32_to_bf16(const float *src, bf16_t *dst, int64_t n, hipStream_t s);

@@ -341,6 +341,38 @@ __global__ void euler_kernel(float *__restrict__ x, const float *__restrict__ v,
   }
 }
 
+// ------------------------------------------------------------------ core-residual reuse
+// delta = float(x_core) - float(x_patch) over n elements (8 per thread).
+__global__ void core_delta_kernel(const bf16_t *__restrict__ x_core, const bf16_t *__restrict__ x_patch,
+                                  float *__restrict__ delta, int64_t n) {
+#pragma clang fp contract(off)
+  const int64_t i8 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  if (i8 >= n) return;
+  float a[8], b[8];
+  unpack8(*reinterpret_cast<const uint4 *>(x_core + i8), a);
+  unpack8(*reinterpret_cast<const uint4 *>(x_patch + i8), b);
+  float4 lo, hi;
+  lo.x = a[0] - b[0]; lo.y = a[1] - b[1]; lo.z = a[2] - b[2]; lo.w = a[3] - b[3];
+  hi.x = a[4] - b[4]; hi.y = a[5] - b[5]; hi.z = a[6] - b[6]; hi.w = a[7] - b[7];
+  reinterpret_cast<float4 *>(delta + i8)[0] = lo;
+  reinterpret_cast<float4 *>(delta + i8)[1] = hi;
+}
+
+// x = bf16(float(x_patch) + delta), in place on x_patch allowed (8 per thread).
+__global__ void core_apply_kernel(const bf16_t *x_patch, const float *__restrict__ delta,
+                                  bf16_t *x, int64_t n) {
+#pragma clang fp contract(off)
+  const int64_t i8 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 8;
+  if (i8 >= n) return;
+  float a[8];
+  unpack8(*reinterpret_cast<const uint4 *>(x_patch + i8), a);
+  const float4 lo = reinterpret_cast<const float4 *>(delta + i8)[0];
+  const float4 hi = reinterpret_cast<const float4 *>(delta + i8)[1];
+  a[0] = a[0] + lo.x; a[1] = a[1] + lo.y; a[2] = a[2] + lo.z; a[3] = a[3] + lo.w;
+  a[4] = a[4] + hi.x; a[5] = a[5] + hi.y; a[6] = a[6] + hi.z; a[7] = a[7] + hi.w;
+  *reinterpret_cast<uint4 *>(x + i8) = pack8(a);
+}
+
 // group == 1024: one wave per (row, group), 16 channels per lane.
 __global__ __launch_bounds__(256) void quant_groups_kernel(const bf16_t *__restrict__ X,
                                                            int8_t *__restrict__ Q,
@@ -543,6 +575,17 @@ void launch_token_reduce(int direction, const h3_geom &geom, int d, const bf16_t
     token_merge_kernel<<<blocks, 256, 0, s>>>(src, dst, n_red, geom.grid_w, d);
   else
     token_restore_kernel<<<blocks, 256, 0, s>>>(src, bypass, dst, n_red, geom.grid_w, d);
+}
+
+void launch_core_delta(const bf16_t *x_core, const bf16_t *x_patch, float *delta, int64_t n,
+                       hipStream_t s) {
+  const int64_t threads = n / 8;
+  core_delta_kernel<<<static_cast<int>((threads + 255) / 256), 256, 0, s>>>(x_core, x_patch, delta, n);
+}
+
+void launch_core_apply(const bf16_t *x_patch, const float *delta, bf16_t *x, int64_t n, hipStream_t s) {
+  const int64_t threads = n / 8;
+  core_apply_kernel<<<static_cast<int>((threads + 255) / 256), 256, 0, s>>>(x_patch, delta, x, n);
 }
 
 void launch_euler(float *x, const float *v, float dt, int64_t n, hipStream_t s) {

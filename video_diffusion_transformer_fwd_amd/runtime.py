@@ -132,16 +132,37 @@ class DiTModel:
                          self.ctx_kv, velocity, ws)
         return velocity
 
-    def denoise(self, latent, steps=None, reuse=None, active=None, opts=None):
-        """Euler loop in place on ``latent``; returns the number of fresh evaluations."""
+    def forward_cached(self, latent, sigma, refresh_core, core_delta, active=None, eval_index=0,
+                       opts=None, velocity=None):
+        """One evaluation under core-residual reuse (``core_delta``: float32 [N, d])."""
+        opts = opts or self.opts()
+        active = self.active() if active is None else active
+        n = self.geo.n_tokens
+        if velocity is None:
+            velocity = torch.empty((n, self.w.latent_ch), dtype=torch.float32, device=self.device)
+        ws = self.workspace(n, opts)
+        B.h3_dit_forward_cached(self.handle, self.geo.geom, opts, latent, float(sigma), active,
+                                eval_index, self.ctx_kv, refresh_core, core_delta, velocity, ws)
+        return velocity
+
+    def denoise(self, latent, steps=None, reuse=None, active=None, opts=None, core_reuse=None):
+        """Euler loop in place on ``latent``; returns the number of fresh (core) evaluations."""
         steps = steps or self.w.steps
         reuse = reuse or self.w.reuse
-        sig, fresh, _ = B.h3_schedule(steps, reuse, 1)
+        core_reuse = core_reuse or self.w.core_reuse
+        sig, fresh, _ = B.h3_schedule(steps, reuse, core_reuse)
         active = self.active() if active is None else active
         v = torch.empty((self.geo.n_tokens, self.w.latent_ch), dtype=torch.float32, device=self.device)
+        delta = None
+        if core_reuse > 1:
+            delta = torch.empty((self.geo.n_tokens, self.w.d_model), dtype=torch.float32,
+                                device=self.device)
         ev = 0
         for i in range(steps):
-            if fresh[i]:
+            if delta is not None:
+                self.forward_cached(latent, float(sig[i]), bool(fresh[i]), delta, active, ev, opts, v)
+                ev += int(fresh[i])
+            elif fresh[i]:
                 self.forward(latent, float(sig[i]), active, ev, opts, v)
                 ev += 1
             B.h3_euler_step(latent, v, float(sig[i]), float(sig[i + 1]))

@@ -74,6 +74,7 @@ class Workload:
     token_reduction: bool = False
     fc2_mode: str = "bf16"
     int8_linear: bool = False  # int8 QKV and FC1 with row-quantised AdaLN outputs
+    core_reuse: int = 1        # --core-reuse k (exclusive with reuse > 1)
     extra: dict = field(default_factory=dict, compare=False)
 
     @property
@@ -100,6 +101,10 @@ WORKLOADS = {
     # AdaLN) and the per-row int8 FC2
     "512sq_22f_int8_all": Workload("512sq_22f_int8_all", 512, 512, 22, 3072, 24, 12288, 256, 50,
                                    steps=4, fc2_mode="row", int8_linear=True),
+    # same shape, --steps 20 --layers 45 --core-reuse 4: the core runs on 6 of the 20 steps,
+    # patch and head on every step
+    "512sq_22f_core4": Workload("512sq_22f_core4", 512, 512, 22, 3072, 24, 12288, 256, 50,
+                                steps=20, layers=45, core_reuse=4),
     # 768x1344, 243 frames, one forward
     "768x1344_243f": Workload("768x1344_243f", 1344, 768, 243, 5120, 40, 20480, 512, 50,
                               steps=1),
