@@ -378,7 +378,9 @@ int32_t h3_qk_norm_rope(void *qkvq, int64_t ld, int32_t n_tokens, int32_t d_mode
 
 /* ------------------------------------------------------------------------------------
  * Per-stage timing (HIP events recorded on the launch stream around every launch of the
- * selected stages).  One session per process; not thread-safe.
+ * selected stages).  One session per process; not thread-safe.  Inside a block the self- and
+ * cross-attention run as one launch, timed under H3_ST_SELF_ATTN (H3_ST_CROSS_ATTN then
+ * counts no launch).
  * ---------------------------------------------------------------------------------- */
 enum {
   H3_ST_MODULATION = 0, H3_ST_PATCH, H3_ST_ADALN, H3_ST_QKV_GEMM, H3_ST_QK_NORM_ROPE,

@@ -184,16 +184,12 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
     launch_qk_norm_rope(qkvq, 4 * d, rows, d, D, reinterpret_cast<const bf16_t *>(w.q_gamma),
                         reinterpret_cast<const bf16_t *>(w.k_gamma), o.qk_norm, rope_table, s);
   }
-  // self-attention -> attn[:, 0:d]; cross-attention -> attn[:, d:2d]
+  // self-attention -> attn[:, 0:d] and cross-attention -> attn[:, d:2d], in one launch
   {
     ProfScope ps(H3_ST_SELF_ATTN, s);
-    launch_attention(qkvq, 4 * d, qkvq + d, 4 * d, qkvq + 2 * d, 4 * d, attn, 2 * d, rows, rows,
-                     H, D, s);
-  }
-  {
-    ProfScope ps(H3_ST_CROSS_ATTN, s);
-    launch_attention(qkvq + 3 * d, 4 * d, ctx_kv, d, ctx_kv + static_cast<size_t>(L) * d, d,
-                     attn + d, 2 * d, rows, L, H, D, s);
+    launch_attention_pair(qkvq, 4 * d, qkvq + d, 4 * d, qkvq + 2 * d, 4 * d, attn, 2 * d, rows, rows,
+                          qkvq + 3 * d, 4 * d, ctx_kv, d, ctx_kv + static_cast<size_t>(L) * d, d,
+                          attn + d, 2 * d, rows, L, H, D, s);
   }
   // y = [O | Oc] [W_o | W_oc]^T + b_o + b_oc
   {

@@ -105,6 +105,12 @@ void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const f
 void launch_attention(const bf16_t *Q, int64_t ldq, const bf16_t *K, int64_t ldk,
                       const bf16_t *V, int64_t ldv, bf16_t *O, int64_t ldo, int nq, int nk,
                       int heads, int head_dim, hipStream_t s);
+// Two independent attention problems of the same head layout in one launch.
+void launch_attention_pair(const bf16_t *Q0, int64_t ldq0, const bf16_t *K0, int64_t ldk0,
+                           const bf16_t *V0, int64_t ldv0, bf16_t *O0, int64_t ldo0, int nq0, int nk0,
+                           const bf16_t *Q1, int64_t ldq1, const bf16_t *K1, int64_t ldk1,
+                           const bf16_t *V1, int64_t ldv1, bf16_t *O1, int64_t ldo1, int nq1, int nk1,
+                           int heads, int head_dim, hipStream_t s);
 // x_out = bf16(x + gate*y) (if y != nullptr), then n_out = bf16(LN(x_out)(1+scale)+shift)
 // (if n_out != nullptr).  With y == nullptr the row is read from x.  x_out may equal x.
 // With q_out != nullptr the normalised row is not stored as bf16 but quantised: q_out int8

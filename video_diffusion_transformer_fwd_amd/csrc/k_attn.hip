@@ -13,6 +13,8 @@
 // Keys beyond n_k are masked to -inf; query rows beyond n_q are computed and not stored.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "h3_internal.h"
 
 namespace h3 {
@@ -38,12 +40,34 @@ struct AttnCfg {
   static constexpr size_t LDS_BYTES = (kBlockN * KS + D * VS) * sizeof(bf16_t);
 };
 
+// One attention problem; a launch may carry two (blockIdx.z selects), e.g. the self- and the
+// cross-attention of a block, so the short one fills the CUs the other leaves idle.
+struct AttnProblem {
+  const bf16_t *Q;
+  int64_t ldq;
+  const bf16_t *K;
+  int64_t ldk;
+  const bf16_t *V;
+  int64_t ldv;
+  bf16_t *O;
+  int64_t ldo;
+  int nq, nk;
+};
+struct AttnProblems {
+  AttnProblem p[2];
+};
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void attention_kernel(
-    const bf16_t *__restrict__ Q, int64_t ldq, const bf16_t *__restrict__ K, int64_t ldk,
-    const bf16_t *__restrict__ V, int64_t ldv, bf16_t *__restrict__ O, int64_t ldo, int nq,
-    int nk, float scale_log2) {
+__global__ __launch_bounds__(256, 2) void attention_kernel(AttnProblems probs, float scale_log2) {
   using Cfg = AttnCfg<D>;
+  const AttnProblem &pb_ = probs.p[blockIdx.z];
+  const bf16_t *__restrict__ Q = pb_.Q;
+  const bf16_t *__restrict__ K = pb_.K;
+  const bf16_t *__restrict__ V = pb_.V;
+  bf16_t *__restrict__ O = pb_.O;
+  const int64_t ldq = pb_.ldq, ldk = pb_.ldk, ldv = pb_.ldv, ldo = pb_.ldo;
+  const int nq = pb_.nq, nk = pb_.nk;
+  if (static_cast<int>(blockIdx.x) * kBlockM >= nq) return;  // this problem has fewer query tiles
   __shared__ __align__(16) bf16_t Ks[kBlockN * Cfg::KS];
   __shared__ __align__(16) bf16_t Vt[D * Cfg::VS];
 
@@ -220,15 +244,36 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(
 
 }  // namespace
 
+namespace {
+void launch_problems(const AttnProblems &pr, int n_problems, int heads, int head_dim, hipStream_t s) {
+  int tiles = 0;
+  for (int i = 0; i < n_problems; ++i) tiles = std::max(tiles, (pr.p[i].nq + kBlockM - 1) / kBlockM);
+  dim3 grid(tiles, heads, n_problems), block(256);
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
+  if (head_dim == 128)
+    attention_kernel<128><<<grid, block, 0, s>>>(pr, scale_log2);
+  else
+    attention_kernel<64><<<grid, block, 0, s>>>(pr, scale_log2);
+}
+}  // namespace
+
 void launch_attention(const bf16_t *Q, int64_t ldq, const bf16_t *K, int64_t ldk,
                       const bf16_t *V, int64_t ldv, bf16_t *O, int64_t ldo, int nq, int nk,
                       int heads, int head_dim, hipStream_t s) {
-  dim3 grid((nq + kBlockM - 1) / kBlockM, heads), block(256);
-  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
-  if (head_dim == 128)
-    attention_kernel<128><<<grid, block, 0, s>>>(Q, ldq, K, ldk, V, ldv, O, ldo, nq, nk, scale_log2);
-  else
-    attention_kernel<64><<<grid, block, 0, s>>>(Q, ldq, K, ldk, V, ldv, O, ldo, nq, nk, scale_log2);
+  AttnProblems pr{};
+  pr.p[0] = AttnProblem{Q, ldq, K, ldk, V, ldv, O, ldo, nq, nk};
+  launch_problems(pr, 1, heads, head_dim, s);
+}
+
+void launch_attention_pair(const bf16_t *Q0, int64_t ldq0, const bf16_t *K0, int64_t ldk0,
+                           const bf16_t *V0, int64_t ldv0, bf16_t *O0, int64_t ldo0, int nq0, int nk0,
+                           const bf16_t *Q1, int64_t ldq1, const bf16_t *K1, int64_t ldk1,
+                           const bf16_t *V1, int64_t ldv1, bf16_t *O1, int64_t ldo1, int nq1, int nk1,
+                           int heads, int head_dim, hipStream_t s) {
+  AttnProblems pr{};
+  pr.p[0] = AttnProblem{Q0, ldq0, K0, ldk0, V0, ldv0, O0, ldo0, nq0, nk0};
+  pr.p[1] = AttnProblem{Q1, ldq1, K1, ldk1, V1, ldv1, O1, ldo1, nq1, nk1};
+  launch_problems(pr, 2, heads, head_dim, s);
 }
 
 }  // namespace h3
