@@ -20,9 +20,9 @@
 //
 // Tile shapes are chosen per problem by plan_gemm (measured on random bf16 operands): 384x192
 // tiles (8 waves of 96x96, two per SIMD, two LDS stages) for the wide QKV / FC1 products,
-// 256x256 tiles with 8 waves of 128x64 for the narrow products at large M and, with K split in
-// three, for the narrow (N = d) products of the 1536-token workload; 192x192 (4 waves, three
-// LDS stages) with K split in four for the narrow products at 768 tokens.
+// 256x256 tiles with 8 waves of 128x64 for the narrow products at large M, and 192x192 tiles
+// (4 waves, three LDS stages) with K split in two for the narrow (N = d) products of the
+// 1536-token workload and in four at 768 tokens.
 //
 // Split-K (S pieces of K per tile in separate workgroups): each piece stores its float32 partial
 // tile with plain stores; a second launch sums the S partials in piece order 0..S-1 and applies
@@ -397,7 +397,6 @@ void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
   switch (p.cfg * 8 + p.split) {
     case 4 * 8 + 1: run_product<384, 192, 4, 2, 2, EPI, OUT_F32, 1>(a, s); break;
     case 2 * 8 + 1: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 1>(a, s); break;
-    case 2 * 8 + 3: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 3>(a, s); break;
     case 1 * 8 + 1: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
     case 1 * 8 + 2: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s); break;
     case 1 * 8 + 4: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 4>(a, s); break;
@@ -412,7 +411,7 @@ void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
 //   N >= 8192, M >= 1536            384x192, 8 waves                 (QKV, FC1)
 //   M >= 4096, N >= 2048            256x256, 8 waves                 (narrow products, 768x1344)
 //   N >= 8192, M >= 192             192x192                          (QKV, FC1 at 768 tokens)
-//   1024 <= M < 4096, N < 8192      256x256, 8 waves, K split in 3   (out-proj, FC2 at 1536)
+//   1024 <= M < 4096, N < 8192      192x192, K split in 2            (out-proj, FC2 at 1536)
 //   192 <= M < 1024, N < 8192       192x192, K split in 4            (out-proj, FC2 at 768)
 //   otherwise                       128x128
 // A split needs K % (64 * split) == 0 and N % 4 == 0, else the product runs unsplit.
@@ -427,8 +426,8 @@ GemmPlan plan_gemm(int M, int N, int K) {
   } else if (N >= 8192 && M >= 192) {
     p.cfg = 1;
   } else if (M >= 1024 && N >= 256) {
-    p.cfg = 2;
-    p.split = 3;
+    p.cfg = 1;
+    p.split = 2;
   } else if (M >= 192 && N >= 192) {
     p.cfg = 1;
     p.split = 4;
