@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "h3_internal.h"
 
@@ -25,19 +26,24 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
-constexpr int kBlockM = 128;  // queries per workgroup
 constexpr int kBlockN = 64;   // keys per tile
 constexpr float kLazy = 8.0f; // log2 headroom of the lazily moved softmax reference
 
-template <int D>
+// WAVES wave64s per workgroup, 32 queries each: 4 (two workgroups per CU) for short
+// sequences, 8 (one per CU, still two waves per SIMD) for long ones, where the same K/V tile
+// then serves twice the queries and each thread stages half of it.
+template <int D, int WAVES>
 struct AttnCfg {
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int BM = 32 * WAVES;    // queries per workgroup
   static constexpr int KS = D + 8;         // K tile row stride (elements)
   static constexpr int VS = kBlockN + 4;   // V^T row stride: 136 bytes, so 32 rows of 8-byte reads cover 64 banks once
   static constexpr int CH = D / 8;         // 16-byte chunks per row
-  static constexpr int K_PASSES = kBlockN * CH / 256;
-  static constexpr int V_GROUPS = 256 / 32;          // chunk groups per pass (32 key pairs)
+  static constexpr int K_PASSES = kBlockN * CH / NT;
+  static constexpr int V_GROUPS = NT / 32;           // chunk groups per pass (32 key pairs)
   static constexpr int V_PASSES = CH / V_GROUPS;
-  static constexpr size_t LDS_BYTES = (kBlockN * KS + D * VS) * sizeof(bf16_t);
+  static_assert(K_PASSES >= 1 && kBlockN * CH % NT == 0, "K tile must split over the threads");
+  static_assert(V_PASSES >= 1 && CH % V_GROUPS == 0, "V tile must split over the threads");
 };
 
 // One attention problem; a launch may carry two (blockIdx.z selects), e.g. the self- and the
@@ -57,16 +63,22 @@ struct AttnProblems {
   AttnProblem p[2];
 };
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void attention_kernel(AttnProblems probs, float scale_log2) {
-  using Cfg = AttnCfg<D>;
-  const AttnProblem &pb_ = probs.p[blockIdx.z];
-  const bf16_t *__restrict__ Q = pb_.Q;
-  const bf16_t *__restrict__ K = pb_.K;
-  const bf16_t *__restrict__ V = pb_.V;
-  bf16_t *__restrict__ O = pb_.O;
-  const int64_t ldq = pb_.ldq, ldk = pb_.ldk, ldv = pb_.ldv, ldo = pb_.ldo;
-  const int nq = pb_.nq, nk = pb_.nk;
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kernel(
+    AttnProblems probs, float scale_log2) {
+  using Cfg = AttnCfg<D, WAVES>;
+  constexpr int kBlockM = Cfg::BM;
+  // select the problem with scalar conditionals (indexing the argument array by blockIdx.z
+  // would copy it to private memory)
+  const bool second = blockIdx.z != 0;
+  const AttnProblem &p0 = probs.p[0], &p1 = probs.p[1];
+  const bf16_t *__restrict__ Q = second ? p1.Q : p0.Q;
+  const bf16_t *__restrict__ K = second ? p1.K : p0.K;
+  const bf16_t *__restrict__ V = second ? p1.V : p0.V;
+  bf16_t *__restrict__ O = second ? p1.O : p0.O;
+  const int64_t ldq = second ? p1.ldq : p0.ldq, ldk = second ? p1.ldk : p0.ldk;
+  const int64_t ldv = second ? p1.ldv : p0.ldv, ldo = second ? p1.ldo : p0.ldo;
+  const int nq = second ? p1.nq : p0.nq, nk = second ? p1.nk : p0.nk;
   if (static_cast<int>(blockIdx.x) * kBlockM >= nq) return;  // this problem has fewer query tiles
   __shared__ __align__(16) bf16_t Ks[kBlockN * Cfg::KS];
   __shared__ __align__(16) bf16_t Vt[D * Cfg::VS];
@@ -101,13 +113,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnProblems probs, f
   // staging registers for the next K/V tile
   uint4 kreg[Cfg::K_PASSES];
   uint4 vreg[Cfg::V_PASSES][2];
-  const int k_row = tid / Cfg::CH, k_chunk = tid % Cfg::CH;  // K: 256/CH rows per pass
+  const int k_row = tid / Cfg::CH, k_chunk = tid % Cfg::CH;  // K: NT/CH rows per pass
   const int v_pair = tid & 31, v_group = tid >> 5;             // V: key pair, chunk group
 
   auto load_tile = [&](int kv0) {
 #pragma unroll
     for (int p = 0; p < Cfg::K_PASSES; ++p) {
-      const int r = kv0 + k_row + p * (256 / Cfg::CH);
+      const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
       kreg[p] = r < nk ? *reinterpret_cast<const uint4 *>(K + static_cast<int64_t>(r) * ldk + hoff + k_chunk * 8)
                        : make_uint4(0, 0, 0, 0);
     }
@@ -125,12 +137,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnProblems probs, f
   auto store_tile = [&]() {
 #pragma unroll
     for (int p = 0; p < Cfg::K_PASSES; ++p)
-      *reinterpret_cast<uint4 *>(Ks + (k_row + p * (256 / Cfg::CH)) * Cfg::KS + k_chunk * 8) = kreg[p];
+      *reinterpret_cast<uint4 *>(Ks + (k_row + p * (Cfg::NT / Cfg::CH)) * Cfg::KS + k_chunk * 8) = kreg[p];
 #pragma unroll
     for (int p = 0; p < Cfg::V_PASSES; ++p) {
       const int chunk = v_group + p * Cfg::V_GROUPS;
-      const uint32_t *a = reinterpret_cast<const uint32_t *>(&vreg[p][0]);
-      const uint32_t *b = reinterpret_cast<const uint32_t *>(&vreg[p][1]);
+      const uint4 va = vreg[p][0], vb = vreg[p][1];
+      const uint32_t a[4] = {va.x, va.y, va.z, va.w}, b[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // channels chunk*8 + 2w and +1; keys 2*v_pair (low half) and 2*v_pair+1 (high half)
@@ -245,15 +257,25 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnProblems probs, f
 }  // namespace
 
 namespace {
-void launch_problems(const AttnProblems &pr, int n_problems, int heads, int head_dim, hipStream_t s) {
+template <int D, int WAVES>
+void launch_cfg(const AttnProblems &pr, int n_problems, int heads, float scale_log2, hipStream_t s) {
+  constexpr int BM = AttnCfg<D, WAVES>::BM;
   int tiles = 0;
-  for (int i = 0; i < n_problems; ++i) tiles = std::max(tiles, (pr.p[i].nq + kBlockM - 1) / kBlockM);
-  dim3 grid(tiles, heads, n_problems), block(256);
+  for (int i = 0; i < n_problems; ++i) tiles = std::max(tiles, (pr.p[i].nq + BM - 1) / BM);
+  dim3 grid(tiles, heads, n_problems), block(64 * WAVES);
+  attention_kernel<D, WAVES><<<grid, block, 0, s>>>(pr, scale_log2);
+}
+
+void launch_problems(const AttnProblems &pr, int n_problems, int heads, int head_dim, hipStream_t s) {
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
-  if (head_dim == 128)
-    attention_kernel<128><<<grid, block, 0, s>>>(pr, scale_log2);
+  int nq = 0;
+  for (int i = 0; i < n_problems; ++i) nq = std::max(nq, pr.p[i].nq);
+  if (head_dim == 128 && nq >= 8192)
+    launch_cfg<128, 8>(pr, n_problems, heads, scale_log2, s);
+  else if (head_dim == 128)
+    launch_cfg<128, 4>(pr, n_problems, heads, scale_log2, s);
   else
-    attention_kernel<64><<<grid, block, 0, s>>>(pr, scale_log2);
+    launch_cfg<64, 4>(pr, n_problems, heads, scale_log2, s);
 }
 }  // namespace
 
