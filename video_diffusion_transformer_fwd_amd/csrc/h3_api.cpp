@@ -119,8 +119,23 @@ QRows qrows(const void *buf, int rows, int d) {
 
 // AdaLN (after the optional gate x <- x + g y) into dst: bf16 [rows, d], or row-quantised
 // (QRows layout) when quant.  fused = gate and AdaLN in one kernel (bit-identical either way).
+// yp (instead of y): the gate's y comes as split-K partials that the gate kernel reduces.
 void gate_then_adaln(bf16_t *x, const bf16_t *y, const float *g, const float *sh, const float *sc,
-                     void *dst, bool quant, bool fused, int rows, int d, hipStream_t s) {
+                     void *dst, bool quant, bool fused, int rows, int d, hipStream_t s,
+                     const GateY *yp = nullptr) {
+  if (yp) {
+    if (!fused) {
+      launch_gate_adaln_part(x, *yp, g, x, nullptr, nullptr, nullptr, rows, d, s);
+      y = nullptr;
+    } else if (quant) {
+      const QRows r = qrows(dst, rows, d);
+      launch_gate_adaln_part(x, *yp, g, x, sh, sc, nullptr, rows, d, s, r.q, r.s);
+      return;
+    } else {
+      launch_gate_adaln_part(x, *yp, g, x, sh, sc, reinterpret_cast<bf16_t *>(dst), rows, d, s);
+      return;
+    }
+  }
   if (y && !fused) {
     launch_gate_adaln(x, y, g, x, nullptr, nullptr, nullptr, rows, d, s);
     y = nullptr;
@@ -191,17 +206,24 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
                           qkvq + 3 * d, 4 * d, ctx_kv, d, ctx_kv + static_cast<size_t>(L) * d, d,
                           attn + d, 2 * d, rows, L, H, D, s);
   }
-  // y = [O | Oc] [W_o | W_oc]^T + b_o + b_oc
+  // y = [O | Oc] [W_o | W_oc]^T + b_o + b_oc.  When the product splits K, its partials go
+  // straight to the gate kernel, which sums them exactly as the split-K reduction would (and
+  // still stores y, so the workspace holds the branch either way).
+  GateY yp{sk.part, 0, static_cast<int64_t>(rows) * d, reinterpret_cast<const bf16_t *>(w.out_b),
+           reinterpret_cast<const bf16_t *>(w.outc_b), y};
   {
     ProfScope ps(H3_ST_OUT_GEMM, s);
-    launch_gemm_bf16(attn, 2 * d, reinterpret_cast<const bf16_t *>(w.out_w), 2 * d, y, d, rows,
-                     d, 2 * d, reinterpret_cast<const bf16_t *>(w.out_b),
-                     reinterpret_cast<const bf16_t *>(w.outc_b), H3_EPI_NONE, 0, s, sk);
+    yp.S = launch_gemm_bf16_partials(attn, 2 * d, reinterpret_cast<const bf16_t *>(w.out_w), 2 * d,
+                                     rows, d, 2 * d, s, sk);
+    if (!yp.S)
+      launch_gemm_bf16(attn, 2 * d, reinterpret_cast<const bf16_t *>(w.out_w), 2 * d, y, d, rows,
+                       d, 2 * d, yp.b1, yp.b2, H3_EPI_NONE, 0, s, sk);
   }
   // x <- x + g1 y ; n2 = AdaLN(x; sh2, sc2)
   {
     ProfScope ps(H3_ST_GATE_ADALN, s);
-    gate_then_adaln(x, y, g1, sh2, sc2, n2, q8, o.fused_gate_adaln != 0, rows, d, s);
+    gate_then_adaln(x, y, g1, sh2, sc2, n2, q8, o.fused_gate_adaln != 0, rows, d, s,
+                    yp.S ? &yp : nullptr);
   }
   // h = GELU(n2 W1^T + b1)
   {
@@ -218,11 +240,16 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
                        reinterpret_cast<const bf16_t *>(w.fc1_b), nullptr, H3_EPI_GELU, 0, s, sk);
     }
   }
-  // m = FC2(h)
+  // m = FC2(h) (bf16 FC2 with K split: partials reduced by the gate kernel, as above)
+  GateY mp{sk.part, 0, static_cast<int64_t>(rows) * d, reinterpret_cast<const bf16_t *>(w.fc2_b),
+           nullptr, mo};
   if (o.fc2_mode == H3_FC2_BF16) {
     ProfScope ps(H3_ST_FC2_GEMM, s);
-    launch_gemm_bf16(h, F, reinterpret_cast<const bf16_t *>(w.fc2_w), F, mo, d, rows, d, F,
-                     reinterpret_cast<const bf16_t *>(w.fc2_b), nullptr, H3_EPI_NONE, 0, s, sk);
+    mp.S = launch_gemm_bf16_partials(h, F, reinterpret_cast<const bf16_t *>(w.fc2_w), F, rows, d,
+                                     F, s, sk);
+    if (!mp.S)
+      launch_gemm_bf16(h, F, reinterpret_cast<const bf16_t *>(w.fc2_w), F, mo, d, rows, d, F,
+                       mp.b1, nullptr, H3_EPI_NONE, 0, s, sk);
   } else {
     const int group = o.fc2_mode == H3_FC2_INT8_ROW ? F : 1024;
     int8_t *hq = reinterpret_cast<int8_t *>(ws + p.hq);
@@ -241,7 +268,9 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
     ProfScope ps(H3_ST_GATE_ADALN, s);
     if (n1_next)
       gate_then_adaln(x, mo, g2, mod_next, mod_next + d, n1_next, n1_next_q,
-                      o.fused_cross_block != 0, rows, d, s);
+                      o.fused_cross_block != 0, rows, d, s, mp.S ? &mp : nullptr);
+    else if (mp.S)
+      launch_gate_adaln_part(x, mp, g2, x, nullptr, nullptr, nullptr, rows, d, s);
     else
       launch_gate_adaln(x, mo, g2, x, nullptr, nullptr, nullptr, rows, d, s);
   }

@@ -98,6 +98,12 @@ void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb
 // Tile / split-K choice of an int8 product with `group` K channels per activation scale
 // (group == K: row mode, which may split K; part_bytes is then the int32 partial buffer).
 GemmPlan plan_gemm_i8(int M, int N, int K, int group);
+// A split-K product without its reduction: the float32 partials [S][M][N] stay in the
+// scratch for a consumer that sums them (launch_gate_adaln with a GateY source).  Returns S,
+// or 0 when the plan does not split this product or the scratch is too small (nothing is
+// launched then).
+int launch_gemm_bf16_partials(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int M,
+                              int N, int K, hipStream_t s, const SplitScratch &scratch);
 void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
                     hipStream_t s, const SplitScratch &scratch = SplitScratch(),
@@ -119,6 +125,19 @@ void launch_attention_pair(const bf16_t *Q0, int64_t ldq0, const bf16_t *K0, int
 void launch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
                        const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
                        hipStream_t s, int8_t *q_out = nullptr, float *s_out = nullptr);
+// The gated branch y given as S float32 split-K partials of a [rows, d] product (part +
+// q * stride, q = 0..S-1) with its biases: y = bf16(((p_0 + p_1) + ...) + ((0 + b1) + b2)), the
+// split-K reduction's own arithmetic, optionally stored to y_out; then as launch_gate_adaln.
+struct GateY {
+  const float *part;
+  int S;
+  int64_t stride;
+  const bf16_t *b1, *b2;
+  bf16_t *y_out;
+};
+void launch_gate_adaln_part(const bf16_t *x, const GateY &ysrc, const float *gate, bf16_t *x_out,
+                            const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
+                            hipStream_t s, int8_t *q_out = nullptr, float *s_out = nullptr);
 void launch_rope_table(float2 *table, const h3_geom &geom, int n_tokens, int head_dim,
                        hipStream_t s);
 void launch_qk_norm_rope(bf16_t *qkvq, int64_t ld, int n_tokens, int d, int head_dim,

@@ -440,6 +440,18 @@ GemmPlan plan_gemm(int M, int N, int K) {
   return p;
 }
 
+int launch_gemm_bf16_partials(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int M,
+                              int N, int K, hipStream_t s, const SplitScratch &sc) {
+  const GemmPlan p = plan_gemm(M, N, K);
+  if (p.split <= 1 || !sc.part || p.part_bytes > sc.part_bytes) return 0;
+  GemmArgs a{A, lda, B, ldb, nullptr, 0, M, N, K, nullptr, nullptr, sc.part};
+  switch (p.cfg * 8 + p.split) {
+    case 1 * 8 + 2: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 2>(a, s); return 2;
+    case 1 * 8 + 4: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 4>(a, s); return 4;
+    default: return 0;
+  }
+}
+
 void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, void *C,
                       int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
                       int epilogue, int out_f32, hipStream_t s, const SplitScratch &sc) {

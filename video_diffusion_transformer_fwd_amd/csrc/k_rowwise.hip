@@ -93,12 +93,15 @@ __device__ __forceinline__ float quant_rcp(float s) { return s > 0.f ? __builtin
 // QUANT (with NORM): instead of n, the row of bf16-rounded n is quantised to int8 with one
 // scale per row by the quant4 rule above and written as q_out (int8) and s_out (float32), the
 // same bits as storing n and quantising it with the row quantiser.
-template <int VPL, bool GATE, bool NORM, bool QUANT>
+// YPART (with GATE): y is not read as bf16 but formed from split-K partials (GateY): the
+// partials summed in piece order plus the bias sum, rounded to bf16 -- the reduction kernel's
+// arithmetic -- and optionally stored to ysrc.y_out.
+template <int VPL, bool GATE, bool NORM, bool QUANT, bool YPART>
 __global__ __launch_bounds__(256) void gate_adaln_kernel(
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ y, const float *__restrict__ gate,
-    bf16_t *x_out, const float *__restrict__ shift, const float *__restrict__ scale,
-    bf16_t *__restrict__ n_out, int8_t *__restrict__ q_out, float *__restrict__ s_out, int rows,
-    int d) {
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ y, GateY ysrc,
+    const float *__restrict__ gate, bf16_t *x_out, const float *__restrict__ shift,
+    const float *__restrict__ scale, bf16_t *__restrict__ n_out, int8_t *__restrict__ q_out,
+    float *__restrict__ s_out, int rows, int d) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -112,7 +115,28 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
     unpack8(xv, v[i]);
     if constexpr (GATE) {
       float yv[8], gv[8];
-      unpack8(*reinterpret_cast<const uint4 *>(y + base + e), yv);
+      if constexpr (YPART) {
+        float t[8], u[8];
+        load8f(ysrc.part + base + e, t);
+        for (int q = 1; q < ysrc.S; ++q) {
+          load8f(ysrc.part + q * ysrc.stride + base + e, u);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) t[k] = t[k] + u[k];
+        }
+        float b1[8], b2[8];
+        if (ysrc.b1) unpack8(*reinterpret_cast<const uint4 *>(ysrc.b1 + e), b1);
+        if (ysrc.b2) unpack8(*reinterpret_cast<const uint4 *>(ysrc.b2 + e), b2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float b = 0.f;
+          if (ysrc.b1) b += b1[k];
+          if (ysrc.b2) b += b2[k];
+          yv[k] = bf2f(f2bf(t[k] + b));
+        }
+        if (ysrc.y_out) *reinterpret_cast<uint4 *>(ysrc.y_out + base + e) = pack8(yv);
+      } else {
+        unpack8(*reinterpret_cast<const uint4 *>(y + base + e), yv);
+      }
       load8f(gate + e, gv);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[i][k] = bf2f(f2bf(v[i][k] + gv[k] * yv[k]));
@@ -174,17 +198,16 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
   }
 }
 
-template <bool GATE, bool NORM, bool QUANT>
+template <bool GATE, bool NORM, bool QUANT, bool YPART = false>
 void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
                          const float *shift, const float *scale, bf16_t *n_out, int8_t *q_out,
-                         float *s_out, int rows, int d, hipStream_t s) {
+                         float *s_out, int rows, int d, hipStream_t s, const GateY &ysrc = GateY{}) {
   dim3 grid((rows + 3) / 4), block(256);
   switch (d / 512) {
 #define H3_CASE(V)                                                                          \
   case V:                                                                                   \
-    gate_adaln_kernel<V, GATE, NORM, QUANT><<<grid, block, 0, s>>>(x, y, gate, x_out, shift,  \
-                                                                   scale, n_out, q_out, s_out, \
-                                                                   rows, d);                \
+    gate_adaln_kernel<V, GATE, NORM, QUANT, YPART><<<grid, block, 0, s>>>(                  \
+        x, y, ysrc, gate, x_out, shift, scale, n_out, q_out, s_out, rows, d);               \
     break;
     H3_CASE(1) H3_CASE(2) H3_CASE(3) H3_CASE(4) H3_CASE(5) H3_CASE(6) H3_CASE(8) H3_CASE(10)
     H3_CASE(12) H3_CASE(16)
@@ -541,6 +564,21 @@ void launch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16
   } else {
     dispatch_gate_adaln<false, true, false>(x, y, gate, x_out, shift, scale, n_out, nullptr, nullptr, rows, d, s);
   }
+}
+
+void launch_gate_adaln_part(const bf16_t *x, const GateY &ysrc, const float *gate, bf16_t *x_out,
+                            const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
+                            hipStream_t s, int8_t *q_out, float *s_out) {
+  if (rows <= 0) return;
+  if (q_out)
+    dispatch_gate_adaln<true, true, true, true>(x, nullptr, gate, x_out, shift, scale, nullptr, q_out,
+                                                s_out, rows, d, s, ysrc);
+  else if (n_out)
+    dispatch_gate_adaln<true, true, false, true>(x, nullptr, gate, x_out, shift, scale, n_out, nullptr,
+                                                 nullptr, rows, d, s, ysrc);
+  else
+    dispatch_gate_adaln<true, false, false, true>(x, nullptr, gate, x_out, shift, scale, nullptr,
+                                                  nullptr, nullptr, rows, d, s, ysrc);
 }
 
 void launch_rope_table(float2 *table, const h3_geom &geom, int n_tokens, int head_dim,
