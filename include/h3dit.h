@@ -197,6 +197,10 @@ typedef struct h3_run_opts {
                                * rounded to bf16 and quantised with one scale per token row
                                * (absmax / 127, the rule of h3_quant_rows); the weights need the
                                * copies of h3_quantize_linear_weights. */
+  int32_t fused_qk_rope;      /* 1: the Q/K RMSNorm + RoPE run inside the QKV product's epilogue
+                               * (P3 "the int8 path", fused epilogues; bf16 and int8 QKV) where
+                               * its tiling allows (h3_qkv_gemm); 0: separate kernel, as the
+                               * pages' `--use-slower-unfused-qkv-rope`.  Bit-identical. */
 } h3_run_opts;
 
 /* Tokens of a geometry (validates it). */
@@ -375,6 +379,26 @@ int32_t h3_rope_table(const h3_geom *geom, int32_t head_dim, void *table, void *
 int32_t h3_qk_norm_rope(void *qkvq, int64_t ld, int32_t n_tokens, int32_t d_model,
                         int32_t head_dim, const void *q_gamma, const void *k_gamma,
                         int32_t qk_norm, const void *table, void *stream);
+
+/* The block's QKV product C = [q | k | v | qc] = A W^T + bias (N = 4 d_model columns, device
+ * bf16 [M, ldc]) followed by the Q/K RMSNorm + RoPE of h3_qk_norm_rope on the q and k heads
+ * (P3 "the int8 path": the fused epilogues apply the RMS norm and RoPE of Q/K inside the QKV
+ * projection tile).  a_q8 = 0: A bf16 [M, K] (row stride lda), W bf16 [4 d_model, K] (ldw),
+ * SA and SW unused; K % 64 == 0, lda, ldw >= K and multiples of 8.  a_q8 = 1: the int8 QKV of
+ * h3_run_opts.int8_linear: A int8 [M, K] with row scales SA float [M], W int8 [4 d_model, K]
+ * with SW float [4 d_model] (h3_quantize_linear_weights), lda = ldw = K, K % 128 == 0.
+ * bias bf16 [4 d_model]; table float2 [M, head_dim / 2] from h3_rope_table for the M tokens;
+ * q_gamma, k_gamma bf16 [head_dim] (unused when qk_norm == 0); d_model % 512 == 0;
+ * ldc >= 4 d_model, ldc % 8 == 0.  fused = 1: the norm and rotation run in the product's
+ * epilogue when its tiling allows it (not for tiles that split K, nor for a C or table that is
+ * not 16-byte aligned; *fused_used, if not NULL, says which ran); fused = 0, or no fused form: the product, then h3_qk_norm_rope.  The two are
+ * bit-identical.  Errors: H3_EINVAL (NULL pointers, flags), H3_EUNSUPPORTED (head_dim not 64
+ * or 128), H3_ESHAPE (sizes, strides). */
+int32_t h3_qkv_gemm(const void *A, int64_t lda, const float *SA, const void *W, int64_t ldw,
+                    const float *SW, const void *bias, void *C, int64_t ldc, int32_t M,
+                    int32_t d_model, int32_t K, int32_t head_dim, const void *q_gamma,
+                    const void *k_gamma, int32_t qk_norm, const void *table, int32_t a_q8,
+                    int32_t fused, int32_t *fused_used, void *stream);
 
 /* ------------------------------------------------------------------------------------
  * Per-stage timing (HIP events recorded on the launch stream around every launch of the

@@ -105,27 +105,30 @@ def test_fused_and_unfused_bit_identical(name, int8_linear):
     mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
     x0 = S.normal("test.block.x2", (n, d), 1.0).to(DEV)
     outs = {}
-    for fg, fc in [(1, 1), (0, 0), (1, 0), (0, 1)]:
-        opts = B.make_opts(fused_gate_adaln=fg, fused_cross_block=fc, int8_linear=int8_linear)
+    # (gate + AdaLN-2, MLP gate + next AdaLN-1, Q/K RMSNorm + RoPE in the QKV epilogue)
+    for fg, fc, fq in [(1, 1, 1), (0, 0, 0), (1, 0, 0), (0, 1, 1)]:
+        opts = B.make_opts(fused_gate_adaln=fg, fused_cross_block=fc, int8_linear=int8_linear,
+                           fused_qk_rope=fq)
         x = x0.clone()
         n1n = torch.empty_like(x)
         ws = run_block(model, w, 0, x, mod_dev, opts, n1n, mod_dev[1])
         lay = B.h3_workspace_layout(model.handle, n, opts)
-        outs[(fg, fc)] = (bits(x), valid_bytes(n1n, n, d, int8_linear),
-                          valid_bytes(ws_view(ws, lay.n2, (n, d)), n, d, int8_linear), x.clone(), n1n.clone())
-    ref = outs[(1, 1)]
+        outs[(fg, fc, fq)] = (bits(x), valid_bytes(n1n, n, d, int8_linear),
+                              valid_bytes(ws_view(ws, lay.n2, (n, d)), n, d, int8_linear),
+                              bits(ws_view(ws, lay.qkvq, (n, 4 * d))), x.clone(), n1n.clone())
+    ref = outs[(1, 1, 1)]
     for k, v in outs.items():
-        for a, b_, what in zip(v[:3], ref[:3], ("x", "n1_next", "n2")):
+        for a, b_, what in zip(v[:4], ref[:4], ("x", "n1_next", "n2", "qkvq")):
             assert np.array_equal(a, b_), f"{name} {what} differs for fused={k}"
     # n1_next is the next block's AdaLN-1 of the output stream (dequantised in int8 mode)
-    want = dit.adaln(f64(ref[3]), mod[1][0], mod[1][1])
+    want = dit.adaln(f64(ref[4]), mod[1][0], mod[1][1])
     if int8_linear:
-        raw = ref[4].view(torch.uint8).reshape(-1)
+        raw = ref[5].view(torch.uint8).reshape(-1)
         q = raw[:n * d].view(torch.int8).reshape(n, d).cpu().numpy().astype(np.float64)
         sc = raw[n * d:n * d + 4 * n].view(torch.float32).cpu().numpy().astype(np.float64)
         assert rel_l2(q * sc[:, None], want) < 2e-2
     else:
-        assert_close(f64(ref[4]), want, rel=1e-2, elem=3e-2, what="n1_next")
+        assert_close(f64(ref[5]), want, rel=1e-2, elem=3e-2, what="n1_next")
 
 
 def test_block_deterministic_run_to_run():

@@ -180,6 +180,80 @@ def test_qk_norm_rope(geom_args, H, D, qk_norm):
     assert np.array_equal(after[:, 2 * d:], before[:, 2 * d:]), "v / qc must be untouched"
 
 
+# ------------------------------------------------------------------ QKV product + Q/K epilogue
+def _rand_table(rng, M, D):
+    ang = rng.uniform(-np.pi, np.pi, size=(M, D // 2))
+    return torch.tensor(np.stack([np.cos(ang), np.sin(ang)], -1), dtype=torch.float32, device=DEV)
+
+
+# (M, d, head_dim, int8, fused form expected): 128x128 natural, 192x192 and 384x192 with the
+# regrouped q/k-head columns (ragged rows, a partial last qc tile at d = 2048), 256x256 natural
+# with ragged rows, head_dim 64 on 192-wide tiles (natural order), and an int8 plan that
+# splits K (no fused form; a bf16 QKV product never splits: K = d gives pieces under 1024)
+QKV_CASES = [
+    (128, 512, 64, False, True), (300, 512, 64, False, True), (100, 3072, 128, False, True),
+    (768, 3072, 128, False, True), (1000, 3072, 128, False, True), (1536, 3072, 128, False, True),
+    (1536, 2048, 128, False, True), (1536, 3072, 64, False, True), (4100, 1024, 128, False, True),
+    (128, 512, 64, True, True), (768, 3072, 128, True, True), (1536, 3072, 128, True, True),
+    (1000, 2048, 128, True, True), (4100, 1024, 128, True, True), (300, 1024, 128, True, False),
+]
+
+
+@pytest.mark.parametrize("M,d,D,q8,expect_fused", QKV_CASES)
+@pytest.mark.parametrize("qk_norm", [1, 0])
+def test_qkv_gemm_fused_epilogue_bit_identical(M, d, D, q8, expect_fused, qk_norm):
+    if not qk_norm and (M, d) not in ((128, 512), (1536, 3072)):
+        pytest.skip("qk_norm = 0 is covered on two shapes")
+    rng = np.random.default_rng(M * 7 + d + D + q8)
+    N, K = 4 * d, d
+    if q8:
+        A = torch.from_numpy(rng.integers(-127, 128, size=(M, K)).astype(np.int8)).to(DEV)
+        W = torch.from_numpy(rng.integers(-127, 128, size=(N, K)).astype(np.int8)).to(DEV)
+        SA = torch.tensor(1e-3 + rng.random(M) * 4e-3, dtype=torch.float32, device=DEV)
+        SW = torch.tensor(1e-3 + rng.random(N) * 4e-3, dtype=torch.float32, device=DEV)
+    else:
+        A, W, SA, SW = randn_bf16(rng, (M, K)), randn_bf16(rng, (N, K), 0.03), None, None
+    bias = bf16_dev(rng.standard_normal(N) * 0.3)
+    qg = bf16_dev(1 + rng.standard_normal(D) * 0.1)
+    kg = bf16_dev(1 + rng.standard_normal(D) * 0.1)
+    table = _rand_table(rng, M, D)
+    ldc = N + (8 if M == 1000 else 0)  # one padded row stride
+    # different fills, so an element one path leaves unwritten shows up
+    Cf = torch.full((M, ldc), float("nan"), dtype=torch.bfloat16, device=DEV)
+    Cu = torch.zeros((M, ldc), dtype=torch.bfloat16, device=DEV)
+    used = B.h3_qkv_gemm(A, W, bias, Cf[:, :N], D, qg, kg, qk_norm, table, SA, SW, fused=True)
+    used_u = B.h3_qkv_gemm(A, W, bias, Cu[:, :N], D, qg, kg, qk_norm, table, SA, SW, fused=False)
+    sync()
+    assert used == expect_fused and not used_u
+    assert torch.equal(Cf[:, :N].view(torch.int16), Cu[:, :N].view(torch.int16))
+    assert not torch.isnan(Cf[:, :N].float()).any()
+
+
+def test_qkv_gemm_fused_matches_oracle():
+    # 2 x 8 x 8 tokens (RoPE halved), d = 512, 8 heads of 64: product, per-head RMSNorm, RoPE
+    f, gh, gw, sc = 2, 8, 8, 0.5
+    geom = B.make_geom(f, gh, gw, sc, 0)
+    M, d, D, H = 128, 512, 64, 8
+    rng = np.random.default_rng(5)
+    A, W = randn_bf16(rng, (M, d)), randn_bf16(rng, (4 * d, d), 0.03)
+    bias = bf16_dev(rng.standard_normal(4 * d) * 0.3)
+    qg = bf16_dev(1 + rng.standard_normal(D) * 0.1)
+    kg = bf16_dev(1 + rng.standard_normal(D) * 0.1)
+    table = torch.empty((M, D // 2, 2), dtype=torch.float32, device=DEV)
+    B.h3_rope_table(geom, D, table)
+    C_out = torch.empty((M, 4 * d), dtype=torch.bfloat16, device=DEV)
+    assert B.h3_qkv_gemm(A, W, bias, C_out, D, qg, kg, 1, table)
+    sync()
+    lin = dit.linear(f64(A), f64(W), f64(bias))
+    coords = dit.rope_coords(f, gh, gw, sc)
+    q = dit.rope_apply(dit.rms_norm_heads(lin[:, :d].reshape(M, H, D), f64(qg)), coords).reshape(M, d)
+    k = dit.rope_apply(dit.rms_norm_heads(lin[:, d:2 * d].reshape(M, H, D), f64(kg)), coords).reshape(M, d)
+    got = f64(C_out)
+    assert_close(got[:, :d], q, rel=8e-3, elem=3e-2, what="q")
+    assert_close(got[:, d:2 * d], k, rel=8e-3, elem=3e-2, what="k")
+    assert_close(got[:, 2 * d:], lin[:, 2 * d:], rel=8e-3, elem=3e-2, what="v | qc")
+
+
 # ------------------------------------------------------------------ token pairing
 @pytest.mark.parametrize("f,gh,gw,d", [(6, 16, 16, 3072), (1, 15, 27, 512), (2, 3, 5, 1024)])
 def test_token_merge_restore_exact(f, gh, gw, d):

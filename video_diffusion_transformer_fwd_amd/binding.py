@@ -54,7 +54,7 @@ class h3_geom(C.Structure):
 class h3_run_opts(C.Structure):
     _fields_ = [(n, C.c_int32) for n in
                 ("fc2_mode", "fused_gate_adaln", "fused_cross_block", "qk_norm", "token_reduction",
-                 "int8_linear")]
+                 "int8_linear", "fused_qk_rope")]
 
 
 class h3_ws_layout(C.Structure):
@@ -104,6 +104,8 @@ SIGNATURES = {
     "h3_gate_adaln_quant": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
     "h3_rope_table": (_I32, [C.POINTER(h3_geom), _I32, _VP, _VP]),
     "h3_qk_norm_rope": (_I32, [_VP, _I64, _I32, _I32, _I32, _VP, _VP, _I32, _VP, _VP]),
+    "h3_qkv_gemm": (_I32, [_VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32,
+                           _VP, _VP, _I32, _VP, _I32, _I32, _PI32, _VP]),
     "h3_profile_begin": (_I32, [C.c_uint32, _I32]),
     "h3_profile_end": (_I32, [C.POINTER(C.c_double), _PI32]),
 }
@@ -213,10 +215,10 @@ def h3_geom_tokens(geom: h3_geom) -> int:
 
 
 def make_opts(fc2_mode="bf16", fused_gate_adaln=True, fused_cross_block=True, qk_norm=True,
-              token_reduction=False, int8_linear=False):
+              token_reduction=False, int8_linear=False, fused_qk_rope=True):
     return h3_run_opts(FC2_MODES[fc2_mode] if isinstance(fc2_mode, str) else fc2_mode,
                        int(fused_gate_adaln), int(fused_cross_block), int(qk_norm),
-                       int(token_reduction), int(int8_linear))
+                       int(token_reduction), int(int8_linear), int(fused_qk_rope))
 
 
 # ------------------------------------------------------------------ model
@@ -320,6 +322,22 @@ def h3_gemm_i8(QA, SA, QW, SW, bias, C_out, group, epilogue=0, stream=None):
     N = QW.shape[0]
     _check(lib().h3_gemm_i8(ptr(QA), ptr(SA), ptr(QW), ptr(SW), ptr(bias), ptr(C_out),
                             C_out.stride(0), M, N, K, group, epilogue, stream_handle(stream)))
+
+
+def h3_qkv_gemm(A, W, bias, C_out, head_dim, q_gamma, k_gamma, qk_norm, table, SA=None, SW=None,
+                fused=True, stream=None) -> bool:
+    """QKV product + Q/K RMSNorm + RoPE; int8 when A is int8 (SA, SW the scales).  Returns
+    whether the fused epilogue ran."""
+    import torch
+    M, K = A.shape
+    d = W.shape[0] // 4
+    a_q8 = int(A.dtype == torch.int8)
+    used = C.c_int32()
+    _check(lib().h3_qkv_gemm(ptr(A), A.stride(0), ptr(SA), ptr(W), W.stride(0), ptr(SW), ptr(bias),
+                             ptr(C_out), C_out.stride(0), M, d, K, head_dim, ptr(q_gamma),
+                             ptr(k_gamma), int(qk_norm), ptr(table), a_q8, int(fused),
+                             C.byref(used), stream_handle(stream)))
+    return bool(used.value)
 
 
 def h3_gate_adaln(x, y, gate, x_out, shift, scale, n_out, stream=None):

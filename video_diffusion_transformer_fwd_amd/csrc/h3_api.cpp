@@ -29,6 +29,7 @@ int32_t check_opts(const h3_run_opts *o) {
   if (o->fc2_mode < H3_FC2_BF16 || o->fc2_mode > H3_FC2_INT8_GROUPED)
     return fail(H3_EINVAL, "fc2_mode must be 0, 1 or 2");
   if (o->int8_linear != 0 && o->int8_linear != 1) return fail(H3_EINVAL, "int8_linear must be 0 or 1");
+  if (o->fused_qk_rope != 0 && o->fused_qk_rope != 1) return fail(H3_EINVAL, "fused_qk_rope must be 0 or 1");
   return H3_OK;
 }
 
@@ -178,26 +179,40 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
     gate_then_adaln(x, nullptr, nullptr, sh1, sc1, n1, q8, true, rows, d, s);
     n1_in = n1;
   }
-  // [q | k | v | qc] = n1 W_qkvq^T + b
+  // [q | k | v | qc] = n1 W_qkvq^T + b, then Q/K RMSNorm + 3D RoPE (in the product's
+  // epilogue when fused and the tiling allows, else in place by its own kernel)
+  const QkEpi qe{reinterpret_cast<const bf16_t *>(w.q_gamma),
+                 reinterpret_cast<const bf16_t *>(w.k_gamma), rope_table, d, o.qk_norm};
+  bool qk_done = false;
   {
     ProfScope ps(H3_ST_QKV_GEMM, s);
     if (q8) {
       const QRows r = qrows(n1_in, rows, d);
-      launch_gemm_i8(r.q, r.s, reinterpret_cast<const int8_t *>(w.qkvq_q),
-                     reinterpret_cast<const float *>(w.qkvq_s),
-                     reinterpret_cast<const bf16_t *>(w.qkvq_b), qkvq, 4 * d, rows, 4 * d, d, d,
-                     s, sk, H3_EPI_NONE);
+      if (o.fused_qk_rope)
+        qk_done = launch_gemm_i8_qkv(r.q, r.s, reinterpret_cast<const int8_t *>(w.qkvq_q),
+                                     reinterpret_cast<const float *>(w.qkvq_s),
+                                     reinterpret_cast<const bf16_t *>(w.qkvq_b), qkvq, 4 * d, rows,
+                                     d, d, D, qe, s) != 0;
+      if (!qk_done)
+        launch_gemm_i8(r.q, r.s, reinterpret_cast<const int8_t *>(w.qkvq_q),
+                       reinterpret_cast<const float *>(w.qkvq_s),
+                       reinterpret_cast<const bf16_t *>(w.qkvq_b), qkvq, 4 * d, rows, 4 * d, d, d,
+                       s, sk, H3_EPI_NONE);
     } else {
-      launch_gemm_bf16(reinterpret_cast<const bf16_t *>(n1_in), d,
-                       reinterpret_cast<const bf16_t *>(w.qkvq_w), d, qkvq, 4 * d, rows, 4 * d, d,
-                       reinterpret_cast<const bf16_t *>(w.qkvq_b), nullptr, H3_EPI_NONE, 0, s, sk);
+      if (o.fused_qk_rope)
+        qk_done = launch_gemm_bf16_qkv(reinterpret_cast<const bf16_t *>(n1_in), d,
+                                       reinterpret_cast<const bf16_t *>(w.qkvq_w), d,
+                                       reinterpret_cast<const bf16_t *>(w.qkvq_b), qkvq, 4 * d, rows,
+                                       d, d, D, qe, s) != 0;
+      if (!qk_done)
+        launch_gemm_bf16(reinterpret_cast<const bf16_t *>(n1_in), d,
+                         reinterpret_cast<const bf16_t *>(w.qkvq_w), d, qkvq, 4 * d, rows, 4 * d, d,
+                         reinterpret_cast<const bf16_t *>(w.qkvq_b), nullptr, H3_EPI_NONE, 0, s, sk);
     }
   }
-  // Q/K RMSNorm + 3D RoPE, in place
-  {
+  if (!qk_done) {
     ProfScope ps(H3_ST_QK_NORM_ROPE, s);
-    launch_qk_norm_rope(qkvq, 4 * d, rows, d, D, reinterpret_cast<const bf16_t *>(w.q_gamma),
-                        reinterpret_cast<const bf16_t *>(w.k_gamma), o.qk_norm, rope_table, s);
+    launch_qk_norm_rope(qkvq, 4 * d, rows, d, D, qe.q_gamma, qe.k_gamma, o.qk_norm, rope_table, s);
   }
   // self-attention -> attn[:, 0:d] and cross-attention -> attn[:, d:2d], in one launch
   {
@@ -783,6 +798,47 @@ int32_t h3_qk_norm_rope(void *qkvq, int64_t ld, int32_t n_tokens, int32_t d_mode
                       reinterpret_cast<const bf16_t *>(q_gamma), reinterpret_cast<const bf16_t *>(k_gamma),
                       qk_norm, reinterpret_cast<const float2 *>(table), as_stream(stream));
   return check_launch("h3_qk_norm_rope");
+}
+
+int32_t h3_qkv_gemm(const void *A, int64_t lda, const float *SA, const void *W, int64_t ldw,
+                    const float *SW, const void *bias, void *C, int64_t ldc, int32_t M,
+                    int32_t d_model, int32_t K, int32_t head_dim, const void *q_gamma,
+                    const void *k_gamma, int32_t qk_norm, const void *table, int32_t a_q8,
+                    int32_t fused, int32_t *fused_used, void *stream) {
+  if (fused_used) *fused_used = 0;
+  if (!A || !W || !bias || !C || !table || (a_q8 && (!SA || !SW)) || (qk_norm && (!q_gamma || !k_gamma)))
+    return fail(H3_EINVAL, "h3_qkv_gemm: NULL pointer");
+  if ((a_q8 != 0 && a_q8 != 1) || (fused != 0 && fused != 1) || (qk_norm != 0 && qk_norm != 1))
+    return fail(H3_EINVAL, "h3_qkv_gemm: a_q8, fused and qk_norm must be 0 or 1");
+  if (head_dim != 64 && head_dim != 128) return fail(H3_EUNSUPPORTED, "h3_qkv_gemm: head_dim must be 64 or 128");
+  if (M < 1 || d_model < 512 || d_model % 512 || d_model % head_dim)
+    return fail(H3_ESHAPE, "h3_qkv_gemm: need M >= 1 and d_model a multiple of 512 and of head_dim");
+  if (ldc < 4 * static_cast<int64_t>(d_model) || ldc % 8) return fail(H3_ESHAPE, "h3_qkv_gemm: ldc too small or not a multiple of 8");
+  if (a_q8) {
+    if (K < 128 || K % 128 || lda != K || ldw != K) return fail(H3_ESHAPE, "h3_qkv_gemm: int8 needs K % 128 == 0 and lda = ldw = K");
+  } else {
+    if (K < 64 || K % 64 || lda < K || ldw < K || lda % 8 || ldw % 8)
+      return fail(H3_ESHAPE, "h3_qkv_gemm: need K % 64 == 0, lda, ldw >= K and multiples of 8");
+  }
+  const hipStream_t s = as_stream(stream);
+  const QkEpi qe{reinterpret_cast<const bf16_t *>(q_gamma), reinterpret_cast<const bf16_t *>(k_gamma),
+                 reinterpret_cast<const float2 *>(table), d_model, qk_norm};
+  bf16_t *c = reinterpret_cast<bf16_t *>(C);
+  const bf16_t *b = reinterpret_cast<const bf16_t *>(bias);
+  int done = 0;
+  if (a_q8) {
+    const int8_t *qa = reinterpret_cast<const int8_t *>(A), *qw = reinterpret_cast<const int8_t *>(W);
+    if (fused) done = launch_gemm_i8_qkv(qa, SA, qw, SW, b, c, ldc, M, d_model, K, head_dim, qe, s);
+    if (!done) launch_gemm_i8(qa, SA, qw, SW, b, c, ldc, M, 4 * d_model, K, K, s);
+  } else {
+    const bf16_t *a = reinterpret_cast<const bf16_t *>(A), *w = reinterpret_cast<const bf16_t *>(W);
+    if (fused) done = launch_gemm_bf16_qkv(a, lda, w, ldw, b, c, ldc, M, d_model, K, head_dim, qe, s);
+    if (!done) launch_gemm_bf16(a, lda, w, ldw, c, ldc, M, 4 * d_model, K, b, nullptr, H3_EPI_NONE, 0, s);
+  }
+  if (!done)
+    launch_qk_norm_rope(c, ldc, M, d_model, head_dim, qe.q_gamma, qe.k_gamma, qk_norm, qe.table, s);
+  if (fused_used) *fused_used = done;
+  return check_launch("h3_qkv_gemm");
 }
 
 }  // extern "C"

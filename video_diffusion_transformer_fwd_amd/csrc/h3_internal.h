@@ -36,6 +36,179 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+__device__ __forceinline__ void unpack8(const uint4 &q, float *f) {
+  f[0] = bf_lo(q.x); f[1] = bf_hi(q.x); f[2] = bf_lo(q.y); f[3] = bf_hi(q.y);
+  f[4] = bf_lo(q.z); f[5] = bf_hi(q.z); f[6] = bf_lo(q.w); f[7] = bf_hi(q.w);
+}
+__device__ __forceinline__ uint4 pack8(const float *f) {
+  uint4 q;
+  q.x = pack_bf2(f[0], f[1]); q.y = pack_bf2(f[2], f[3]);
+  q.z = pack_bf2(f[4], f[5]); q.w = pack_bf2(f[6], f[7]);
+  return q;
+}
+
+// ---------------------------------------------------------------- Q/K RMSNorm + RoPE
+// Per head of D channels: x <- x / sqrt(mean(x^2) + 1e-6) * gamma (when norm), then each
+// interleaved pair (x_2j, x_2j+1) is rotated by the token's angle for that pair, given as
+// (cos, sin) in a [tokens, D/2] table.  A lane owns 8 consecutive channels of a head (4 pairs);
+// the D/8 lanes of a head are adjacent and start at a multiple of D/8, so a head is one DPP row
+// of 16 lanes (D = 128) or half of one (D = 64).  The standalone kernel and the QKV products'
+// fused epilogue both use these helpers, with the same lane grouping and no contraction, so
+// their results agree bit for bit.
+constexpr float kQkRmsEps = 1e-6f;
+__device__ __forceinline__ float qk_sumsq8(const float *a) {
+#pragma clang fp contract(off)
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ss = ss + a[k] * a[k];
+  return ss;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_take(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// The head's sum of the lanes' partial sums, on every lane of the head: pairs (l, l^1), then
+// (l, l^2) (quad_perm), then the two quads of each 8 lanes (row_half_mirror: l <-> 7 - l), then
+// the two halves of the 16-lane row (row_mirror: l <-> 15 - l).  Every lane adds the same two
+// values, so all lanes of the head end with the same sum.
+template <int D>
+__device__ __forceinline__ float qk_head_sumsq(float ss) {
+  static_assert(D == 64 || D == 128, "head of 8 or 16 lanes");
+  ss = ss + dpp_take<0xB1>(ss);   // quad_perm [1, 0, 3, 2]
+  ss = ss + dpp_take<0x4E>(ss);   // quad_perm [2, 3, 0, 1]
+  ss = ss + dpp_take<0x141>(ss);  // row_half_mirror
+  if constexpr (D == 128) ss = ss + dpp_take<0x140>(ss);  // row_mirror
+  return ss;
+}
+// a: the lane's 8 channels; ss: the head's sum of squares; g: the 8 gains of those channels
+// (read only when norm); cs: the (cos, sin) of the lane's 4 pairs.
+template <int D>
+__device__ __forceinline__ void qk_norm_rope8(float *a, float ss, const float *g, const float2 *cs,
+                                              bool norm) {
+#pragma clang fp contract(off)
+  if (norm) {
+    const float r = 1.0f / sqrtf(ss / static_cast<float>(D) + kQkRmsEps);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = (a[k] * r) * g[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = a[2 * k], x1 = a[2 * k + 1];
+    a[2 * k] = x0 * cs[k].x - x1 * cs[k].y;
+    a[2 * k + 1] = x0 * cs[k].y + x1 * cs[k].x;
+  }
+}
+
+// Output-column order of a QKV product tile whose epilogue applies the Q/K RMSNorm + RoPE.
+// The product's columns are [q | k | v | qc], d each, heads of D channels.  When the tile
+// width BN is a multiple of D, tiles keep the natural order and the q/k columns of a tile are
+// whole heads.  For BN = 192 with D = 128 (a head does not divide the tile) the columns are
+// regrouped: tile t < 2d/128 holds q/k head t (128 columns) followed by the 64 columns
+// 2d + 64 t .. of v; the later tiles hold qc in natural order (3d + 192 (t - 2d/128) + j).  The
+// B rows of a tile are gathered in that order and the epilogue scatters each column back, so
+// the stored product is the plain one.
+struct QkEpi {
+  const bf16_t *q_gamma, *k_gamma;  // [D] each
+  const float2 *table;              // [M, D/2] (cos, sin) of each token's rotation angles
+  int d;                            // model width
+  int norm;                         // 1: RMSNorm before the rotation
+};
+template <int BN, int D>
+struct QkMap {
+  static constexpr bool kMixed = BN % D != 0;
+  static_assert(!kMixed || (BN == 192 && D == 128), "unsupported QKV tile / head combination");
+  // canonical column of local column j of tile tn (may be >= 4d past the end)
+  static __device__ __forceinline__ int col(int tn, int j, int d) {
+    if constexpr (kMixed) {
+      const int qk_tiles = 2 * d / 128;
+      if (tn < qk_tiles) return j < 128 ? tn * 128 + j : 2 * d + tn * 64 + (j - 128);
+      return 3 * d + (tn - qk_tiles) * 192 + j;
+    } else {
+      return tn * BN + j;
+    }
+  }
+  // leading local columns of tile tn that are q/k channels (whole heads)
+  static __device__ __forceinline__ int head_cols(int tn, int d) {
+    if constexpr (kMixed) {
+      return tn < 2 * d / 128 ? 128 : 0;
+    } else {
+      const int c = 2 * d - tn * BN;
+      return c <= 0 ? 0 : (c < BN ? c : BN);
+    }
+  }
+};
+
+// The q/k-head part of a QKV product's fused epilogue, for one thread.  The tile's accumulators
+// pass through an LDS band of WM * 32 rows (band row r = token m0 + ((r >> 5) TM + i) 32 + r % 32
+// for band i) in TM bands; the leading hc columns of a band row are hc / QKD whole heads.  Task
+// k of this thread (t = tid + k NT < items) is 8 channels of one (row, head), QKD / 8 adjacent
+// lanes per head.  fetch(i) loads the rotation (cos, sin) slices and gains of band i's tasks
+// into registers (issued ahead so their latency overlaps other work); run(i, ...) forms each
+// task's bf16 values (value(row, col, a): what the plain product would store), applies the
+// RMSNorm + rotation and stores 16 bytes.  items is a multiple of 64, so a wave is wholly in or
+// out of a task and the DPP sums see only lanes of that head.
+template <int BN, int QKD, int WM, int TM, int NT>
+struct QkHeadPass {
+  using Map = QkMap<BN, QKD>;
+  static constexpr int LPH = QKD / 8;
+  static constexpr int HI = (WM * 32 * (BN / QKD) * LPH + NT - 1) / NT;
+  const QkEpi &qk;
+  int tid, tn, m0, M, hpr, items;
+  float4 tb[HI][2];
+  uint4 gm[HI];
+
+  __device__ QkHeadPass(const QkEpi &q, int tid_, int tn_, int m0_, int M_)
+      : qk(q), tid(tid_), tn(tn_), m0(m0_), M(M_) {
+    hpr = Map::head_cols(tn, qk.d) / QKD;
+    items = WM * 32 * hpr * LPH;
+  }
+  __device__ __forceinline__ void task(int k, int i, int &row, int &col, int &m, int &n) const {
+    const int t = tid + k * NT;
+    const int item = t / LPH;
+    row = item / hpr;
+    col = (item - row * hpr) * QKD + (t % LPH) * 8;
+    m = m0 + ((row >> 5) * TM + i) * 32 + (row & 31);
+    n = Map::col(tn, col, qk.d);
+  }
+  __device__ __forceinline__ void fetch(int i) {
+#pragma unroll
+    for (int k = 0; k < HI; ++k) {
+      if (tid + k * NT < items) {
+        int row, col, m, n;
+        task(k, i, row, col, m, n);
+        const int mt = m < M ? m : M - 1;
+        const int pos = col % QKD;
+        const float4 *tp =
+            reinterpret_cast<const float4 *>(qk.table + static_cast<int64_t>(mt) * (QKD / 2) + pos / 2);
+        tb[k][0] = tp[0];
+        tb[k][1] = tp[1];
+        if (qk.norm) gm[k] = *reinterpret_cast<const uint4 *>((n < qk.d ? qk.q_gamma : qk.k_gamma) + pos);
+      }
+    }
+  }
+  template <class Value>
+  __device__ __forceinline__ void run(int i, Value value, bf16_t *C, int64_t ldc) {
+#pragma unroll
+    for (int k = 0; k < HI; ++k) {
+      if (tid + k * NT < items) {
+        int row, col, m, n;
+        task(k, i, row, col, m, n);
+        float a[8], g[8];
+        value(row, col, a);
+        float ss = 0.f;
+        if (qk.norm) {
+          ss = qk_head_sumsq<QKD>(qk_sumsq8(a));
+          unpack8(gm[k], g);
+        }
+        const float2 cs[4] = {make_float2(tb[k][0].x, tb[k][0].y), make_float2(tb[k][0].z, tb[k][0].w),
+                              make_float2(tb[k][1].x, tb[k][1].y), make_float2(tb[k][1].z, tb[k][1].w)};
+        qk_norm_rope8<QKD>(a, ss, g, cs, qk.norm != 0);
+        if (m < M) *reinterpret_cast<uint4 *>(C + static_cast<int64_t>(m) * ldc + n) = pack8(a);
+      }
+    }
+  }
+};
+
 // GELU(x) = x Phi(x) with Phi the standard normal CDF.  erfc by Abramowitz & Stegun, Handbook
 // of Mathematical Functions, formula 7.1.26: erfc(z) = (a1 t + ... + a5 t^5) exp(-z^2) with
 // t = 1 / (1 + p z), z >= 0, absolute error <= 1.5e-7.  With z = |x| / sqrt 2 and
@@ -108,6 +281,16 @@ void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const f
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
                     hipStream_t s, const SplitScratch &scratch = SplitScratch(),
                     int epilogue = H3_EPI_NONE);
+// The QKV product [q | k | v | qc] = A W^T + bias (N = 4d) with the Q/K RMSNorm + RoPE of
+// launch_qk_norm_rope applied in the product's epilogue (QkEpi; table rows are the M tokens),
+// bit-identical to the product followed by that kernel.  Returns 1 when launched, 0 when the
+// product's plan has no fused form (split K, head_dim not 64 or 128): nothing is launched then.
+int launch_gemm_bf16_qkv(const bf16_t *A, int64_t lda, const bf16_t *W, int64_t ldw,
+                         const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int d, int K,
+                         int head_dim, const QkEpi &qk, hipStream_t s);
+int launch_gemm_i8_qkv(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
+                       const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int d, int K,
+                       int head_dim, const QkEpi &qk, hipStream_t s);
 void launch_attention(const bf16_t *Q, int64_t ldq, const bf16_t *K, int64_t ldk,
                       const bf16_t *V, int64_t ldv, bf16_t *O, int64_t ldo, int nq, int nk,
                       int heads, int head_dim, hipStream_t s);

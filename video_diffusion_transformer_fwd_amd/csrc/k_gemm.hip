@@ -96,10 +96,14 @@ struct GemmArgs {
   int M, N, K;
   const bf16_t *bias, *bias2;
   float *part;  // split-K partials [S][M][N]
+  QkEpi qk;     // QKV product with the Q/K RMSNorm + RoPE epilogue (QKD > 0)
 };
 
-template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT>
+// QKD > 0: the QKV product with heads of QKD channels; columns follow QkMap<BN, QKD> and the
+// epilogue applies the Q/K RMSNorm + RoPE to the q/k heads (bias, no GELU, bf16, unsplit).
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
+  static_assert(QKD == 0 || (EPI == H3_EPI_NONE && !OUT_F32 && SPLIT == 1), "QKV epilogue form");
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -125,6 +129,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int kc = g.K / SPLIT, kbeg = split * kc;
+  // output column of local tile column j
+  auto ncol = [&](int j) {
+    if constexpr (QKD > 0)
+      return QkMap<BN, QKD>::col(tn, j, g.qk.d);
+    else
+      return n0 + j;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -151,7 +162,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
         r = r < g.M ? r : g.M - 1;
         goff[i] = static_cast<uint32_t>((static_cast<int64_t>(r) * g.lda + kbeg + chunk * 8) * 2);
       } else {
-        int r = n0 + R - BM;
+        int r = ncol(R - BM);
         r = r < g.N ? r : g.N - 1;
         goff[i] = static_cast<uint32_t>((static_cast<int64_t>(r) * g.ldb + kbeg + chunk * 8) * 2);
       }
@@ -272,7 +283,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   float *sbias = band + Cfg::EPI_BAND;
   __syncthreads();
   for (int c = tid; c < BN; c += NT) {
-    const int n = n0 + c;
+    const int n = ncol(c);
     float bs = 0.f;
     if (n < g.N) {
       if (g.bias) bs += bf2f(g.bias[n]);
@@ -285,6 +296,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
                    (reinterpret_cast<uintptr_t>(g.C) % (OUT_F32 ? 16 : 8) == 0);
   constexpr int CHUNKS_PER_ROW = BN / 4;
   constexpr int BAND_CHUNKS = WM * 32 * CHUNKS_PER_ROW;
+  if constexpr (QKD > 0) {
+    // QKV: the leading hc columns of the tile are whole q/k heads, normalised and rotated by
+    // QkHeadPass (the bf16 value the plain product stores, then RMSNorm + RoPE); the remaining
+    // columns get the plain bias epilogue.  Each band's rotation slices and gains are fetched
+    // while the previous band's plain columns are stored.  The host guarantees 8 | ldc, a
+    // 16-byte aligned C and table.
+    using Map = QkMap<BN, QKD>;
+    QkHeadPass<BN, QKD, WM, TM, NT> hp(g.qk, tid, tn, m0, g.M);
+    const int hc = hp.hpr * QKD;
+    const int pc4 = (BN - hc) / 4;  // 4-column chunks per row after the heads
+    bf16_t *C = reinterpret_cast<bf16_t *>(g.C);
+    hp.fetch(0);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i > 0) __syncthreads();
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4 *>(band + (wm * 32 + m_l) * LD + (wn * TN + j) * 32 + q * 8 + n_l) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      __syncthreads();
+      hp.run(i, [&](int row, int col, float *a) {
+        const float4 *bp = reinterpret_cast<const float4 *>(band + row * LD + col);
+        const float4 *sp = reinterpret_cast<const float4 *>(sbias + col);
+        const float4 v0 = bp[0], v1 = bp[1], b0 = sp[0], b1 = sp[1];
+        const float v[8] = {v0.x + b0.x, v0.y + b0.y, v0.z + b0.z, v0.w + b0.w,
+                            v1.x + b1.x, v1.y + b1.y, v1.z + b1.z, v1.w + b1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = bf2f(f2bf(v[e]));
+      }, C, g.ldc);
+      if (i + 1 < TM) hp.fetch(i + 1);
+      for (int c4 = tid; c4 < WM * 32 * pc4; c4 += NT) {
+        const int row = c4 / pc4, col = hc + (c4 - row * pc4) * 4;
+        const int m = m0 + ((row >> 5) * TM + i) * 32 + (row & 31);
+        const int n = Map::col(tn, col, g.qk.d);
+        if (m >= g.M || n >= g.N) continue;
+        const float4 a4 = *reinterpret_cast<const float4 *>(band + row * LD + col);
+        const float4 b4 = *reinterpret_cast<const float4 *>(sbias + col);
+        uint2 pk;
+        pk.x = pack_bf2(a4.x + b4.x, a4.y + b4.y);
+        pk.y = pack_bf2(a4.z + b4.z, a4.w + b4.w);
+        *reinterpret_cast<uint2 *>(C + static_cast<int64_t>(m) * g.ldc + n) = pk;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (i > 0) __syncthreads();  // previous band fully read
@@ -330,11 +388,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT>
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0>
 void run_gemm(const GemmArgs &a, hipStream_t s) {
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT>;
+  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD>;
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -467,6 +525,35 @@ void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb
     gemm_dispatch<H3_EPI_GELU, 0>(p, a, s);
   else
     gemm_dispatch<H3_EPI_NONE, 0>(p, a, s);
+}
+
+namespace {
+template <int QKD>
+void qkv_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
+  switch (p.cfg) {
+    case 4: run_gemm<384, 192, 4, 2, 2, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
+    case 2: run_gemm<256, 256, 2, 4, 2, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
+    case 1: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
+    case 3: run_gemm<128, 256, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
+    default: run_gemm<128, 128, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
+  }
+}
+}  // namespace
+
+int launch_gemm_bf16_qkv(const bf16_t *A, int64_t lda, const bf16_t *W, int64_t ldw,
+                         const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int d, int K,
+                         int head_dim, const QkEpi &qk, hipStream_t s) {
+  const GemmPlan p = plan_gemm(M, 4 * d, K);
+  if (p.split > 1 || (head_dim != 64 && head_dim != 128) || d % 128 || ldc % 8 ||
+      reinterpret_cast<uintptr_t>(C) % 16 ||
+      reinterpret_cast<uintptr_t>(qk.table) % 16)
+    return 0;
+  GemmArgs a{A, lda, W, ldw, C, ldc, M, 4 * d, K, bias, nullptr, nullptr, qk};
+  if (head_dim == 128)
+    qkv_dispatch<128>(p, a, s);
+  else
+    qkv_dispatch<64>(p, a, s);
+  return 1;
 }
 
 }  // namespace h3

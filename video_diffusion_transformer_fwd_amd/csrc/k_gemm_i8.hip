@@ -74,12 +74,16 @@ struct GemmI8Args {
   int64_t ldc;
   int M, N, K, group;
   int32_t *part;  // split-K int32 partials [S][M][N] (row mode)
+  QkEpi qk;       // QKV product with the Q/K RMSNorm + RoPE epilogue (QKD > 0)
 };
 
-template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT, int EPI>
+// QKD > 0: the QKV product with heads of QKD channels, columns in QkMap<BN, QKD> order and the
+// Q/K RMSNorm + RoPE applied to the q/k heads in the epilogue (row mode, unsplit, no GELU).
+template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT, int EPI, int QKD = 0>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
 #pragma clang fp contract(off)
   static_assert(!(GROUPED && SPLIT > 1), "the grouped float fold is never split");
+  static_assert(QKD == 0 || (!GROUPED && SPLIT == 1 && EPI == H3_EPI_NONE), "QKV epilogue form");
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
   extern __shared__ __align__(16) unsigned char smem8[];
@@ -105,6 +109,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int kc = g.K / SPLIT, kbeg = split * kc;
+  // output column of local tile column j
+  auto ncol = [&](int j) {
+    if constexpr (QKD > 0)
+      return QkMap<BN, QKD>::col(tn, j, g.qk.d);
+    else
+      return n0 + j;
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
         r = r < g.M ? r : g.M - 1;
         goff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * g.K + kbeg + chunk * 16);
       } else {
-        int r = n0 + R - BM;
+        int r = ncol(R - BM);
         r = r < g.N ? r : g.N - 1;
         goff[i] = static_cast<uint32_t>(static_cast<int64_t>(r) * g.K + kbeg + chunk * 16);
       }
@@ -284,13 +295,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
   float *sbias = ssw + BN;
   __syncthreads();
   for (int c = tid; c < BN; c += NT) {
-    const int n = n0 + c;
+    const int n = ncol(c);
     ssw[c] = n < g.N ? g.SW[n] : 0.f;
     sbias[c] = n < g.N ? bf2f(g.bias[n]) : 0.f;
   }
   const bool vec = (g.ldc % 4 == 0) && (reinterpret_cast<uintptr_t>(g.C) % 8 == 0);
   constexpr int CHUNKS_PER_ROW = BN / 4;
   constexpr int BAND_CHUNKS = WM * 32 * CHUNKS_PER_ROW;
+  // QKV: rotation slices and gains of band 0's q/k-head tasks, fetched before the band fills
+  QkHeadPass<BN, QKD ? QKD : 128, WM, TM, NT> hp(g.qk, tid, tn, m0, g.M);
+  if constexpr (QKD > 0) hp.fetch(0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (i > 0) __syncthreads();  // previous band fully read
@@ -316,6 +330,41 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
             make_float4(v[0], v[1], v[2], v[3]);
       }
     __syncthreads();
+    if constexpr (QKD > 0) {
+      // QKV: q/k heads first (QkHeadPass: the bf16 value the plain product stores, then
+      // RMSNorm + RoPE), then the other columns with the plain dequantising epilogue.  The host
+      // guarantees 8 | ldc, a 16-byte aligned C and table.
+      using Map = QkMap<BN, QKD>;
+      const int hc = hp.hpr * QKD;
+      const int pc4 = (BN - hc) / 4;
+      hp.run(i, [&](int row, int col, float *a) {
+        const float4 *bp = reinterpret_cast<const float4 *>(band + row * LD + col);
+        const float4 *wp = reinterpret_cast<const float4 *>(ssw + col);
+        const float4 *sp = reinterpret_cast<const float4 *>(sbias + col);
+        const float4 v0 = bp[0], v1 = bp[1], w0 = wp[0], w1 = wp[1], b0 = sp[0], b1 = sp[1];
+        const float t[8] = {v0.x * w0.x, v0.y * w0.y, v0.z * w0.z, v0.w * w0.w,
+                            v1.x * w1.x, v1.y * w1.y, v1.z * w1.z, v1.w * w1.w};
+        const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = bf2f(f2bf(t[e] + b[e]));
+      }, g.C, g.ldc);
+      if (i + 1 < TM) hp.fetch(i + 1);
+      for (int c4 = tid; c4 < WM * 32 * pc4; c4 += NT) {
+        const int row = c4 / pc4, col = hc + (c4 - row * pc4) * 4;
+        const int m = m0 + ((row >> 5) * TM + i) * 32 + (row & 31);
+        const int n = Map::col(tn, col, g.qk.d);
+        if (m >= g.M || n >= g.N) continue;
+        const float4 a4 = *reinterpret_cast<const float4 *>(band + row * LD + col);
+        const float4 w4 = *reinterpret_cast<const float4 *>(ssw + col);
+        const float4 b4 = *reinterpret_cast<const float4 *>(sbias + col);
+        const float t0 = a4.x * w4.x, t1 = a4.y * w4.y, t2 = a4.z * w4.z, t3 = a4.w * w4.w;
+        uint2 pk;
+        pk.x = pack_bf2(t0 + b4.x, t1 + b4.y);
+        pk.y = pack_bf2(t2 + b4.z, t3 + b4.w);
+        *reinterpret_cast<uint2 *>(g.C + static_cast<int64_t>(m) * g.ldc + n) = pk;
+      }
+      continue;
+    }
 #pragma unroll 2
     for (int c4 = tid; c4 < BAND_CHUNKS; c4 += NT) {
       const int row = c4 / CHUNKS_PER_ROW, col = (c4 - row * CHUNKS_PER_ROW) * 4;
@@ -390,11 +439,11 @@ __global__ __launch_bounds__(256) void splitk_i8_reduce_kernel(const int32_t *__
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT, int EPI>
+template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT, int EPI, int QKD = 0>
 void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS, GROUPED, SPLIT, EPI>;
+  auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS, GROUPED, SPLIT, EPI, QKD>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -460,6 +509,16 @@ void dispatch_i8(const GemmPlan &p, const GemmI8Args &a, bool grouped, hipStream
     default: run_gemm_i8<128, 128, 2, 2, 3, false, 1, EPI>(a, s); break;
   }
 }
+
+template <int QKD>
+void qkv_dispatch_i8(const GemmPlan &p, const GemmI8Args &a, hipStream_t s) {
+  switch (p.cfg) {
+    case 2: run_gemm_i8<256, 256, 2, 4, 2, false, 1, H3_EPI_NONE, QKD>(a, s); break;
+    case 4: run_gemm_i8<384, 192, 4, 2, 2, false, 1, H3_EPI_NONE, QKD>(a, s); break;
+    case 1: run_gemm_i8<192, 192, 2, 2, 3, false, 1, H3_EPI_NONE, QKD>(a, s); break;
+    default: run_gemm_i8<128, 128, 2, 2, 3, false, 1, H3_EPI_NONE, QKD>(a, s); break;
+  }
+}
 }  // namespace
 
 void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
@@ -472,6 +531,22 @@ void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const f
     dispatch_i8<H3_EPI_GELU>(p, a, group != K, s);
   else
     dispatch_i8<H3_EPI_NONE>(p, a, group != K, s);
+}
+
+int launch_gemm_i8_qkv(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
+                       const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int d, int K,
+                       int head_dim, const QkEpi &qk, hipStream_t s) {
+  const GemmPlan p = plan_gemm_i8(M, 4 * d, K, K);
+  if (p.split > 1 || (head_dim != 64 && head_dim != 128) || d % 128 || ldc % 8 ||
+      reinterpret_cast<uintptr_t>(C) % 16 ||
+      reinterpret_cast<uintptr_t>(qk.table) % 16)
+    return 0;
+  GemmI8Args a{QA, SA, QW, SW, bias, C, ldc, M, 4 * d, K, K, nullptr, qk};
+  if (head_dim == 128)
+    qkv_dispatch_i8<128>(p, a, s);
+  else
+    qkv_dispatch_i8<64>(p, a, s);
+  return 1;
 }
 
 }  // namespace h3

@@ -17,7 +17,6 @@ namespace h3 {
 namespace {
 
 constexpr float kLnEps = 1e-6f;
-constexpr float kRmsEps = 1e-6f;
 
 __device__ __forceinline__ float wave_sum(float v) {
   // xor butterfly: lanes i and i^o add the same two values (commutative), so every lane ends
@@ -32,16 +31,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ void unpack8(const uint4 &q, float *f) {
-  f[0] = bf_lo(q.x); f[1] = bf_hi(q.x); f[2] = bf_lo(q.y); f[3] = bf_hi(q.y);
-  f[4] = bf_lo(q.z); f[5] = bf_hi(q.z); f[6] = bf_lo(q.w); f[7] = bf_hi(q.w);
-}
-__device__ __forceinline__ uint4 pack8(const float *f) {
-  uint4 q;
-  q.x = pack_bf2(f[0], f[1]); q.y = pack_bf2(f[2], f[3]);
-  q.z = pack_bf2(f[4], f[5]); q.w = pack_bf2(f[6], f[7]);
-  return q;
-}
 __device__ __forceinline__ void load8f(const float *p, float *f) {
   float4 a = reinterpret_cast<const float4 *>(p)[0];
   float4 b = reinterpret_cast<const float4 *>(p)[1];
@@ -270,29 +259,17 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
   const int pos = (lane * 8) % D;  // channel offset inside the head
   for (int c = 0; c < chunks; ++c) {
     const int e = c * 512 + lane * 8;
-    float a[8];
+    float a[8], g[8];
+    float2 cs[4];
     unpack8(*reinterpret_cast<const uint4 *>(rp + e), a);
+    float ss = 0.f;
     if (qk_norm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) ss += a[k] * a[k];
-#pragma unroll
-      for (int o = 1; o < D / 8; o <<= 1) ss += __shfl_xor(ss, o);
-      const float r = 1.0f / sqrtf(ss / static_cast<float>(D) + kRmsEps);
-      const bf16_t *gp = (e < d ? q_gamma : k_gamma) + pos;
-      uint4 gq = *reinterpret_cast<const uint4 *>(gp);
-      float g[8];
-      unpack8(gq, g);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) a[k] = a[k] * r * g[k];
+      ss = qk_head_sumsq<D>(qk_sumsq8(a));
+      unpack8(*reinterpret_cast<const uint4 *>((e < d ? q_gamma : k_gamma) + pos), g);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float2 cs = tr[pos / 2 + k];
-      const float x0 = a[2 * k], x1 = a[2 * k + 1];
-      a[2 * k] = x0 * cs.x - x1 * cs.y;
-      a[2 * k + 1] = x0 * cs.y + x1 * cs.x;
-    }
+    for (int k = 0; k < 4; ++k) cs[k] = tr[pos / 2 + k];
+    qk_norm_rope8<D>(a, ss, g, cs, qk_norm != 0);
     *reinterpret_cast<uint4 *>(rp + e) = pack8(a);
   }
 }
