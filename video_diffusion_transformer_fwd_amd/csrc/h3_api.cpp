@@ -228,8 +228,10 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
            reinterpret_cast<const bf16_t *>(w.outc_b), y};
   {
     ProfScope ps(H3_ST_OUT_GEMM, s);
-    yp.S = launch_gemm_bf16_partials(attn, 2 * d, reinterpret_cast<const bf16_t *>(w.out_w), 2 * d,
-                                     rows, d, 2 * d, s, sk);
+    // (widths above 4096 keep the separate reduction: the gate kernel's registers would spill)
+    if (d <= 4096)
+      yp.S = launch_gemm_bf16_partials(attn, 2 * d, reinterpret_cast<const bf16_t *>(w.out_w),
+                                       2 * d, rows, d, 2 * d, s, sk);
     if (!yp.S)
       launch_gemm_bf16(attn, 2 * d, reinterpret_cast<const bf16_t *>(w.out_w), 2 * d, y, d, rows,
                        d, 2 * d, yp.b1, yp.b2, H3_EPI_NONE, 0, s, sk);
@@ -260,8 +262,9 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
            nullptr, mo};
   if (o.fc2_mode == H3_FC2_BF16) {
     ProfScope ps(H3_ST_FC2_GEMM, s);
-    mp.S = launch_gemm_bf16_partials(h, F, reinterpret_cast<const bf16_t *>(w.fc2_w), F, rows, d,
-                                     F, s, sk);
+    if (d <= 4096)
+      mp.S = launch_gemm_bf16_partials(h, F, reinterpret_cast<const bf16_t *>(w.fc2_w), F, rows, d,
+                                       F, s, sk);
     if (!mp.S)
       launch_gemm_bf16(h, F, reinterpret_cast<const bf16_t *>(w.fc2_w), F, mo, d, rows, d, F,
                        mp.b1, nullptr, H3_EPI_NONE, 0, s, sk);

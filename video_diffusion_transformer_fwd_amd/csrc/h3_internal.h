@@ -309,8 +309,9 @@ void launch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16
                        const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
                        hipStream_t s, int8_t *q_out = nullptr, float *s_out = nullptr);
 // The gated branch y given as S float32 split-K partials of a [rows, d] product (part +
-// q * stride, q = 0..S-1) with its biases: y = bf16(((p_0 + p_1) + ...) + ((0 + b1) + b2)), the
-// split-K reduction's own arithmetic, optionally stored to y_out; then as launch_gate_adaln.
+// q * stride, q = 0..S-1, S = 2 or 4) with its biases (b1 required, b2 optional): y =
+// bf16(((p_0 + p_1) + ...) + ((0 + b1) + b2)), the split-K reduction's own arithmetic,
+// optionally stored to y_out; then as launch_gate_adaln.
 struct GateY {
   const float *part;
   int S;

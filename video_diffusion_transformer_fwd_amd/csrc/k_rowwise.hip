@@ -10,6 +10,8 @@
 
 #include <cmath>
 
+#include <type_traits>
+
 #include "h3_internal.h"
 
 namespace h3 {
@@ -82,10 +84,13 @@ __device__ __forceinline__ float quant_rcp(float s) { return s > 0.f ? __builtin
 // QUANT (with NORM): instead of n, the row of bf16-rounded n is quantised to int8 with one
 // scale per row by the quant4 rule above and written as q_out (int8) and s_out (float32), the
 // same bits as storing n and quantising it with the row quantiser.
-// YPART (with GATE): y is not read as bf16 but formed from split-K partials (GateY): the
+// YS > 0 (with GATE): y is not read as bf16 but formed from YS split-K partials (GateY): the
 // partials summed in piece order plus the bias sum, rounded to bf16 -- the reduction kernel's
-// arithmetic -- and optionally stored to ysrc.y_out.
-template <int VPL, bool GATE, bool NORM, bool QUANT, bool YPART>
+// arithmetic -- and optionally stored to ysrc.y_out.  An absent second bias adds +0, which
+// leaves every sum's bits unchanged, so the bias loads need no branch.
+// All loads of a chunk are issued before its values are used (no branches, no runtime loops),
+// and the AdaLN shift / scale are loaded before the row reductions.
+template <int VPL, bool GATE, bool NORM, bool QUANT, int YS>
 __global__ __launch_bounds__(256) void gate_adaln_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ y, GateY ysrc,
     const float *__restrict__ gate, bf16_t *x_out, const float *__restrict__ shift,
@@ -97,6 +102,10 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
   if (row >= rows) return;
   const size_t base = static_cast<size_t>(row) * d;
   float v[VPL][8];
+  // the branch values y (stored afterwards when y_out is given)
+  float yk[YS > 0 ? VPL : 1][8];
+  // all loads of the row first, stores after: x_out may alias x, so a store between them would
+  // hold the later chunks' loads back
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = (i * 64 + lane) * 8;
@@ -104,31 +113,50 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
     unpack8(xv, v[i]);
     if constexpr (GATE) {
       float yv[8], gv[8];
-      if constexpr (YPART) {
-        float t[8], u[8];
+      if constexpr (YS > 0) {
+        float t[8], u[8], b1[8], b2[8];
         load8f(ysrc.part + base + e, t);
-        for (int q = 1; q < ysrc.S; ++q) {
+        unpack8(*reinterpret_cast<const uint4 *>(ysrc.b1 + e), b1);
+        unpack8(*reinterpret_cast<const uint4 *>((ysrc.b2 ? ysrc.b2 : ysrc.b1) + e), b2);
+#pragma unroll
+        for (int q = 1; q < YS; ++q) {
           load8f(ysrc.part + q * ysrc.stride + base + e, u);
 #pragma unroll
           for (int k = 0; k < 8; ++k) t[k] = t[k] + u[k];
         }
-        float b1[8], b2[8];
-        if (ysrc.b1) unpack8(*reinterpret_cast<const uint4 *>(ysrc.b1 + e), b1);
-        if (ysrc.b2) unpack8(*reinterpret_cast<const uint4 *>(ysrc.b2 + e), b2);
+        const bool has_b2 = ysrc.b2 != nullptr;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           float b = 0.f;
-          if (ysrc.b1) b += b1[k];
-          if (ysrc.b2) b += b2[k];
+          b += b1[k];
+          b += has_b2 ? b2[k] : 0.f;
           yv[k] = bf2f(f2bf(t[k] + b));
+          yk[i][k] = yv[k];
         }
-        if (ysrc.y_out) *reinterpret_cast<uint4 *>(ysrc.y_out + base + e) = pack8(yv);
       } else {
         unpack8(*reinterpret_cast<const uint4 *>(y + base + e), yv);
       }
       load8f(gate + e, gv);
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[i][k] = bf2f(f2bf(v[i][k] + gv[k] * yv[k]));
+    }
+  }
+  float shv[NORM ? VPL : 1][8], scv[NORM ? VPL : 1][8];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = (i * 64 + lane) * 8;
+      load8f(shift + e, shv[i]);
+      load8f(scale + e, scv[i]);
+    }
+  }
+  if constexpr (GATE) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = (i * 64 + lane) * 8;
+      if constexpr (YS > 0) {
+        if (ysrc.y_out) *reinterpret_cast<uint4 *>(ysrc.y_out + base + e) = pack8(yk[i]);
+      }
       *reinterpret_cast<uint4 *>(x_out + base + e) = pack8(v[i]);
     }
   }
@@ -153,11 +181,9 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int e = (i * 64 + lane) * 8;
-      float sh[8], sc[8], o[8];
-      load8f(shift + e, sh);
-      load8f(scale + e, sc);
+      float o[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = ((v[i][k] - mean) * rstd) * (1.0f + sc[k]) + sh[k];
+      for (int k = 0; k < 8; ++k) o[k] = ((v[i][k] - mean) * rstd) * (1.0f + scv[i][k]) + shv[i][k];
       if constexpr (QUANT) {
         // keep the bf16-rounded output in place of the (no longer needed) input vector
 #pragma unroll
@@ -187,7 +213,7 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
   }
 }
 
-template <bool GATE, bool NORM, bool QUANT, bool YPART = false>
+template <bool GATE, bool NORM, bool QUANT, int YS = 0>
 void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
                          const float *shift, const float *scale, bf16_t *n_out, int8_t *q_out,
                          float *s_out, int rows, int d, hipStream_t s, const GateY &ysrc = GateY{}) {
@@ -195,7 +221,7 @@ void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf
   switch (d / 512) {
 #define H3_CASE(V)                                                                          \
   case V:                                                                                   \
-    gate_adaln_kernel<V, GATE, NORM, QUANT, YPART><<<grid, block, 0, s>>>(                  \
+    gate_adaln_kernel<V, GATE, NORM, QUANT, YS><<<grid, block, 0, s>>>(                     \
         x, y, ysrc, gate, x_out, shift, scale, n_out, q_out, s_out, rows, d);               \
     break;
     H3_CASE(1) H3_CASE(2) H3_CASE(3) H3_CASE(4) H3_CASE(5) H3_CASE(6) H3_CASE(8) H3_CASE(10)
@@ -547,15 +573,22 @@ void launch_gate_adaln_part(const bf16_t *x, const GateY &ysrc, const float *gat
                             const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
                             hipStream_t s, int8_t *q_out, float *s_out) {
   if (rows <= 0) return;
-  if (q_out)
-    dispatch_gate_adaln<true, true, true, true>(x, nullptr, gate, x_out, shift, scale, nullptr, q_out,
-                                                s_out, rows, d, s, ysrc);
-  else if (n_out)
-    dispatch_gate_adaln<true, true, false, true>(x, nullptr, gate, x_out, shift, scale, n_out, nullptr,
-                                                 nullptr, rows, d, s, ysrc);
-  else
-    dispatch_gate_adaln<true, false, false, true>(x, nullptr, gate, x_out, shift, scale, nullptr,
+  const auto go = [&](auto ys) {
+    constexpr int YS = decltype(ys)::value;
+    if (q_out)
+      dispatch_gate_adaln<true, true, true, YS>(x, nullptr, gate, x_out, shift, scale, nullptr,
+                                                q_out, s_out, rows, d, s, ysrc);
+    else if (n_out)
+      dispatch_gate_adaln<true, true, false, YS>(x, nullptr, gate, x_out, shift, scale, n_out,
+                                                 nullptr, nullptr, rows, d, s, ysrc);
+    else
+      dispatch_gate_adaln<true, false, false, YS>(x, nullptr, gate, x_out, shift, scale, nullptr,
                                                   nullptr, nullptr, rows, d, s, ysrc);
+  };
+  if (ysrc.S == 4)
+    go(std::integral_constant<int, 4>());
+  else
+    go(std::integral_constant<int, 2>());
 }
 
 void launch_rope_table(float2 *table, const h3_geom &geom, int n_tokens, int head_dim,
