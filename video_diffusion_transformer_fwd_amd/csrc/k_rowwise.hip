@@ -90,16 +90,43 @@ __device__ __forceinline__ float quant_rcp(float s) { return s > 0.f ? __builtin
 // leaves every sum's bits unchanged, so the bias loads need no branch.
 // All loads of a chunk are issued before its values are used (no branches, no runtime loops),
 // and the AdaLN shift / scale are loaded before the row reductions.
-template <int VPL, bool GATE, bool NORM, bool QUANT, int YS>
+// WPR waves per row: 1 (four rows per 256-thread block) or 2 (one row per 128-thread block,
+// the two waves' butterfly sums added wave 0 first through LDS); thread t of the row holds
+// the VPL 8-channel chunks at (i * 64 WPR + t) * 8.
+template <int WPR>
+__device__ __forceinline__ float row_sum(float v, float *red, int t) {
+  v = wave_sum(v);
+  if constexpr (WPR == 2) {
+    if ((t & 63) == 0) red[t >> 6] = v;
+    __syncthreads();
+    v = red[0] + red[1];
+  }
+  return v;
+}
+template <int WPR>
+__device__ __forceinline__ float row_max(float v, float *red, int t) {
+  v = wave_max(v);
+  if constexpr (WPR == 2) {
+    if ((t & 63) == 0) red[t >> 6] = v;
+    __syncthreads();
+    v = fmaxf(red[0], red[1]);
+  }
+  return v;
+}
+
+template <int VPL, int WPR, bool GATE, bool NORM, bool QUANT, int YS>
 __global__ __launch_bounds__(256) void gate_adaln_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ y, GateY ysrc,
     const float *__restrict__ gate, bf16_t *x_out, const float *__restrict__ shift,
     const float *__restrict__ scale, bf16_t *__restrict__ n_out, int8_t *__restrict__ q_out,
     float *__restrict__ s_out, int rows, int d) {
 #pragma clang fp contract(off)
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  static_assert(WPR == 1 || WPR == 2, "one or two waves per row");
+  constexpr int TPR = 64 * WPR;
+  __shared__ float red[3][2];  // (sum, sum of squares, absmax) x wave of the row
+  const int lane = threadIdx.x % TPR;  // thread of the row
+  const int row = WPR == 2 ? static_cast<int>(blockIdx.x) : blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // WPR == 2: the grid has exactly `rows` blocks
   const size_t base = static_cast<size_t>(row) * d;
   float v[VPL][8];
   // the branch values y (stored afterwards when y_out is given)
@@ -108,7 +135,7 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
   // hold the later chunks' loads back
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
-    const int e = (i * 64 + lane) * 8;
+    const int e = (i * TPR + lane) * 8;
     uint4 xv = *reinterpret_cast<const uint4 *>(x + base + e);
     unpack8(xv, v[i]);
     if constexpr (GATE) {
@@ -145,7 +172,7 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
   if constexpr (NORM) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int e = (i * 64 + lane) * 8;
+      const int e = (i * TPR + lane) * 8;
       load8f(shift + e, shv[i]);
       load8f(scale + e, scv[i]);
     }
@@ -153,7 +180,7 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
   if constexpr (GATE) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int e = (i * 64 + lane) * 8;
+      const int e = (i * TPR + lane) * 8;
       if constexpr (YS > 0) {
         if (ysrc.y_out) *reinterpret_cast<uint4 *>(ysrc.y_out + base + e) = pack8(yk[i]);
       }
@@ -166,7 +193,7 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
     for (int i = 0; i < VPL; ++i)
 #pragma unroll
       for (int k = 0; k < 8; ++k) s += v[i][k];
-    s = wave_sum(s);
+    s = row_sum<WPR>(s, red[0], lane);
     const float mean = s / static_cast<float>(d);
     float q = 0.f;
 #pragma unroll
@@ -176,11 +203,11 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
         const float c = v[i][k] - mean;
         q += c * c;
       }
-    q = wave_sum(q);
+    q = row_sum<WPR>(q, red[1], lane);
     const float rstd = 1.0f / sqrtf(q / static_cast<float>(d) + kLnEps);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int e = (i * 64 + lane) * 8;
+      const int e = (i * TPR + lane) * 8;
       float o[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = ((v[i][k] - mean) * rstd) * (1.0f + scv[i][k]) + shv[i][k];
@@ -198,11 +225,11 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
       for (int i = 0; i < VPL; ++i)
 #pragma unroll
         for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(v[i][k]));
-      m = wave_max(m);
+      m = row_max<WPR>(m, red[2], lane);
       const float sq = m / 127.0f, rq = quant_rcp(sq);
 #pragma unroll
       for (int i = 0; i < VPL; ++i) {
-        const int e = (i * 64 + lane) * 8;
+        const int e = (i * TPR + lane) * 8;
         uint2 w;
         w.x = quant4(v[i], sq, rq);
         w.y = quant4(v[i] + 4, sq, rq);
@@ -217,16 +244,24 @@ template <bool GATE, bool NORM, bool QUANT, int YS = 0>
 void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
                          const float *shift, const float *scale, bf16_t *n_out, int8_t *q_out,
                          float *s_out, int rows, int d, hipStream_t s, const GateY &ysrc = GateY{}) {
-  dim3 grid((rows + 3) / 4), block(256);
+  // an even number of 512-channel chunks: two waves per row (twice the waves in flight for
+  // the same rows); otherwise one
+  const dim3 grid1((rows + 3) / 4), block1(256), grid2(rows), block2(128);
   switch (d / 512) {
-#define H3_CASE(V)                                                                          \
+#define H3_CASE1(V)                                                                         \
   case V:                                                                                   \
-    gate_adaln_kernel<V, GATE, NORM, QUANT, YS><<<grid, block, 0, s>>>(                     \
+    gate_adaln_kernel<V, 1, GATE, NORM, QUANT, YS><<<grid1, block1, 0, s>>>(                \
         x, y, ysrc, gate, x_out, shift, scale, n_out, q_out, s_out, rows, d);               \
     break;
-    H3_CASE(1) H3_CASE(2) H3_CASE(3) H3_CASE(4) H3_CASE(5) H3_CASE(6) H3_CASE(8) H3_CASE(10)
-    H3_CASE(12) H3_CASE(16)
-#undef H3_CASE
+#define H3_CASE2(V)                                                                         \
+  case 2 * V:                                                                               \
+    gate_adaln_kernel<V, 2, GATE, NORM, QUANT, YS><<<grid2, block2, 0, s>>>(                \
+        x, y, ysrc, gate, x_out, shift, scale, n_out, q_out, s_out, rows, d);               \
+    break;
+    H3_CASE1(1) H3_CASE1(3) H3_CASE1(5) H3_CASE2(1) H3_CASE2(2) H3_CASE2(3) H3_CASE2(4)
+    H3_CASE2(5) H3_CASE2(6) H3_CASE2(8)
+#undef H3_CASE1
+#undef H3_CASE2
     default: break;
   }
 }
@@ -428,20 +463,21 @@ __global__ __launch_bounds__(256) void quant_groups_kernel(const bf16_t *__restr
   if (lane == 0) S[item] = s;
 }
 
-// Row mode with K = 1024 V: 128 threads (two waves) per row, the row held in registers (V
+// Row mode with K = 8 V T: T threads (T / 64 waves) per row, the row held in registers (V
 // 16-byte vectors per thread, consecutive threads on consecutive vectors), one pass over HBM.
-template <int V>
-__global__ __launch_bounds__(128) void quant_row_kernel(const bf16_t *__restrict__ X,
-                                                        int8_t *__restrict__ Q,
-                                                        float *__restrict__ S) {
-  constexpr int K = V * 1024;
+// The row maximum is exact in any order, so the thread count does not change the result.
+template <int V, int T>
+__global__ __launch_bounds__(T) void quant_row_kernel(const bf16_t *__restrict__ X,
+                                                      int8_t *__restrict__ Q,
+                                                      float *__restrict__ S) {
+  constexpr int K = V * 8 * T, W = T / 64;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const bf16_t *xr = X + row * K;
   int8_t *qr = Q + row * K;
   uint4 raw[V];
 #pragma unroll
-  for (int v = 0; v < V; ++v) raw[v] = *reinterpret_cast<const uint4 *>(xr + (v * 128 + tid) * 8);
+  for (int v = 0; v < V; ++v) raw[v] = *reinterpret_cast<const uint4 *>(xr + (v * T + tid) * 8);
   float m = 0.f;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
@@ -451,10 +487,12 @@ __global__ __launch_bounds__(128) void quant_row_kernel(const bf16_t *__restrict
     for (int k = 0; k < 8; ++k) m = fmaxf(m, fabsf(a[k]));
   }
   m = wave_max(m);
-  __shared__ float red[2];
+  __shared__ float red[W];
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
-  m = fmaxf(red[0], red[1]);
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) m = fmaxf(m, red[w]);
   const float s = m / 127.0f, r = quant_rcp(s);
 #pragma unroll
   for (int v = 0; v < V; ++v) {
@@ -463,7 +501,7 @@ __global__ __launch_bounds__(128) void quant_row_kernel(const bf16_t *__restrict
     uint2 w;
     w.x = quant4(a, s, r);
     w.y = quant4(a + 4, s, r);
-    *reinterpret_cast<uint2 *>(qr + (v * 128 + tid) * 8) = w;
+    *reinterpret_cast<uint2 *>(qr + (v * T + tid) * 8) = w;
   }
   if (tid == 0) S[row] = s;
 }
@@ -648,9 +686,17 @@ void launch_quant_rows(const bf16_t *X, int8_t *Q, float *S, int rows, int K, in
     quant_groups_kernel<<<static_cast<int>((items + 3) / 4), 256, 0, s>>>(X, Q, S, rows, K);
     return;
   }
+  // long rows (K = 2048 n >= 8192): four waves per row, for more waves in flight
+  switch (K % 2048 == 0 && K >= 8192 ? K / 2048 : 0) {
+#define H3_QROW4(V) \
+  case V: quant_row_kernel<V, 256><<<rows, 256, 0, s>>>(X, Q, S); return;
+    H3_QROW4(4) H3_QROW4(5) H3_QROW4(6) H3_QROW4(8) H3_QROW4(10)
+#undef H3_QROW4
+    default: break;
+  }
   switch (K % 1024 == 0 ? K / 1024 : 0) {
 #define H3_QROW(V) \
-  case V: quant_row_kernel<V><<<rows, 128, 0, s>>>(X, Q, S); return;
+  case V: quant_row_kernel<V, 128><<<rows, 128, 0, s>>>(X, Q, S); return;
     H3_QROW(1) H3_QROW(2) H3_QROW(3) H3_QROW(4) H3_QROW(5) H3_QROW(6) H3_QROW(8) H3_QROW(10)
     H3_QROW(12) H3_QROW(16) H3_QROW(20)
 #undef H3_QROW
