@@ -163,16 +163,30 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     __syncthreads();
     if (t + 1 < n_tiles) load_tile(kv0 + kBlockN);
 
-    // S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks)
-    f32x16_t s[2];
+    // S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks).  The K fragments of step
+    // ks + 2 are read while step ks's two MFMAs run (a ring of three), so the LDS latency is
+    // covered instead of waited out before every MFMA.
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    {
+      constexpr int KSTEPS = D / 16;
+      const bf16_t *kp0 = Ks + l32 * Cfg::KS + 8 * g;
+      const bf16_t *kp1 = kp0 + 32 * Cfg::KS;
+      bf16x8_t kf[3][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16_t{};
-      const bf16_t *kp = Ks + (kb * 32 + l32) * Cfg::KS + 8 * g;
+      for (int ks = 0; ks < 2; ++ks) {
+        kf[ks][0] = *reinterpret_cast<const bf16x8_t *>(kp0 + ks * 16);
+        kf[ks][1] = *reinterpret_cast<const bf16x8_t *>(kp1 + ks * 16);
+      }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(kp + ks * 16);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (ks + 2 < KSTEPS) {
+          kf[(ks + 2) % 3][0] = *reinterpret_cast<const bf16x8_t *>(kp0 + (ks + 2) * 16);
+          kf[(ks + 2) % 3][1] = *reinterpret_cast<const bf16x8_t *>(kp1 + (ks + 2) * 16);
+        }
+        // keep those reads here: the scheduler would otherwise sink them next to their use
+        __builtin_amdgcn_sched_barrier(0);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % 3][0], qf[ks], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % 3][1], qf[ks], s[1], 0, 0, 0);
       }
     }
     // Online softmax with the scale folded into the exponent: p = 2^(s c - m c) with the raw
@@ -217,21 +231,32 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
       }
     l_run += psum;
 
-    // O^T += V^T P^T over 4 steps of 16 keys
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kb = st >> 1, half = st & 1;
-      bf16x8_t pb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(s[kb][8 * half + j]);
-      const int kbase = kb * 32 + 16 * half + 4 * g;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16_t *vp = Vt + (db * 32 + l32) * Cfg::VS + kbase;
+    // O^T += V^T P^T over 4 steps of 16 keys; the V^T fragments of step st + 1 are read
+    // while step st's MFMAs run
+    {
+      auto vfrag = [&](int st, int db) {
+        const bf16_t *vp = Vt + (db * 32 + l32) * Cfg::VS + (st >> 1) * 32 + 16 * (st & 1) + 4 * g;
         const bf16x4_t v0 = *reinterpret_cast<const bf16x4_t *>(vp);
         const bf16x4_t v1 = *reinterpret_cast<const bf16x4_t *>(vp + 8);
-        const bf16x8_t a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8_t vf[2][D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) vf[0][db] = vfrag(0, db);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int kb = st >> 1, half = st & 1, cur = st & 1;
+        if (st + 1 < 4) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) vf[cur ^ 1][db] = vfrag(st + 1, db);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8_t pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(s[kb][8 * half + j]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][db], pb, o[db], 0, 0, 0);
       }
     }
   }
