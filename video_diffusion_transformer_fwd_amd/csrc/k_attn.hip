@@ -116,7 +116,27 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
   const int k_row = tid / Cfg::CH, k_chunk = tid % Cfg::CH;  // K: NT/CH rows per pass
   const int v_pair = tid & 31, v_group = tid >> 5;             // V: key pair, chunk group
 
+  // with 8 waves (long sequences) interior tiles load unconditionally; otherwise, and for the
+  // last (ragged) tile, keys beyond n_k are zero-filled (measured: the 4-wave shape is faster
+  // with the single guarded form)
   auto load_tile = [&](int kv0) {
+    if (WAVES >= 8 && kv0 + kBlockN <= nk) {  // wave-uniform
+#pragma unroll
+      for (int p = 0; p < Cfg::K_PASSES; ++p) {
+        const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
+        kreg[p] = *reinterpret_cast<const uint4 *>(K + static_cast<int64_t>(r) * ldk + hoff + k_chunk * 8);
+      }
+#pragma unroll
+      for (int p = 0; p < Cfg::V_PASSES; ++p) {
+        const int chunk = v_group + p * Cfg::V_GROUPS;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int r = kv0 + 2 * v_pair + e;
+          vreg[p][e] = *reinterpret_cast<const uint4 *>(V + static_cast<int64_t>(r) * ldv + hoff + chunk * 8);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < Cfg::K_PASSES; ++p) {
       const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
