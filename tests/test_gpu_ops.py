@@ -89,6 +89,21 @@ def test_attention(nq, nk, H, D):
     assert_close(f64(O), ref.reshape(nq, H * D), rel=1e-2, elem=3e-2, what="attention")
 
 
+def test_attention_long_sequence_sampled_rows():
+    # 8192+ queries take the 8-wave workgroups, whose interior key tiles load without bounds
+    # checks; ragged query and key counts exercise the last tiles.  The oracle computes a
+    # sample of query rows (every key).
+    rng = np.random.default_rng(23)
+    nq, nk, H, D = 8200, 8263, 2, 128
+    Q, K, V = (randn_bf16(rng, (n, H * D)) for n in (nq, nk, nk))
+    O = torch.empty((nq, H * D), dtype=torch.bfloat16, device=DEV)
+    B.h3_attention(Q, K, V, O, nq, nk, H, D)
+    sync()
+    rows = np.concatenate([np.arange(0, 40), rng.integers(40, nq - 40, 48), np.arange(nq - 40, nq)])
+    ref = dit.attention(f64(Q)[rows].reshape(-1, H, D), f64(K).reshape(nk, H, D), f64(V).reshape(nk, H, D))
+    assert_close(f64(O)[rows], ref.reshape(-1, H * D), rel=1e-2, elem=3e-2, what="long attention")
+
+
 def test_attention_strided_views_of_qkvq():
     # the block's layout: q, k, v, qc as column slices of one [N, 4d] buffer, output into [N, 2d]
     rng = np.random.default_rng(11)
@@ -199,11 +214,12 @@ QKV_CASES = [
 ]
 
 
-@pytest.mark.parametrize("M,d,D,q8,expect_fused", QKV_CASES)
-@pytest.mark.parametrize("qk_norm", [1, 0])
+# every shape with the RMSNorm, and RoPE alone on the small and the 1536-token shapes
+QKV_PARAMS = [c + (1,) for c in QKV_CASES] + [c + (0,) for c in QKV_CASES if c[:2] in ((128, 512), (1536, 3072))]
+
+
+@pytest.mark.parametrize("M,d,D,q8,expect_fused,qk_norm", QKV_PARAMS)
 def test_qkv_gemm_fused_epilogue_bit_identical(M, d, D, q8, expect_fused, qk_norm):
-    if not qk_norm and (M, d) not in ((128, 512), (1536, 3072)):
-        pytest.skip("qk_norm = 0 is covered on two shapes")
     rng = np.random.default_rng(M * 7 + d + D + q8)
     N, K = 4 * d, d
     if q8:
