@@ -244,23 +244,32 @@ template <bool GATE, bool NORM, bool QUANT, int YS = 0>
 void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
                          const float *shift, const float *scale, bf16_t *n_out, int8_t *q_out,
                          float *s_out, int rows, int d, hipStream_t s, const GateY &ysrc = GateY{}) {
-  // an even number of 512-channel chunks: two waves per row (twice the waves in flight for
-  // the same rows); otherwise one
+  // few rows (under 16384) and an even number of 512-channel chunks: two waves per row, twice
+  // the waves in flight for the same rows; otherwise one (with many rows the GPU is full
+  // anyway and the second wave's LDS exchange only costs: measured at 61,488 rows)
   const dim3 grid1((rows + 3) / 4), block1(256), grid2(rows), block2(128);
-  switch (d / 512) {
+  const int v512 = d / 512;
+  if (rows >= 16384 || v512 % 2) {
+    switch (v512) {
 #define H3_CASE1(V)                                                                         \
   case V:                                                                                   \
     gate_adaln_kernel<V, 1, GATE, NORM, QUANT, YS><<<grid1, block1, 0, s>>>(                \
         x, y, ysrc, gate, x_out, shift, scale, n_out, q_out, s_out, rows, d);               \
     break;
+      H3_CASE1(1) H3_CASE1(2) H3_CASE1(3) H3_CASE1(4) H3_CASE1(5) H3_CASE1(6) H3_CASE1(8)
+      H3_CASE1(10) H3_CASE1(12) H3_CASE1(16)
+#undef H3_CASE1
+      default: break;
+    }
+    return;
+  }
+  switch (v512) {
 #define H3_CASE2(V)                                                                         \
   case 2 * V:                                                                               \
     gate_adaln_kernel<V, 2, GATE, NORM, QUANT, YS><<<grid2, block2, 0, s>>>(                \
         x, y, ysrc, gate, x_out, shift, scale, n_out, q_out, s_out, rows, d);               \
     break;
-    H3_CASE1(1) H3_CASE1(3) H3_CASE1(5) H3_CASE2(1) H3_CASE2(2) H3_CASE2(3) H3_CASE2(4)
-    H3_CASE2(5) H3_CASE2(6) H3_CASE2(8)
-#undef H3_CASE1
+    H3_CASE2(1) H3_CASE2(2) H3_CASE2(3) H3_CASE2(4) H3_CASE2(5) H3_CASE2(6) H3_CASE2(8)
 #undef H3_CASE2
     default: break;
   }
