@@ -7,8 +7,12 @@
 // scores of a single query (lane % 32) and the row max / row sum need only the partner lane
 // (lane ^ 32): one cross-lane swap instead of a 32-lane reduction.  The exponentiated scores
 // stay in registers and are fed straight back as the B operand of O^T += V^T P^T: the 16 keys of
-// each PV step are taken in the order the score accumulator already holds them, and V is
-// staged transposed in LDS so the matching A operand is two 8-byte LDS reads per lane.
+// each PV step are taken in the order the score accumulator already holds them.  V is staged
+// row-major in LDS ([key][channel], 16-byte stores straight from the loaded rows) and the
+// matching A operand (one channel, 4 + 4 keys per lane) comes from two transposing LDS reads
+// (ds_read_b64_tr_b16): within each 16-lane group, output lane j receives element j % 4 of
+// the 8-byte pieces that lanes j / 4 + {0, 4, 8, 12} point at, so pointing lane i at key
+// 4 (i / 4) + ... and channels 4 (i % 4) + ... hands every lane its channel across 4 keys.
 // Softmax is online (running max m, running sum l, float32, base-2 exponentials).
 // Keys beyond n_k are masked to -inf; query rows beyond n_q are computed and not stored.
 #include <hip/hip_runtime.h>
@@ -24,6 +28,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kBlockN = 64;   // keys per tile
@@ -37,13 +42,12 @@ struct AttnCfg {
   static constexpr int NT = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;    // queries per workgroup
   static constexpr int KS = D + 8;         // K tile row stride (elements)
-  static constexpr int VS = kBlockN + 4;   // V^T row stride: 136 bytes, so 32 rows of 8-byte reads cover 64 banks once
+  static constexpr int VS = D + 16;        // V row stride (elements): rows 288 bytes apart, so the
+                                           // four 32-byte row pieces of a transposing read use
+                                           // distinct banks
   static constexpr int CH = D / 8;         // 16-byte chunks per row
   static constexpr int K_PASSES = kBlockN * CH / NT;
-  static constexpr int V_GROUPS = NT / 32;           // chunk groups per pass (32 key pairs)
-  static constexpr int V_PASSES = CH / V_GROUPS;
-  static_assert(K_PASSES >= 1 && kBlockN * CH % NT == 0, "K tile must split over the threads");
-  static_assert(V_PASSES >= 1 && CH % V_GROUPS == 0, "V tile must split over the threads");
+  static_assert(K_PASSES >= 1 && kBlockN * CH % NT == 0, "K / V tile must split over the threads");
 };
 
 // One attention problem; a launch may carry two (blockIdx.z selects), e.g. the self- and the
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
   const int nq = second ? p1.nq : p0.nq, nk = second ? p1.nk : p0.nk;
   if (static_cast<int>(blockIdx.x) * kBlockM >= nq) return;  // this problem has fewer query tiles
   __shared__ __align__(16) bf16_t Ks[kBlockN * Cfg::KS];
-  __shared__ __align__(16) bf16_t Vt[D * Cfg::VS];
+  __shared__ __align__(16) bf16_t Vs[kBlockN * Cfg::VS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
@@ -112,9 +116,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
 
   // staging registers for the next K/V tile
   uint4 kreg[Cfg::K_PASSES];
-  uint4 vreg[Cfg::V_PASSES][2];
-  const int k_row = tid / Cfg::CH, k_chunk = tid % Cfg::CH;  // K: NT/CH rows per pass
-  const int v_pair = tid & 31, v_group = tid >> 5;             // V: key pair, chunk group
+  uint4 vreg[Cfg::K_PASSES];
+  // K and V rows alike: thread t stages 16-byte chunk t % CH of row t / CH (+ NT/CH per pass)
+  const int k_row = tid / Cfg::CH, k_chunk = tid % Cfg::CH;
 
   // with 8 waves (long sequences) interior tiles load unconditionally; otherwise, and for the
   // last (ragged) tile, keys beyond n_k are zero-filled (measured: the 4-wave shape is faster
@@ -127,13 +131,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
         kreg[p] = *reinterpret_cast<const uint4 *>(K + static_cast<int64_t>(r) * ldk + hoff + k_chunk * 8);
       }
 #pragma unroll
-      for (int p = 0; p < Cfg::V_PASSES; ++p) {
-        const int chunk = v_group + p * Cfg::V_GROUPS;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int r = kv0 + 2 * v_pair + e;
-          vreg[p][e] = *reinterpret_cast<const uint4 *>(V + static_cast<int64_t>(r) * ldv + hoff + chunk * 8);
-        }
+      for (int p = 0; p < Cfg::K_PASSES; ++p) {
+        const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
+        vreg[p] = *reinterpret_cast<const uint4 *>(V + static_cast<int64_t>(r) * ldv + hoff + k_chunk * 8);
       }
       return;
     }
@@ -144,14 +144,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
                        : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int p = 0; p < Cfg::V_PASSES; ++p) {
-      const int chunk = v_group + p * Cfg::V_GROUPS;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = kv0 + 2 * v_pair + e;
-        vreg[p][e] = r < nk ? *reinterpret_cast<const uint4 *>(V + static_cast<int64_t>(r) * ldv + hoff + chunk * 8)
-                            : make_uint4(0, 0, 0, 0);
-      }
+    for (int p = 0; p < Cfg::K_PASSES; ++p) {
+      const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
+      vreg[p] = r < nk ? *reinterpret_cast<const uint4 *>(V + static_cast<int64_t>(r) * ldv + hoff + k_chunk * 8)
+                       : make_uint4(0, 0, 0, 0);
     }
   };
   auto store_tile = [&]() {
@@ -159,19 +155,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     for (int p = 0; p < Cfg::K_PASSES; ++p)
       *reinterpret_cast<uint4 *>(Ks + (k_row + p * (Cfg::NT / Cfg::CH)) * Cfg::KS + k_chunk * 8) = kreg[p];
 #pragma unroll
-    for (int p = 0; p < Cfg::V_PASSES; ++p) {
-      const int chunk = v_group + p * Cfg::V_GROUPS;
-      const uint4 va = vreg[p][0], vb = vreg[p][1];
-      const uint32_t a[4] = {va.x, va.y, va.z, va.w}, b[4] = {vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // channels chunk*8 + 2w and +1; keys 2*v_pair (low half) and 2*v_pair+1 (high half)
-        const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);
-        const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t *>(Vt + (chunk * 8 + 2 * w) * Cfg::VS + 2 * v_pair) = lo;
-        *reinterpret_cast<uint32_t *>(Vt + (chunk * 8 + 2 * w + 1) * Cfg::VS + 2 * v_pair) = hi;
-      }
-    }
+    for (int p = 0; p < Cfg::K_PASSES; ++p)
+      *reinterpret_cast<uint4 *>(Vs + (k_row + p * (Cfg::NT / Cfg::CH)) * Cfg::VS + k_chunk * 8) = vreg[p];
   };
 
   const int n_tiles = (nk + kBlockN - 1) / kBlockN;
@@ -254,11 +239,17 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     // O^T += V^T P^T over 4 steps of 16 keys; the V^T fragments of step st + 1 are read
     // while step st's MFMAs run
     {
+      // lane l = 16 q + i points at key 4 (q / 2) + i / 4 (+ 8 for the second read) of the
+      // step and channels db*32 + 16 (q % 2) + 4 (i % 4) .. +3; it receives channel
+      // db*32 + l % 32 at keys 4 (l / 32) + 0..3 (and + 8..11) of the step
+      const int vq = lane >> 4, vi = lane & 15;
+      const int v_lane = (4 * (vq >> 1) + (vi >> 2)) * Cfg::VS + 16 * (vq & 1) + 4 * (vi & 3);
       auto vfrag = [&](int st, int db) {
-        const bf16_t *vp = Vt + (db * 32 + l32) * Cfg::VS + (st >> 1) * 32 + 16 * (st & 1) + 4 * g;
-        const bf16x4_t v0 = *reinterpret_cast<const bf16x4_t *>(vp);
-        const bf16x4_t v1 = *reinterpret_cast<const bf16x4_t *>(vp + 8);
-        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16_t *vp = Vs + ((st >> 1) * 32 + 16 * (st & 1)) * Cfg::VS + db * 32 + v_lane;
+        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + 8 * Cfg::VS));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8_t vf[2][D / 32];
 #pragma unroll
