@@ -87,15 +87,19 @@ def test_token_reduction_forward_and_loop():
     loop_parity(w, model, om, {"token_reduction": True}, 5, 2, active)
 
 
-def test_unfused_forward_bit_identical_to_fused():
-    w = TR_SMALL
+@pytest.mark.parametrize("int8_linear", [False, True])
+def test_unfused_forward_bit_identical_to_fused(int8_linear):
+    # every fusion (gate + AdaLN-2, MLP gate + next AdaLN-1, Q/K RMSNorm + RoPE in the QKV
+    # epilogue) on and off, with and without token pairing, bf16 and int8 QKV / FC1
+    w = dataclasses.replace(TR_SMALL, int8_linear=int8_linear)
     model = DiTModel(w)
     lat = model.initial_latent()
     outs = []
-    for fg, fc in [(1, 1), (0, 0)]:
+    for fused in (1, 0):
         for tr in (False, True):
-            v = model.forward(lat, 0.8, eval_index=0, opts=model.opts(fused_gate_adaln=fg, fused_cross_block=fc,
-                                                                        token_reduction=tr))
+            v = model.forward(lat, 0.8, eval_index=0,
+                              opts=model.opts(fused_gate_adaln=fused, fused_cross_block=fused,
+                                              fused_qk_rope=fused, token_reduction=tr))
             torch.cuda.synchronize()
             outs.append(bits(v))
     assert np.array_equal(outs[0], outs[2]) and np.array_equal(outs[1], outs[3])
