@@ -169,14 +169,18 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
     }
   }
   float shv[NORM ? VPL : 1][8], scv[NORM ? VPL : 1][8];
-  if constexpr (NORM) {
+  // AdaLN shift / scale: with one wave per row loaded before the reductions; with two (fewer
+  // rows) after the mean, in flight during the variance reduction, which keeps the registers
+  // low enough for three waves per SIMD
+  auto load_mod = [&]() {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int e = (i * TPR + lane) * 8;
       load8f(shift + e, shv[i]);
       load8f(scale + e, scv[i]);
     }
-  }
+  };
+  if constexpr (NORM && WPR == 1) load_mod();
   if constexpr (GATE) {
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -194,6 +198,7 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
 #pragma unroll
       for (int k = 0; k < 8; ++k) s += v[i][k];
     s = row_sum<WPR>(s, red[0], lane);
+    if constexpr (WPR == 2) load_mod();
     const float mean = s / static_cast<float>(d);
     float q = 0.f;
 #pragma unroll
