@@ -322,7 +322,8 @@ int32_t h3_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, voi
 
 /* Multi-head attention O = softmax(Q K^T / sqrt(D)) V, unmasked, float32 softmax, bf16
  * MFMA.  Q (device, bf16 [Nq, H*D] at row stride ldq), K/V ([Nk, H*D] at ldk/ldv), O
- * ([Nq, H*D] at ldo).  head_dim 64 or 128; Nq, Nk >= 1. */
+ * ([Nq, H*D] at ldo).  head_dim 64 or 128; Nq, Nk >= 1; strides multiples of 8, ldk and
+ * ldv at most 2^24 elements (H3_ESHAPE otherwise). */
 int32_t h3_attention(const void *Q, int64_t ldq, const void *K, int64_t ldk, const void *V,
                      int64_t ldv, void *O, int64_t ldo, int32_t n_q, int32_t n_k,
                      int32_t n_heads, int32_t head_dim, void *stream);

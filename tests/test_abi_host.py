@@ -166,6 +166,10 @@ def test_entry_points_reject_bad_arguments_without_launching(lib):
     assert L.h3_gemm_bf16(None, 64, 16, 64, 16, 64, 8, 8, 64, None, None, 0, 0, None) == B.H3_EINVAL
     assert L.h3_gemm_bf16(16, 64, 16, 64, 16, 64, 4, 4, 60, None, None, 0, 0, None) == B.H3_ESHAPE
     assert L.h3_attention(16, 128, 16, 128, 16, 128, 16, 128, 1, 1, 1, 96, None) == B.H3_EUNSUPPORTED
+    # key / value strides above 2^24 elements (the kernel's 32-bit in-tile source offsets)
+    big = (1 << 24) + 8
+    assert L.h3_attention(16, 128, 16, big, 16, 128, 16, 128, 1, 1, 1, 128, None) == B.H3_ESHAPE
+    assert L.h3_attention(16, 128, 16, 128, 16, big, 16, 128, 1, 1, 1, 128, None) == B.H3_ESHAPE
     assert L.h3_quant_rows(16, 16, 16, 1, 1000, 1000, None) == B.H3_ESHAPE
     assert L.h3_gemm_i8(16, 16, 16, 16, 16, 16, 8, 1, 8, 2048, 512, 0, None) == B.H3_EINVAL
     assert L.h3_gemm_i8(16, 16, 16, 16, 16, 16, 8, 1, 8, 2048, 2048, 7, None) == B.H3_EINVAL

@@ -719,6 +719,8 @@ int32_t h3_attention(const void *Q, int64_t ldq, const void *K, int64_t ldk, con
   const int64_t w = static_cast<int64_t>(n_heads) * head_dim;
   if (ldq < w || ldk < w || ldv < w || ldo < w || ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8)
     return fail(H3_ESHAPE, "h3_attention: strides too small or not multiples of 8");
+  if (ldk > (int64_t{1} << 24) || ldv > (int64_t{1} << 24))
+    return fail(H3_ESHAPE, "h3_attention: key / value strides above 2^24 elements");
   launch_attention(reinterpret_cast<const bf16_t *>(Q), ldq, reinterpret_cast<const bf16_t *>(K), ldk,
                    reinterpret_cast<const bf16_t *>(V), ldv, reinterpret_cast<bf16_t *>(O), ldo, n_q,
                    n_k, n_heads, head_dim, as_stream(stream));

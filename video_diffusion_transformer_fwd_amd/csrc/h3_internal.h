@@ -29,6 +29,18 @@ typedef __attribute__((ext_vector_type(2))) __bf16 h3_bf16x2_t;
 __device__ __forceinline__ uint32_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+// s_waitcnt immediate that waits until at most `vm` vector-memory operations are outstanding
+// (expcnt and lgkmcnt left unconstrained): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
+
+// Waits for this thread's direct-to-LDS loads down to `VM` outstanding, then meets the other
+// waves at a barrier; afterwards every wave sees the LDS bytes those loads wrote.
+template <int VM>
+__device__ __forceinline__ void lds_dma_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
+  __builtin_amdgcn_s_barrier();
+}
+
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   h3_bf16x2_t r;
   r.x = static_cast<__bf16>(lo);

@@ -1,17 +1,21 @@
 // Flash-style multi-head attention on the gfx950 matrix cores (self-attention over the video
 // tokens and cross-attention to the text context use the same kernel).
 //
-// Workgroup = 4 wave64s = 128 query rows of one head; each wave owns 32 queries.  Keys and
-// values stream through LDS in tiles of 64.  Per tile a wave computes the transposed scores
-// S^T = K Q^T (32 keys x 32 queries per v_mfma_f32_32x32x16_bf16 block), so every lane holds
-// scores of a single query (lane % 32) and the row max / row sum need only the partner lane
-// (lane ^ 32): one cross-lane swap instead of a 32-lane reduction.  The exponentiated scores
-// stay in registers and are fed straight back as the B operand of O^T += V^T P^T: the 16 keys of
-// each PV step are taken in the order the score accumulator already holds them.  V is staged
-// row-major in LDS ([key][channel], 16-byte stores straight from the loaded rows) and the
-// matching A operand (one channel, 4 + 4 keys per lane) comes from two transposing LDS reads
-// (ds_read_b64_tr_b16): within each 16-lane group, output lane j receives element j % 4 of
-// the 8-byte pieces that lanes j / 4 + {0, 4, 8, 12} point at, so pointing lane i at key
+// A workgroup holds WAVES wave64s and 32 WAVES query rows of one head; every wave owns 32
+// queries.  Keys and values stream through LDS in tiles of 64 rows, loaded straight from
+// global memory into LDS (global_load_lds_dwordx4) one tile ahead of the one in use, in two
+// stages; the tile loop is unrolled over the two stages, so every LDS read address is a
+// loop-invariant per-lane base plus an immediate offset.
+//
+// Per tile a wave computes the transposed scores S^T = K Q^T (32 keys x 32 queries per
+// v_mfma_f32_32x32x16_bf16 block), so every lane holds scores of a single query (lane % 32)
+// and the row max / row sum need only the partner lane (lane ^ 32): one cross-lane swap
+// instead of a 32-lane reduction.  The exponentiated scores stay in registers and are fed
+// straight back as the B operand of O^T += V^T P^T: the 16 keys of each PV step are taken in
+// the order the score accumulator already holds them.  The matching A operand (one channel,
+// 4 + 4 keys per lane) comes from row-major V through two transposing LDS reads
+// (ds_read_b64_tr_b16): within each 16-lane group, output lane j receives element j % 4 of the
+// 8-byte pieces that lanes j / 4 + {0, 4, 8, 12} point at, so pointing lane i at key
 // 4 (i / 4) + ... and channels 4 (i % 4) + ... hands every lane its channel across 4 keys.
 // Softmax is online (running max m, running sum l, float32, base-2 exponentials).
 // Keys beyond n_k are masked to -inf; query rows beyond n_q are computed and not stored.
@@ -27,27 +31,45 @@ namespace h3 {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kBlockN = 64;   // keys per tile
 constexpr float kLazy = 8.0f; // log2 headroom of the lazily moved softmax reference
 
-// WAVES wave64s per workgroup, 32 queries each: 4 (two workgroups per CU) for short
-// sequences, 8 (one per CU, still two waves per SIMD) for long ones, where the same K/V tile
-// then serves twice the queries and each thread stages half of it.
+// LDS layout of a staged K or V tile: 64 key rows of D bf16, unpadded (2D bytes a row, so one
+// 256-byte bank line holds 256 / 2D rows).  The 16-byte unit u of bank line `line` sits in
+// slot u ^ lds_key(line): the sixteen rows one K-fragment read touches at one unit land on
+// sixteen distinct slots, and the four rows x four units of a transposing V read on sixteen,
+// so neither read has bank conflicts.  The layout satisfies (x < 16, c' < 4)
+//   lds_off(r, 2k + g)  = lds_off(r, g) ^ 32k       lds_off(r + 32, c)  = lds_off(r, c) + 64 D
+//   lds_off(r, 4b + c') = lds_off(r, c') ^ 64b      lds_off(16s + x, c) = lds_off(x, c) + 32 s D
+// so every read address is a per-lane base combined with a compile-time constant.
+template <int D>
+__device__ __forceinline__ int lds_key(int line) {
+  if constexpr (D == 128)
+    return ((line & 3) << 2) | ((line >> 2) & 3);
+  else
+    return ((line & 1) << 2) | ((line >> 1) & 3);
+}
+// byte offset of 16-byte unit c (channels 8c .. 8c+7) of key row r within a tile
+template <int D>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  constexpr int RPL = 256 / (2 * D), UPR = D / 8;
+  const int line = r / RPL, u = (r % RPL) * UPR + c;
+  return line * 256 + ((u ^ lds_key<D>(line)) << 4);
+}
+
 template <int D, int WAVES>
 struct AttnCfg {
   static constexpr int NT = 64 * WAVES;
-  static constexpr int BM = 32 * WAVES;    // queries per workgroup
-  static constexpr int KS = D + 8;         // K tile row stride (elements)
-  static constexpr int VS = D + 16;        // V row stride (elements): rows 288 bytes apart, so the
-                                           // four 32-byte row pieces of a transposing read use
-                                           // distinct banks
-  static constexpr int CH = D / 8;         // 16-byte chunks per row
-  static constexpr int K_PASSES = kBlockN * CH / NT;
-  static_assert(K_PASSES >= 1 && kBlockN * CH % NT == 0, "K / V tile must split over the threads");
+  static constexpr int BM = 32 * WAVES;                // queries per workgroup
+  static constexpr int ROW = 2 * D;                    // bytes per staged key row
+  static constexpr int TILE = kBlockN * ROW;           // bytes per K (or V) tile
+  static constexpr int STAGE = 2 * TILE;               // K tile, then V tile
+  static constexpr int LDS = 2 * STAGE;                // two stages
+  static constexpr int LOADS = TILE / (1024 * WAVES);  // DMA instructions per wave per K or V tile
+  static_assert(LOADS >= 1 && TILE % (1024 * WAVES) == 0, "a tile must split over the waves");
 };
 
 // One attention problem; a launch may carry two (blockIdx.z selects), e.g. the self- and the
@@ -71,7 +93,7 @@ template <int D, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kernel(
     AttnProblems probs, float scale_log2) {
   using Cfg = AttnCfg<D, WAVES>;
-  constexpr int kBlockM = Cfg::BM;
+  extern __shared__ __align__(16) unsigned char smem[];
   // select the problem with scalar conditionals (indexing the argument array by blockIdx.z
   // would copy it to private memory)
   const bool second = blockIdx.z != 0;
@@ -83,13 +105,23 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
   const int64_t ldq = second ? p1.ldq : p0.ldq, ldk = second ? p1.ldk : p0.ldk;
   const int64_t ldv = second ? p1.ldv : p0.ldv, ldo = second ? p1.ldo : p0.ldo;
   const int nq = second ? p1.nq : p0.nq, nk = second ? p1.nk : p0.nk;
-  if (static_cast<int>(blockIdx.x) * kBlockM >= nq) return;  // this problem has fewer query tiles
-  __shared__ __align__(16) bf16_t Ks[kBlockN * Cfg::KS];
-  __shared__ __align__(16) bf16_t Vs[kBlockN * Cfg::VS];
+  // (query tile, head) of this workgroup.  Hardware ids go round-robin over the 8 XCDs; with
+  // four-wave workgroups (short sequences) each XCD takes a contiguous run of (tile, head)
+  // pairs instead, so the query tiles of one head share its keys and values in that XCD's L2
+  int tile = blockIdx.x, head = blockIdx.y;
+  if constexpr (WAVES == 4) {
+    const int per_plane = gridDim.x * gridDim.y;
+    if (per_plane % 8 == 0) {
+      int pid = blockIdx.x + gridDim.x * blockIdx.y;
+      pid = (pid % 8) * (per_plane / 8) + pid / 8;
+      tile = pid % gridDim.x;
+      head = pid / gridDim.x;
+    }
+  }
+  if (tile * Cfg::BM >= nq) return;  // this problem has fewer query tiles
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int head = blockIdx.y;
-  const int q_base = blockIdx.x * kBlockM + wave * 32;
+  const int q_base = tile * Cfg::BM + wave * 32;
   const int hoff = head * D;
   const int l32 = lane & 31, g = lane >> 5;
 
@@ -114,59 +146,96 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
   // first tile, whose maximum always raises it (alpha = 2^-inf = 0 clears nothing yet stored)
   float m_ref = -INFINITY, l_run = 0.f;
 
-  // staging registers for the next K/V tile
-  uint4 kreg[Cfg::K_PASSES];
-  uint4 vreg[Cfg::K_PASSES];
-  // K and V rows alike: thread t stages 16-byte chunk t % CH of row t / CH (+ NT/CH per pass)
-  const int k_row = tid / Cfg::CH, k_chunk = tid % Cfg::CH;
-
-  // with 8 waves (long sequences) interior tiles load unconditionally; otherwise, and for the
-  // last (ragged) tile, keys beyond n_k are zero-filled (measured: the 4-wave shape is faster
-  // with the single guarded form)
-  auto load_tile = [&](int kv0) {
-    if (WAVES >= 8 && kv0 + kBlockN <= nk) {  // wave-uniform
-#pragma unroll
-      for (int p = 0; p < Cfg::K_PASSES; ++p) {
-        const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
-        kreg[p] = *reinterpret_cast<const uint4 *>(K + static_cast<int64_t>(r) * ldk + hoff + k_chunk * 8);
-      }
-#pragma unroll
-      for (int p = 0; p < Cfg::K_PASSES; ++p) {
-        const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
-        vreg[p] = *reinterpret_cast<const uint4 *>(V + static_cast<int64_t>(r) * ldv + hoff + k_chunk * 8);
-      }
-      return;
-    }
-#pragma unroll
-    for (int p = 0; p < Cfg::K_PASSES; ++p) {
-      const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
-      kreg[p] = r < nk ? *reinterpret_cast<const uint4 *>(K + static_cast<int64_t>(r) * ldk + hoff + k_chunk * 8)
-                       : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int p = 0; p < Cfg::K_PASSES; ++p) {
-      const int r = kv0 + k_row + p * (Cfg::NT / Cfg::CH);
-      vreg[p] = r < nk ? *reinterpret_cast<const uint4 *>(V + static_cast<int64_t>(r) * ldv + hoff + k_chunk * 8)
-                       : make_uint4(0, 0, 0, 0);
-    }
+  // Staging: DMA instruction j of this wave fills tile bytes 1024 (j WAVES + wave) + 16 lane,
+  // i.e. bank line 4 (j WAVES + wave) + lane / 16, slot lane % 16, which holds unit
+  // (lane % 16) ^ lds_key(line) of the line; src_row_unit names that key row and unit
+  auto src_row_unit = [&](int j, int &r, int &c) {
+    constexpr int RPL = 256 / Cfg::ROW, UPR = D / 8;
+    const int line = 4 * (j * WAVES + wave) + (lane >> 4);
+    const int u = (lane & 15) ^ lds_key<D>(line);
+    r = line * RPL + u / UPR;
+    c = u % UPR;
   };
-  auto store_tile = [&]() {
+  // byte offsets of this lane's sources relative to the tile's first key row (strides are
+  // at most 2^24 elements, so they fit 32 bits)
+  uint32_t koff[Cfg::LOADS], voff[Cfg::LOADS];
 #pragma unroll
-    for (int p = 0; p < Cfg::K_PASSES; ++p)
-      *reinterpret_cast<uint4 *>(Ks + (k_row + p * (Cfg::NT / Cfg::CH)) * Cfg::KS + k_chunk * 8) = kreg[p];
-#pragma unroll
-    for (int p = 0; p < Cfg::K_PASSES; ++p)
-      *reinterpret_cast<uint4 *>(Vs + (k_row + p * (Cfg::NT / Cfg::CH)) * Cfg::VS + k_chunk * 8) = vreg[p];
-  };
-
+  for (int j = 0; j < Cfg::LOADS; ++j) {
+    int r, c;
+    src_row_unit(j, r, c);
+    koff[j] = static_cast<uint32_t>((r * ldk + hoff + 8 * c) * 2);
+    voff[j] = static_cast<uint32_t>((r * ldv + hoff + 8 * c) * 2);
+  }
   const int n_tiles = (nk + kBlockN - 1) / kBlockN;
-  load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
+  // loads tile t into stage S (S a compile-time constant: the LDS destinations are immediates)
+  auto issue = [&](int t, auto stage) {
+    constexpr int S = decltype(stage)::value;
     const int kv0 = t * kBlockN;
-    __syncthreads();  // previous tile fully consumed
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(kv0 + kBlockN);
+    const unsigned char *kb = reinterpret_cast<const unsigned char *>(K + static_cast<int64_t>(kv0) * ldk);
+    const unsigned char *vb = reinterpret_cast<const unsigned char *>(V + static_cast<int64_t>(kv0) * ldv);
+    uint32_t ko[Cfg::LOADS], vo[Cfg::LOADS];
+    if (kv0 + kBlockN <= nk) {  // workgroup-uniform
+#pragma unroll
+      for (int j = 0; j < Cfg::LOADS; ++j) ko[j] = koff[j], vo[j] = voff[j];
+    } else {
+      // last tile: rows past n_k repeat row n_k - 1 (their scores are masked, so P is 0)
+#pragma unroll
+      for (int j = 0; j < Cfg::LOADS; ++j) {
+        int r, c;
+        src_row_unit(j, r, c);
+        r = r < nk - 1 - kv0 ? r : nk - 1 - kv0;
+        ko[j] = static_cast<uint32_t>((r * ldk + hoff + 8 * c) * 2);
+        vo[j] = static_cast<uint32_t>((r * ldv + hoff + 8 * c) * 2);
+      }
+    }
+    // (source and destination as named pointers: written inline into the builtin's arguments,
+    // the host pass drops the kernel's launch stub)
+#pragma unroll
+    for (int j = 0; j < Cfg::LOADS; ++j) {
+      const unsigned char *src = kb + ko[j];
+      unsigned char *dst = smem + S * Cfg::STAGE + (j * WAVES + wave) * 1024;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < Cfg::LOADS; ++j) {
+      const unsigned char *src = vb + vo[j];
+      unsigned char *dst = smem + S * Cfg::STAGE + Cfg::TILE + (j * WAVES + wave) * 1024;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
+    }
+  };
+
+  // Loop-invariant read addresses (bytes from the stage start).  K fragment of step ks and
+  // 32-key block kb: lds_off(32 kb + l32, 2 ks + g) = ka[ks] + 64 D kb.  V^T fragment of PV
+  // step st, channel block db, first / second read: va[h][db] + 32 D st, where lane
+  // l = 16 q + i points at key 4 (q / 2) + i / 4 (+ 8) of the step and channels
+  // db*32 + 16 (q % 2) + 4 (i % 4) .. +3; it receives channel db*32 + l % 32 at keys
+  // 4 (l / 32) + 0..3 (and + 8..11) of the step
+  int ka[D / 16], va[2][D / 32];
+  {
+    const int k_base = lds_off<D>(l32, g);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) ka[ks] = k_base ^ (32 * ks);
+    const int vq = lane >> 4, vi = lane & 15;
+    const int x = 4 * (vq >> 1) + (vi >> 2);
+    const int cp = 2 * (vq & 1) + ((vi & 3) >> 1);
+    const int vb0 = Cfg::TILE + lds_off<D>(x, cp) + 8 * (vi & 1);
+    const int vb1 = Cfg::TILE + lds_off<D>(x + 8, cp) + 8 * (vi & 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      va[0][db] = vb0 ^ (64 * db);
+      va[1][db] = vb1 ^ (64 * db);
+    }
+  }
+
+  // one key tile out of stage S
+  auto tile_step = [&](int t, auto stage) {
+    constexpr int S = decltype(stage)::value;
+    const int kv0 = t * kBlockN;
+    // tile t has landed (this thread's loads, then every thread's at the barrier), and every
+    // wave is done with the other stage, which the next issue refills
+    lds_dma_barrier<0>();
+    if (t + 1 < n_tiles) issue(t + 1, std::integral_constant<int, S ^ 1>{});
+    const unsigned char *st = smem + S * Cfg::STAGE;
 
     // S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks).  The K fragments of step
     // ks + 2 are read while step ks's two MFMAs run (a ring of three), so the LDS latency is
@@ -174,19 +243,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
     {
       constexpr int KSTEPS = D / 16;
-      const bf16_t *kp0 = Ks + l32 * Cfg::KS + 8 * g;
-      const bf16_t *kp1 = kp0 + 32 * Cfg::KS;
+      auto kfrag = [&](int ks, int kb) {
+        return *reinterpret_cast<const bf16x8_t *>(st + ka[ks] + kb * 64 * D);
+      };
       bf16x8_t kf[3][2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        kf[ks][0] = *reinterpret_cast<const bf16x8_t *>(kp0 + ks * 16);
-        kf[ks][1] = *reinterpret_cast<const bf16x8_t *>(kp1 + ks * 16);
+        kf[ks][0] = kfrag(ks, 0);
+        kf[ks][1] = kfrag(ks, 1);
       }
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         if (ks + 2 < KSTEPS) {
-          kf[(ks + 2) % 3][0] = *reinterpret_cast<const bf16x8_t *>(kp0 + (ks + 2) * 16);
-          kf[(ks + 2) % 3][1] = *reinterpret_cast<const bf16x8_t *>(kp1 + (ks + 2) * 16);
+          kf[(ks + 2) % 3][0] = kfrag(ks + 2, 0);
+          kf[(ks + 2) % 3][1] = kfrag(ks + 2, 1);
         }
         // keep those reads here: the scheduler would otherwise sink them next to their use
         __builtin_amdgcn_sched_barrier(0);
@@ -236,30 +306,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
       }
     l_run += psum;
 
-    // O^T += V^T P^T over 4 steps of 16 keys; the V^T fragments of step st + 1 are read
-    // while step st's MFMAs run
+    // O^T += V^T P^T over 4 steps of 16 keys; the V^T fragments of step st + 1 are read while
+    // step st's MFMAs run
     {
-      // lane l = 16 q + i points at key 4 (q / 2) + i / 4 (+ 8 for the second read) of the
-      // step and channels db*32 + 16 (q % 2) + 4 (i % 4) .. +3; it receives channel
-      // db*32 + l % 32 at keys 4 (l / 32) + 0..3 (and + 8..11) of the step
-      const int vq = lane >> 4, vi = lane & 15;
-      const int v_lane = (4 * (vq >> 1) + (vi >> 2)) * Cfg::VS + 16 * (vq & 1) + 4 * (vi & 3);
-      auto vfrag = [&](int st, int db) {
-        const bf16_t *vp = Vs + ((st >> 1) * 32 + 16 * (st & 1)) * Cfg::VS + db * 32 + v_lane;
+      auto vfrag = [&](int step, int db) {
         typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp));
-        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(vp + 8 * Cfg::VS));
+        const unsigned char *a0 = st + va[0][db] + 32 * D * step;
+        const unsigned char *a1 = st + va[1][db] + 32 * D * step;
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a1));
         return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8_t vf[2][D / 32];
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) vf[0][db] = vfrag(0, db);
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kb = st >> 1, half = st & 1, cur = st & 1;
-        if (st + 1 < 4) {
+      for (int step = 0; step < 4; ++step) {
+        const int kb = step >> 1, half = step & 1, cur = step & 1;
+        if (step + 1 < 4) {
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) vf[cur ^ 1][db] = vfrag(st + 1, db);
+          for (int db = 0; db < D / 32; ++db) vf[cur ^ 1][db] = vfrag(step + 1, db);
         }
         __builtin_amdgcn_sched_barrier(0);
         bf16x8_t pb;
@@ -270,6 +336,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[cur][db], pb, o[db], 0, 0, 0);
       }
     }
+  };
+
+  if (n_tiles > 0) issue(0, std::integral_constant<int, 0>{});
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) tile_step(t + 1, std::integral_constant<int, 1>{});
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -290,16 +362,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
   }
 }
 
-}  // namespace
-
-namespace {
 template <int D, int WAVES>
 void launch_cfg(const AttnProblems &pr, int n_problems, int heads, float scale_log2, hipStream_t s) {
-  constexpr int BM = AttnCfg<D, WAVES>::BM;
+  using Cfg = AttnCfg<D, WAVES>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attention_kernel<D, WAVES>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+    attr_set = true;
+  }
   int tiles = 0;
-  for (int i = 0; i < n_problems; ++i) tiles = std::max(tiles, (pr.p[i].nq + BM - 1) / BM);
-  dim3 grid(tiles, heads, n_problems), block(64 * WAVES);
-  attention_kernel<D, WAVES><<<grid, block, 0, s>>>(pr, scale_log2);
+  for (int i = 0; i < n_problems; ++i) tiles = std::max(tiles, (pr.p[i].nq + Cfg::BM - 1) / Cfg::BM);
+  dim3 grid(tiles, heads, n_problems), block(Cfg::NT);
+  attention_kernel<D, WAVES><<<grid, block, Cfg::LDS, s>>>(pr, scale_log2);
 }
 
 void launch_problems(const AttnProblems &pr, int n_problems, int heads, int head_dim, hipStream_t s) {
@@ -313,6 +388,7 @@ void launch_problems(const AttnProblems &pr, int n_problems, int heads, int head
   else
     launch_cfg<64, 4>(pr, n_problems, heads, scale_log2, s);
 }
+
 }  // namespace
 
 void launch_attention(const bf16_t *Q, int64_t ldq, const bf16_t *K, int64_t ldk,

@@ -54,18 +54,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-// s_waitcnt immediate that waits until at most `vm` vector-memory operations are outstanding
-// (expcnt and lgkmcnt left unconstrained): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14.
-constexpr int waitcnt_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
-
-// Waits for this thread's direct-to-LDS loads down to `VM` outstanding, then meets the other
-// waves at a barrier; afterwards every wave sees the LDS bytes those loads wrote.
-template <int VM>
-__device__ __forceinline__ void lds_dma_barrier() {
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
-  __builtin_amdgcn_s_barrier();
-}
-
 template <int BM, int BN, int WM, int WN, int NS = 2>
 struct GemmCfg {
   static constexpr int NT = 64 * WM * WN;

@@ -39,14 +39,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-constexpr int waitcnt_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
-
-template <int VM>
-__device__ __forceinline__ void lds_dma_barrier() {
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
-  __builtin_amdgcn_s_barrier();
-}
-
 template <int BM, int BN, int WM, int WN, int NS>
 struct GemmI8Cfg {
   static constexpr int NT = 64 * WM * WN;
