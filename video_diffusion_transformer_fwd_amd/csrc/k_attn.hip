@@ -33,6 +33,11 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+// LDS pointers in the LDS address space: 32-bit arithmetic whose constant parts fold into the
+// offset fields of the DS instructions
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 constexpr int kBlockN = 64;   // keys per tile
 constexpr float kLazy = 8.0f; // log2 headroom of the lazily moved softmax reference
@@ -67,7 +72,7 @@ struct AttnCfg {
   static constexpr int ROW = 2 * D;                    // bytes per staged key row
   static constexpr int TILE = kBlockN * ROW;           // bytes per K (or V) tile
   static constexpr int STAGE = 2 * TILE;               // K tile, then V tile
-  static constexpr int LDS = 2 * STAGE;                // two stages
+  static constexpr int LDS = 2 * STAGE;                // two stages (64 KiB at D = 128)
   static constexpr int LOADS = TILE / (1024 * WAVES);  // DMA instructions per wave per K or V tile
   static_assert(LOADS >= 1 && TILE % (1024 * WAVES) == 0, "a tile must split over the waves");
 };
@@ -93,7 +98,10 @@ template <int D, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kernel(
     AttnProblems probs, float scale_log2) {
   using Cfg = AttnCfg<D, WAVES>;
-  extern __shared__ __align__(16) unsigned char smem[];
+  // static (its address known when the kernel is compiled, so constant parts of LDS addresses
+  // fold into the instructions' offsets; a dynamic array's base is a link-time symbol)
+  __shared__ __align__(16) unsigned char smem[Cfg::LDS];
+  lds_u8 *const lds = (lds_u8 *)smem;
   // select the problem with scalar conditionals (indexing the argument array by blockIdx.z
   // would copy it to private memory)
   const bool second = blockIdx.z != 0;
@@ -193,13 +201,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
 #pragma unroll
     for (int j = 0; j < Cfg::LOADS; ++j) {
       const unsigned char *src = kb + ko[j];
-      unsigned char *dst = smem + S * Cfg::STAGE + (j * WAVES + wave) * 1024;
+      lds_u8 *dst = lds + S * Cfg::STAGE + (j * WAVES + wave) * 1024;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < Cfg::LOADS; ++j) {
       const unsigned char *src = vb + vo[j];
-      unsigned char *dst = smem + S * Cfg::STAGE + Cfg::TILE + (j * WAVES + wave) * 1024;
+      lds_u8 *dst = lds + S * Cfg::STAGE + Cfg::TILE + (j * WAVES + wave) * 1024;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
     }
   };
@@ -235,7 +243,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     // wave is done with the other stage, which the next issue refills
     lds_dma_barrier<0>();
     if (t + 1 < n_tiles) issue(t + 1, std::integral_constant<int, S ^ 1>{});
-    const unsigned char *st = smem + S * Cfg::STAGE;
+    const lds_u8 *st = lds + S * Cfg::STAGE;
 
     // S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks).  The K fragments of step
     // ks + 2 are read while step ks's two MFMAs run (a ring of three), so the LDS latency is
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     {
       constexpr int KSTEPS = D / 16;
       auto kfrag = [&](int ks, int kb) {
-        return *reinterpret_cast<const bf16x8_t *>(st + ka[ks] + kb * 64 * D);
+        return *reinterpret_cast<lds_bf16x8 *>(st + ka[ks] + kb * 64 * D);
       };
       bf16x8_t kf[3][2];
 #pragma unroll
@@ -310,11 +318,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     // step st's MFMAs run
     {
       auto vfrag = [&](int step, int db) {
-        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-        const unsigned char *a0 = st + va[0][db] + 32 * D * step;
-        const unsigned char *a1 = st + va[1][db] + 32 * D * step;
-        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a0));
-        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(a1));
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(st + va[0][db] + 32 * D * step));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(st + va[1][db] + 32 * D * step));
         return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       };
       bf16x8_t vf[2][D / 32];
@@ -365,16 +370,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
 template <int D, int WAVES>
 void launch_cfg(const AttnProblems &pr, int n_problems, int heads, float scale_log2, hipStream_t s) {
   using Cfg = AttnCfg<D, WAVES>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&attention_kernel<D, WAVES>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-    attr_set = true;
-  }
   int tiles = 0;
   for (int i = 0; i < n_problems; ++i) tiles = std::max(tiles, (pr.p[i].nq + Cfg::BM - 1) / Cfg::BM);
   dim3 grid(tiles, heads, n_problems), block(Cfg::NT);
-  attention_kernel<D, WAVES><<<grid, block, Cfg::LDS, s>>>(pr, scale_log2);
+  attention_kernel<D, WAVES><<<grid, block, 0, s>>>(pr, scale_log2);
 }
 
 void launch_problems(const AttnProblems &pr, int n_problems, int heads, int head_dim, hipStream_t s) {
