@@ -381,13 +381,8 @@ void run_gemm(const GemmArgs &a, hipStream_t s) {
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(Cfg::LDS_BYTES));
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  set_dynamic_lds(reinterpret_cast<const void *>(kern), static_cast<int>(Cfg::LDS_BYTES), lds_set);
   kern<<<tiles * SPLIT, Cfg::NT, Cfg::LDS_BYTES, s>>>(a);
 }
 

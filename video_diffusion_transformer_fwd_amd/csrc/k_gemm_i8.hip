@@ -436,13 +436,8 @@ void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS, GROUPED, SPLIT, EPI, QKD>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              static_cast<int>(Cfg::LDS_BYTES));
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  set_dynamic_lds(reinterpret_cast<const void *>(kern), static_cast<int>(Cfg::LDS_BYTES), lds_set);
   kern<<<tiles * SPLIT, Cfg::NT, Cfg::LDS_BYTES, s>>>(a);
   if constexpr (SPLIT > 1) {
     const int64_t total4 = static_cast<int64_t>(a.M) * a.N / 4;
