@@ -104,6 +104,21 @@ def test_attention_long_sequence_sampled_rows():
     assert_close(f64(O)[rows], ref.reshape(-1, H * D), rel=1e-2, elem=3e-2, what="long attention")
 
 
+@pytest.mark.parametrize("nk", [1, 64, 65])
+def test_attention_long_queries_short_keys(nk):
+    # 8192 queries take the 8-wave workgroups; one key (every staged row repeats it), exactly
+    # one tile, and one tile plus a one-key tail.  Sampled query rows against the oracle.
+    rng = np.random.default_rng(31 + nk)
+    nq, H, D = 8192, 2, 128
+    Q, K, V = (randn_bf16(rng, (n, H * D)) for n in (nq, nk, nk))
+    O = torch.empty((nq, H * D), dtype=torch.bfloat16, device=DEV)
+    B.h3_attention(Q, K, V, O, nq, nk, H, D)
+    sync()
+    rows = np.concatenate([np.arange(0, 64), rng.integers(64, nq - 64, 64), np.arange(nq - 64, nq)])
+    ref = dit.attention(f64(Q)[rows].reshape(-1, H, D), f64(K).reshape(nk, H, D), f64(V).reshape(nk, H, D))
+    assert_close(f64(O)[rows], ref.reshape(-1, H * D), rel=1e-2, elem=3e-2, what=f"attention nk={nk}")
+
+
 def test_attention_strided_views_of_qkvq():
     # the block's layout: q, k, v, qc as column slices of one [N, 4d] buffer, output into [N, 2d]
     rng = np.random.default_rng(11)
