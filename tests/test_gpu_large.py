@@ -143,3 +143,77 @@ def test_forward_full_size_zero_gates_and_fused_identity():
     ref = dit.final_head(dit.patch_embed(f64(lat[rows]), g), g, fin)
     assert_close(f64(v0[rows]), ref, rel=2e-2, elem=8e-2, what="zero-gate velocity rows")
     model.close()
+
+
+def test_block_local_chain_sampled_rows():
+    """Blocks 0, 24 and 49 of the 768x1344 model, each on its own seeded bf16 input, in the
+    forward's launch configuration (fused gates, Q/K RMSNorm + RoPE in the QKV epilogue).
+    Every stage is checked on sampled token rows against the oracle applied to the GPU's own
+    input to that stage, read back from the workspace: AdaLN-1 from x; QKV, q/k and qc from
+    n1; both attentions from q or qc and all of the GPU's keys and values; the output
+    projection from [O | Oc]; AdaLN-2 of x + g1 y from y; FC1 + GELU from n2; FC2 from h; and
+    the block output x + g1 y + g2 m from m."""
+    from video_diffusion_transformer_fwd_amd.runtime import DiTModel
+    w = S.WORKLOADS["768x1344_243f"]
+    model = DiTModel(w)
+    d, H, F = w.d_model, w.n_heads, w.ffn_dim
+    Dh = d // H
+    geo = model.geo
+    g = {k: f64(model.gw[k]) for k in model.gw}
+    mod, _ = dit.modulation(g, 0.75)
+    mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
+    coords = dit.rope_coords(geo.f_lat, geo.grid_h, geo.grid_w, geo.scale)
+    opts = B.make_opts()
+    lay = B.h3_workspace_layout(model.handle, N, opts)
+    rows = sample_rows(N, 10, 21)
+    rt = torch.as_tensor(rows, device=DEV)
+
+    def ws_view(ws, off, width, dtype=torch.bfloat16):
+        n = N * width * torch.tensor([], dtype=dtype).element_size()
+        return ws[off:off + n].view(dtype).view(N, width)
+
+    for b in (0, 24, 49):
+        print(f"block {b}", flush=True)
+        x0 = randn_bf16(100 + b, (N, d))
+        x = x0.clone()
+        ws = model.workspace(N, opts)
+        B.h3_dit_block_fwd(model.handle, b, geo.geom, opts, x, None, None, mod_dev[b], None,
+                           model.ctx_kv[b], ws)
+        torch.cuda.synchronize()
+        sh1, sc1, g1, sh2, sc2, g2 = mod[b]
+        blk = model.blocks[b]
+        tag = f"block {b}"
+        xr = f64(x0[rt])
+        n1 = f64(ws_view(ws, lay.n1, d)[rt])
+        assert_close(n1, dit.adaln(xr, sh1, sc1), what=f"{tag} n1")
+        pre = dit.linear(n1, f64(blk["qkvq_w"]), f64(blk["qkvq_b"]))
+        full = ws_view(ws, lay.qkvq, 4 * d)
+        qkvq = f64(full[rt])
+        q = dit.rope_apply(dit.rms_norm_heads(pre[:, :d].reshape(-1, H, Dh), f64(blk["q_gamma"])), coords[rows])
+        k = dit.rope_apply(dit.rms_norm_heads(pre[:, d:2 * d].reshape(-1, H, Dh), f64(blk["k_gamma"])), coords[rows])
+        assert_close(qkvq[:, :d], q.reshape(-1, d), what=f"{tag} q")
+        assert_close(qkvq[:, d:2 * d], k.reshape(-1, d), what=f"{tag} k")
+        assert_close(qkvq[:, 2 * d:], pre[:, 2 * d:], what=f"{tag} v, qc")
+        kk = f64(full[:, d:2 * d]).reshape(N, H, Dh)
+        vv = f64(full[:, 2 * d:3 * d]).reshape(N, H, Dh)
+        o_ref = dit.attention(qkvq[:, :d].reshape(-1, H, Dh), kk, vv).reshape(-1, d)
+        del kk, vv
+        kc = f64(model.ctx_kv[b, 0]).reshape(-1, H, Dh)
+        vc = f64(model.ctx_kv[b, 1]).reshape(-1, H, Dh)
+        oc_ref = dit.attention(qkvq[:, 3 * d:].reshape(-1, H, Dh), kc, vc).reshape(-1, d)
+        attn = f64(ws_view(ws, lay.attn, 2 * d)[rt])
+        assert_close(attn[:, :d], o_ref, what=f"{tag} self-attention")
+        assert_close(attn[:, d:], oc_ref, what=f"{tag} cross-attention")
+        y_ref = dit.linear(attn, f64(blk["out_w"]), f64(blk["out_b"]) + f64(blk["outc_b"]))
+        y = f64(ws_view(ws, lay.y, d)[rt])
+        assert_close(y, y_ref, what=f"{tag} y")
+        x1 = dit.gated_residual(xr, g1, y)
+        n2 = f64(ws_view(ws, lay.n2, d)[rt])
+        assert_close(n2, dit.adaln(x1, sh2, sc2), what=f"{tag} n2")
+        h = f64(ws_view(ws, lay.h, F)[rt])
+        assert_close(h, dit.gelu(dit.linear(n2, f64(blk["fc1_w"]), f64(blk["fc1_b"]))), what=f"{tag} h")
+        m = f64(ws_view(ws, lay.m, d)[rt])
+        assert_close(m, dit.linear(h, f64(blk["fc2_w"]), f64(blk["fc2_b"])), what=f"{tag} m")
+        assert_close(f64(x[rt]), dit.gated_residual(x1, g2, m), what=f"{tag} output")
+        del ws
+    model.close()
