@@ -194,3 +194,12 @@ def test_864x480_geometry_and_odd_width_pairing(lib):
     last = plan["pairs"].reshape(6 * 15, 14, 2)[:, 13]
     np.testing.assert_array_equal(last[:, 0], last[:, 1])
     np.testing.assert_array_equal(last[:, 0] % 27, 26)
+
+
+def test_binding_refuses_host_tensors():
+    # the library takes bare device addresses; the binding refuses a host tensor before any call
+    import torch
+    with pytest.raises(ValueError):
+        B.ptr(torch.zeros(4))
+    with pytest.raises(ValueError):
+        B.h3_euler_step(torch.zeros(4), torch.zeros(4), 1.0, 0.5)

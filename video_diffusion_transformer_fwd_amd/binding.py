@@ -138,9 +138,32 @@ def _check(code):
         raise H3Error(code, lib().h3_last_error().decode())
 
 
-def ptr(t):
-    """Raw pointer of a tensor (or None)."""
-    return None if t is None else C.c_void_p(t.data_ptr())
+_DTYPES = {}
+
+
+def _dtype(name):
+    if not _DTYPES:
+        import torch
+        _DTYPES.update(bf16=torch.bfloat16, f32=torch.float32, i8=torch.int8)
+    return _DTYPES[name]
+
+
+def ptr(t, dtype=None):
+    """Raw device pointer of a tensor (or None).  The library takes bare device addresses and
+    cannot check them, so a tensor that is not on a GPU, whose innermost stride is not 1, or
+    whose dtype is not ``dtype`` ("bf16", "f32", "i8", or a tuple of them) raises here instead
+    of reaching a kernel."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a device tensor, got one on {t.device}")
+    if t.dim() > 0 and t.size(-1) > 1 and t.stride(-1) != 1:
+        raise ValueError(f"the innermost stride must be 1, got {t.stride(-1)}")
+    if dtype is not None:
+        names = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in tuple(_dtype(n) for n in names):
+            raise TypeError(f"expected {' or '.join(names)}, got {t.dtype}")
+    return C.c_void_p(t.data_ptr())
 
 
 def stream_handle(stream=None):
@@ -246,7 +269,7 @@ def h3_workspace_layout(m, n_tokens, opts) -> h3_ws_layout:
 
 
 def h3_prepare_context(m, ctx, ctx_kv, stream=None):
-    _check(lib().h3_prepare_context(m, ptr(ctx), ptr(ctx_kv), stream_handle(stream)))
+    _check(lib().h3_prepare_context(m, ptr(ctx, "bf16"), ptr(ctx_kv, "bf16"), stream_handle(stream)))
 
 
 def h3_quantize_fc2_weights(m, stream=None):
@@ -258,40 +281,43 @@ def h3_quantize_linear_weights(m, stream=None):
 
 
 def h3_modulation(m, sigma, mod, mod_final, ws, stream=None):
-    _check(lib().h3_modulation(m, sigma, ptr(mod), ptr(mod_final), ptr(ws), ws.numel() * ws.element_size(),
+    _check(lib().h3_modulation(m, sigma, ptr(mod, "f32"), ptr(mod_final, "f32"), ptr(ws), ws.numel() * ws.element_size(),
                                stream_handle(stream)))
 
 
 def h3_dit_block_fwd(m, block, geom, opts, x, n1_in, n1_next, mod, mod_next, ctx_kv, ws, stream=None):
-    _check(lib().h3_dit_block_fwd(m, block, C.byref(geom), C.byref(opts), ptr(x), ptr(n1_in),
-                                  ptr(n1_next), ptr(mod), ptr(mod_next), ptr(ctx_kv), ptr(ws),
+    _check(lib().h3_dit_block_fwd(m, block, C.byref(geom), C.byref(opts), ptr(x, "bf16"), ptr(n1_in),
+                                  ptr(n1_next), ptr(mod, "f32"), ptr(mod_next, "f32"),
+                                  ptr(ctx_kv, "bf16"), ptr(ws),
                                   ws.numel() * ws.element_size(), stream_handle(stream)))
 
 
 def h3_dit_forward(m, geom, opts, latent, sigma, active, eval_index, ctx_kv, velocity, ws, stream=None):
     act = np.ascontiguousarray(active, dtype=np.int32)
-    _check(lib().h3_dit_forward(m, C.byref(geom), C.byref(opts), ptr(latent), sigma,
-                                act.ctypes.data_as(_PI32), len(act), eval_index, ptr(ctx_kv),
-                                ptr(velocity), ptr(ws), ws.numel() * ws.element_size(),
+    _check(lib().h3_dit_forward(m, C.byref(geom), C.byref(opts), ptr(latent, "f32"), sigma,
+                                act.ctypes.data_as(_PI32), len(act), eval_index, ptr(ctx_kv, "bf16"),
+                                ptr(velocity, "f32"), ptr(ws), ws.numel() * ws.element_size(),
                                 stream_handle(stream)))
 
 
 def h3_dit_forward_cached(m, geom, opts, latent, sigma, active, eval_index, ctx_kv, refresh_core,
                           core_delta, velocity, ws, stream=None):
     act = np.ascontiguousarray(active, dtype=np.int32)
-    _check(lib().h3_dit_forward_cached(m, C.byref(geom), C.byref(opts), ptr(latent), sigma,
-                                       act.ctypes.data_as(_PI32), len(act), eval_index, ptr(ctx_kv),
-                                       int(refresh_core), ptr(core_delta), ptr(velocity), ptr(ws),
+    _check(lib().h3_dit_forward_cached(m, C.byref(geom), C.byref(opts), ptr(latent, "f32"), sigma,
+                                       act.ctypes.data_as(_PI32), len(act), eval_index,
+                                       ptr(ctx_kv, "bf16"), int(refresh_core), ptr(core_delta, "f32"),
+                                       ptr(velocity, "f32"), ptr(ws),
                                        ws.numel() * ws.element_size(), stream_handle(stream)))
 
 
 def h3_euler_step(latent, velocity, sigma_cur, sigma_next, stream=None):
-    _check(lib().h3_euler_step(ptr(latent), ptr(velocity), sigma_cur, sigma_next, latent.numel(),
+    _check(lib().h3_euler_step(ptr(latent, "f32"), ptr(velocity, "f32"), sigma_cur, sigma_next, latent.numel(),
                                stream_handle(stream)))
 
 
 def h3_token_reduce(direction, geom, d_model, src, bypass, dst, stream=None):
-    _check(lib().h3_token_reduce(direction, C.byref(geom), d_model, ptr(src), ptr(bypass), ptr(dst),
+    _check(lib().h3_token_reduce(direction, C.byref(geom), d_model, ptr(src, "bf16"), ptr(bypass, "bf16"),
+                                 ptr(dst, "bf16"),
                                  stream_handle(stream)))
 
 
@@ -302,25 +328,28 @@ def h3_gemm_bf16(A, B, C_out, bias=None, bias2=None, epilogue=H3_EPI_NONE, lda=N
     K = K if K is not None else A.shape[1]
     N = N if N is not None else B.shape[0]
     out_f32 = 1 if C_out.dtype.itemsize == 4 else 0
-    _check(lib().h3_gemm_bf16(ptr(A), lda or A.stride(0), ptr(B), ldb or B.stride(0), ptr(C_out),
-                              ldc or C_out.stride(0), M, N, K, ptr(bias), ptr(bias2), epilogue,
+    _check(lib().h3_gemm_bf16(ptr(A, "bf16"), lda or A.stride(0), ptr(B, "bf16"), ldb or B.stride(0),
+                              ptr(C_out, ("bf16", "f32")), ldc or C_out.stride(0), M, N, K,
+                              ptr(bias, "bf16"), ptr(bias2, "bf16"), epilogue,
                               out_f32, stream_handle(stream)))
 
 
 def h3_attention(Q, K, V, O, n_q, n_k, n_heads, head_dim, stream=None):
-    _check(lib().h3_attention(ptr(Q), Q.stride(0), ptr(K), K.stride(0), ptr(V), V.stride(0), ptr(O),
-                              O.stride(0), n_q, n_k, n_heads, head_dim, stream_handle(stream)))
+    _check(lib().h3_attention(ptr(Q, "bf16"), Q.stride(0), ptr(K, "bf16"), K.stride(0), ptr(V, "bf16"),
+                              V.stride(0), ptr(O, "bf16"), O.stride(0), n_q, n_k, n_heads, head_dim, stream_handle(stream)))
 
 
 def h3_quant_rows(X, Q, S, group, stream=None):
     rows, K = X.shape
-    _check(lib().h3_quant_rows(ptr(X), ptr(Q), ptr(S), rows, K, group, stream_handle(stream)))
+    _check(lib().h3_quant_rows(ptr(X, "bf16"), ptr(Q, "i8"), ptr(S, "f32"), rows, K, group,
+                               stream_handle(stream)))
 
 
 def h3_gemm_i8(QA, SA, QW, SW, bias, C_out, group, epilogue=0, stream=None):
     M, K = QA.shape
     N = QW.shape[0]
-    _check(lib().h3_gemm_i8(ptr(QA), ptr(SA), ptr(QW), ptr(SW), ptr(bias), ptr(C_out),
+    _check(lib().h3_gemm_i8(ptr(QA, "i8"), ptr(SA, "f32"), ptr(QW, "i8"), ptr(SW, "f32"), ptr(bias, "bf16"),
+                            ptr(C_out, "bf16"),
                             C_out.stride(0), M, N, K, group, epilogue, stream_handle(stream)))
 
 
@@ -333,33 +362,38 @@ def h3_qkv_gemm(A, W, bias, C_out, head_dim, q_gamma, k_gamma, qk_norm, table, S
     d = W.shape[0] // 4
     a_q8 = int(A.dtype == torch.int8)
     used = C.c_int32()
-    _check(lib().h3_qkv_gemm(ptr(A), A.stride(0), ptr(SA), ptr(W), W.stride(0), ptr(SW), ptr(bias),
-                             ptr(C_out), C_out.stride(0), M, d, K, head_dim, ptr(q_gamma),
-                             ptr(k_gamma), int(qk_norm), ptr(table), a_q8, int(fused),
+    kind = "i8" if a_q8 else "bf16"
+    _check(lib().h3_qkv_gemm(ptr(A, kind), A.stride(0), ptr(SA, "f32"), ptr(W, kind), W.stride(0),
+                             ptr(SW, "f32"), ptr(bias, "bf16"), ptr(C_out, "bf16"), C_out.stride(0), M,
+                             d, K, head_dim, ptr(q_gamma, "bf16"), ptr(k_gamma, "bf16"), int(qk_norm),
+                             ptr(table, "f32"), a_q8, int(fused),
                              C.byref(used), stream_handle(stream)))
     return bool(used.value)
 
 
 def h3_gate_adaln(x, y, gate, x_out, shift, scale, n_out, stream=None):
     rows, d = x.shape
-    _check(lib().h3_gate_adaln(ptr(x), ptr(y), ptr(gate), ptr(x_out), ptr(shift), ptr(scale),
-                               ptr(n_out), rows, d, stream_handle(stream)))
+    _check(lib().h3_gate_adaln(ptr(x, "bf16"), ptr(y, "bf16"), ptr(gate, "f32"), ptr(x_out, "bf16"),
+                               ptr(shift, "f32"), ptr(scale, "f32"), ptr(n_out, "bf16"), rows, d,
+                               stream_handle(stream)))
 
 
 def h3_gate_adaln_quant(x, y, gate, x_out, shift, scale, q_out, s_out, stream=None):
     rows, d = x.shape
-    _check(lib().h3_gate_adaln_quant(ptr(x), ptr(y), ptr(gate), ptr(x_out), ptr(shift), ptr(scale),
-                                     ptr(q_out), ptr(s_out), rows, d, stream_handle(stream)))
+    _check(lib().h3_gate_adaln_quant(ptr(x, "bf16"), ptr(y, "bf16"), ptr(gate, "f32"),
+                                     ptr(x_out, "bf16"), ptr(shift, "f32"), ptr(scale, "f32"),
+                                     ptr(q_out, "i8"), ptr(s_out, "f32"), rows, d,
+                                     stream_handle(stream)))
 
 
 def h3_rope_table(geom, head_dim, table, stream=None):
-    _check(lib().h3_rope_table(C.byref(geom), head_dim, ptr(table), stream_handle(stream)))
+    _check(lib().h3_rope_table(C.byref(geom), head_dim, ptr(table, "f32"), stream_handle(stream)))
 
 
 def h3_qk_norm_rope(qkvq, n_tokens, d_model, head_dim, q_gamma, k_gamma, qk_norm, table,
                     stream=None):
-    _check(lib().h3_qk_norm_rope(ptr(qkvq), qkvq.stride(0), n_tokens, d_model, head_dim,
-                                 ptr(q_gamma), ptr(k_gamma), int(qk_norm), ptr(table),
+    _check(lib().h3_qk_norm_rope(ptr(qkvq, "bf16"), qkvq.stride(0), n_tokens, d_model, head_dim,
+                                 ptr(q_gamma, "bf16"), ptr(k_gamma, "bf16"), int(qk_norm), ptr(table, "f32"),
                                  stream_handle(stream)))
 
 
