@@ -1,6 +1,7 @@
 """ctypes binding of libh3dit.so: the C ABI of include/h3dit.h under the same names.
 
-Argument marshalling only: tensors become raw device pointers, host arrays become ctypes
+Argument marshalling only: tensors become raw device pointers (after checking that they are
+on a GPU, with unit inner stride and the dtype the header names), host arrays become ctypes
 buffers, error codes become ``H3Error``.  Loading fails loudly when the library has not
 been built; there is no fallback path.
 """
