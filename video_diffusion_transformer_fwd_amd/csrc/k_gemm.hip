@@ -42,6 +42,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
@@ -94,7 +95,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(QKD == 0 || (EPI == H3_EPI_NONE && !OUT_F32 && SPLIT == 1), "QKV epilogue form");
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
-  extern __shared__ __align__(16) unsigned char smem[];
+  // static (its address is known when the kernel is compiled, so the constant parts of the
+  // fragment addresses fold into the LDS instructions' offsets)
+  __shared__ __align__(16) unsigned char smem[Cfg::LDS_BYTES];
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int tile_id = blockIdx.x / SPLIT;
@@ -125,13 +128,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
       return n0 + j;
   };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy targets are scalar
   const int wm = wave / WN, wn = wave % WN;
 
   // Staging: direct global -> LDS loads (global_load_lds_dwordx4).  One wave instruction fills
   // 8 consecutive tile rows = 1 KiB of LDS, lane L landing at byte 16 L: row R = R0 + L/8, slot
   // L%8, which holds chunk (L%8) ^ ((R >> 1) & 7) of that row.  Row blocks R0 = (i * NW + wave)
-  // * 8 walk the A rows then the B rows.
+  // * 8 walk the A rows then the B rows.  LDS holds the NS A stages, then the NS B stages.
   constexpr int NW = NT / 64;
   constexpr int ROW_BLOCKS = (BM + BN) / 8;
   constexpr int LOADS = ROW_BLOCKS / NW;  // load instructions per wave per K slice
@@ -156,14 +160,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
       }
     }
   }
-  auto issue_slice = [&](int stage, int kt) {
+  constexpr int A_BYTES = NS * BM * 128;  // the B stages start here
+  // copies K slice kt into stage S (a compile-time constant: the LDS targets are scalar)
+  auto issue_slice = [&](int kt, auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
     const uint32_t kb = static_cast<uint32_t>(kt * BK * 2);
-    unsigned char *st = smem + stage * Cfg::STAGE;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int R0 = (i * NW + wave) * 8;
-      const unsigned char *src = (R0 < BM ? abase : bbase) + (goff[i] + kb);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(st + R0 * 128), 16, 0, 0);
+      const unsigned char *base = (R0 < BM ? abase : bbase) + kb;  // uniform
+      const unsigned char *src = base + goff[i];
+      lds_u8 *dst = (lds_u8 *)smem +
+                    (R0 < BM ? S * BM * 128 + R0 * 128 : A_BYTES + S * BN * 128 + (R0 - BM) * 128);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
     }
   };
 
@@ -173,43 +182,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16_t{};
 
+  // Fragment addresses.  Row (wm TM + i) 32 + fr of A has swizzle key (fr >> 1) & 7 for every i,
+  // so the chunk 2 ks + fh of that row sits at a_lane ^ 32 ks + 4096 i (+ BM 128 S for stage S),
+  // with a_lane the lane's row of block 0 and its swizzled chunk fh; B likewise from b_lane.
   const int fr = lane & 31, fh = lane >> 5;
-  int a_row[TM], b_row[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) a_row[i] = (wm * TM + i) * 32 + fr;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) b_row[j] = (wn * TN + j) * 32 + fr;
+  const int a_lane = (wm * TM * 32 + fr) * 128 + ((fh ^ ((fr >> 1) & 7)) << 4);
+  const int b_lane = A_BYTES + (wn * TN * 32 + fr) * 128 + ((fh ^ ((fr >> 1) & 7)) << 4);
+  const lds_u8 *lds = (const lds_u8 *)smem;
 
   // NS-stage pipeline: slices kt+1 .. kt+NS-1 stream into LDS while slice kt feeds the MFMAs.
+  // The K loop is unrolled over the stages, so each stage's offsets are compile-time constants.
   const int KT = kc / BK;
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < KT) issue_slice(p, p);
+  issue_slice(0, std::integral_constant<int, 0>{});
+  if constexpr (NS == 3)
+    if (KT > 1) issue_slice(1, std::integral_constant<int, 1>{});
   if (KT >= NS - 1)
     lds_dma_barrier<LOADS * (NS - 2)>();
   else
     lds_dma_barrier<0>();
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const unsigned char *st = smem + (kt % NS) * Cfg::STAGE;
+  auto slice = [&](int kt, auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
     const bool more = kt + NS - 1 < KT;
-    if (more) issue_slice((kt + NS - 1) % NS, kt + NS - 1);
+    if (more) issue_slice(kt + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+    auto afrag = [&](int i, int ks) {
+      return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
+          lds + ((a_lane ^ (32 * ks)) + S * BM * 128 + i * 4096));
+    };
+    auto bfrag = [&](int j, int ks) {
+      return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
+          lds + ((b_lane ^ (32 * ks)) + S * BN * 128 + j * 4096));
+    };
     bf16x8_t af[2][TM], bfr[2][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const bf16x8_t *>(st + swz(a_row[i], fh));
+    for (int i = 0; i < TM; ++i) af[0][i] = afrag(i, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8_t *>(st + BM * 128 + swz(b_row[j], fh));
+    for (int j = 0; j < TN; ++j) bfr[0][j] = bfrag(j, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int cur = ks & 1;
       if (ks + 1 < BK / 16) {
-        const int ch = 2 * (ks + 1) + fh;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = *reinterpret_cast<const bf16x8_t *>(st + swz(a_row[i], ch));
+        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = afrag(i, ks + 1);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bfr[cur ^ 1][j] = *reinterpret_cast<const bf16x8_t *>(st + BM * 128 + swz(b_row[j], ch));
+        for (int j = 0; j < TN; ++j) bfr[cur ^ 1][j] = bfrag(j, ks + 1);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -228,11 +245,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
       }
     }
     // slice kt+1 must be complete (later slices may still be in flight); every wave must be
-    // done reading stage kt % NS before the next iteration refills it
+    // done reading stage S before the next slice refills it
     if (more)
       lds_dma_barrier<LOADS * (NS - 2)>();
     else
       lds_dma_barrier<0>();
+  };
+  for (int kt = 0; kt < KT; kt += NS) {
+    slice(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < KT) slice(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS == 3)
+      if (kt + 2 < KT) slice(kt + 2, std::integral_constant<int, 2>{});
   }
 
   // lane holds C[m_l][n_l + 8q + e], e = 0..3, in accumulator registers 4q + e of each 32x32 block
@@ -381,9 +404,7 @@ void run_gemm(const GemmArgs &a, hipStream_t s) {
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD>;
-  static std::atomic<uint64_t> lds_set{0};
-  set_dynamic_lds(reinterpret_cast<const void *>(kern), static_cast<int>(Cfg::LDS_BYTES), lds_set);
-  kern<<<tiles * SPLIT, Cfg::NT, Cfg::LDS_BYTES, s>>>(a);
+  kern<<<tiles * SPLIT, Cfg::NT, 0, s>>>(a);
 }
 
 // Sums the split-K partials [S][M][N] in piece order and applies the bias / GELU epilogue.
