@@ -3,7 +3,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstddef>
 #include <cstdint>
 #include <string>
@@ -18,18 +17,6 @@ void clear_error();
 int32_t fail(int32_t code, const std::string &msg);
 // Checks the launch status of the last kernel(s); returns H3_OK or H3_EHIP.
 int32_t check_launch(const char *what);
-
-// Raises kernel `kern`'s dynamic LDS limit to `bytes` on the current device, once per device
-// (`done` holds one bit per device id; concurrent first calls both set the same value).  A
-// failure is left to the launch, which then reports it.
-inline void set_dynamic_lds(const void *kern, int bytes, std::atomic<uint64_t> &done) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return;
-  const uint64_t bit = uint64_t{1} << (dev & 63);
-  if (done.load(std::memory_order_acquire) & bit) return;
-  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess)
-    done.fetch_or(bit, std::memory_order_release);
-}
 
 // ---------------------------------------------------------------- bf16 helpers
 typedef uint16_t bf16_t;

@@ -48,12 +48,9 @@ constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
 // LDS holds 64 banks of 4 bytes; a 16-byte-per-lane read is served 16 lanes per cycle.  Tile
-// rows are 128 bytes, so two rows share one 256-byte bank line: chunk c of row r is stored in
-// slot c ^ ((r >> 1) & 7), which puts the 16 rows an MFMA-operand read touches at one chunk
-// on 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
+// rows are 128 bytes, so two rows share one 256-byte bank line: 16-byte chunk c of row r is
+// stored at byte r * 128 + ((c ^ ((r >> 1) & 7)) << 4), which puts the 16 rows an MFMA-operand
+// read touches at one chunk on 16 distinct 16-byte bank groups.
 
 template <int BM, int BN, int WM, int WN, int NS = 2>
 struct GemmCfg {

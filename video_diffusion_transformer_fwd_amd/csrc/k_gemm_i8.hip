@@ -23,6 +23,8 @@
 // of the bf16 product) runs from an LDS band in a rolled loop, as in the bf16 product.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "h3_internal.h"
 
 namespace h3 {
@@ -35,9 +37,7 @@ typedef __attribute__((ext_vector_type(16))) int i32x16_t;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 template <int BM, int BN, int WM, int WN, int NS>
 struct GemmI8Cfg {
@@ -78,7 +78,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
   static_assert(QKD == 0 || (!GROUPED && SPLIT == 1 && EPI == H3_EPI_NONE), "QKV epilogue form");
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
-  extern __shared__ __align__(16) unsigned char smem8[];
+  // static: constant parts of the fragment addresses fold into the LDS instructions' offsets
+  __shared__ __align__(16) unsigned char smem8[Cfg::LDS_BYTES];
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int tile_id = blockIdx.x / SPLIT;
@@ -108,10 +109,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
     else
       return n0 + j;
   };
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy targets are scalar
   const int wm = wave / WN, wn = wave % WN;
 
-  // direct global -> LDS staging, as in the bf16 product (1 byte per element here)
+  // direct global -> LDS staging, as in the bf16 product (1 byte per element here); LDS holds
+  // the NS A stages, then the NS B stages
   constexpr int NW = NT / 64;
   constexpr int ROW_BLOCKS = (BM + BN) / 8;
   constexpr int LOADS = ROW_BLOCKS / NW;
@@ -136,23 +139,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
       }
     }
   }
-  auto issue_slice = [&](int stage, int kt) {
+  constexpr int A_BYTES = NS * BM * 128;  // the B stages start here
+  // stage: a compile-time constant (the unrolled loop: LDS offsets are immediates) or an int
+  auto issue_slice = [&](int kt, auto stage) __attribute__((always_inline)) {
+    const int S = stage;
     const uint32_t kb = static_cast<uint32_t>(kt * BK);
-    unsigned char *st = smem8 + stage * Cfg::STAGE;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int R0 = (i * NW + wave) * 8;
-      const unsigned char *src = (R0 < BM ? abase : bbase) + (goff[i] + kb);
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(st + R0 * 128), 16, 0, 0);
+      const unsigned char *base = (R0 < BM ? abase : bbase) + kb;  // uniform
+      const unsigned char *src = base + goff[i];
+      lds_u8 *dst = (lds_u8 *)smem8 +
+                    (R0 < BM ? S * BM * 128 + R0 * 128 : A_BYTES + S * BN * 128 + (R0 - BM) * 128);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
     }
   };
 
+  // fragment addresses, as in the bf16 product: chunk 2 ks + fh of A row (wm TM + i) 32 + fr
+  // sits at a_lane ^ 32 ks + 4096 i (+ BM 128 S for stage S); B likewise from b_lane
   const int fr = lane & 31, fh = lane >> 5;
-  int a_row[TM], b_row[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) a_row[i] = (wm * TM + i) * 32 + fr;
-#pragma unroll
-  for (int j = 0; j < TN; ++j) b_row[j] = (wn * TN + j) * 32 + fr;
+  const int a_lane = (wm * TM * 32 + fr) * 128 + ((fh ^ ((fr >> 1) & 7)) << 4);
+  const int b_lane = A_BYTES + (wn * TN * 32 + fr) * 128 + ((fh ^ ((fr >> 1) & 7)) << 4);
+  const lds_u8 *lds = (const lds_u8 *)smem8;
 
   // lane holds C[m_l][n_l + 8q + e], e = 0..3, in accumulator registers 4q + e of each block
   const int m_l = lane & 31, n_l = (lane >> 5) * 4;
@@ -174,16 +182,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
   const int KT = kc / BK;
   const int slices_per_group = g.group / BK;
   const int ngroups = g.K / g.group;
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < KT) issue_slice(p, p);
+  issue_slice(0, std::integral_constant<int, 0>{});
+  if constexpr (NS == 3)
+    if (KT > 1) issue_slice(1, std::integral_constant<int, 1>{});
   if (KT >= NS - 1)
     lds_dma_barrier<LOADS * (NS - 2)>();
   else
     lds_dma_barrier<0>();
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const unsigned char *st = smem8 + (kt % NS) * Cfg::STAGE;
+  // one K slice out of stage S; the K loop is unrolled over the stages (rolled for the grouped
+  // fold, whose float totals leave no registers for copies of the loop body)
+  auto slice = [&](int kt, auto stage) __attribute__((always_inline)) {
+    const int S = stage;
     const bool more = kt + NS - 1 < KT;
     // grouped: this slice ends a group -> fetch the group's activation scales now (before this
     // iteration's slice loads, so waiting for them never waits for those) and use them after
@@ -201,23 +211,34 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
         }
       }
     }
-    if (more) issue_slice((kt + NS - 1) % NS, kt + NS - 1);
+    if (more) {
+      if constexpr (std::is_same_v<decltype(stage), int>)
+        issue_slice(kt + NS - 1, (S + NS - 1) % NS);
+      else
+        issue_slice(kt + NS - 1, std::integral_constant<int, (decltype(stage)::value + NS - 1) % NS>{});
+    }
+    auto afrag = [&](int i, int ks) {
+      return *reinterpret_cast<const __attribute__((address_space(3))) i32x4_t *>(
+          lds + ((a_lane ^ (32 * ks)) + S * BM * 128 + i * 4096));
+    };
+    auto bfrag = [&](int j, int ks) {
+      return *reinterpret_cast<const __attribute__((address_space(3))) i32x4_t *>(
+          lds + ((b_lane ^ (32 * ks)) + S * BN * 128 + j * 4096));
+    };
     i32x4_t af[2][TM], bfr[2][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const i32x4_t *>(st + swz(a_row[i], fh));
+    for (int i = 0; i < TM; ++i) af[0][i] = afrag(i, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[0][j] = *reinterpret_cast<const i32x4_t *>(st + BM * 128 + swz(b_row[j], fh));
+    for (int j = 0; j < TN; ++j) bfr[0][j] = bfrag(j, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       const int cur = ks & 1;
       if (ks + 1 < BK / 32) {
-        const int ch = 2 * (ks + 1) + fh;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = *reinterpret_cast<const i32x4_t *>(st + swz(a_row[i], ch));
+        for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = afrag(i, ks + 1);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bfr[cur ^ 1][j] = *reinterpret_cast<const i32x4_t *>(st + BM * 128 + swz(b_row[j], ch));
+        for (int j = 0; j < TN; ++j) bfr[cur ^ 1][j] = bfrag(j, ks + 1);
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -255,6 +276,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_i8_kernel(GemmI8Args g) {
       lds_dma_barrier<LOADS * (NS - 2)>();
     else
       lds_dma_barrier<0>();
+  };
+  if constexpr (GROUPED) {
+    for (int kt = 0; kt < KT; ++kt) slice(kt, kt % NS);
+  } else {
+    for (int kt = 0; kt < KT; kt += NS) {
+      slice(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < KT) slice(kt + 1, std::integral_constant<int, 1>{});
+      if constexpr (NS == 3)
+        if (kt + 2 < KT) slice(kt + 2, std::integral_constant<int, 2>{});
+    }
   }
 
   if constexpr (SPLIT > 1) {
@@ -436,9 +467,7 @@ void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS, GROUPED, SPLIT, EPI, QKD>;
-  static std::atomic<uint64_t> lds_set{0};
-  set_dynamic_lds(reinterpret_cast<const void *>(kern), static_cast<int>(Cfg::LDS_BYTES), lds_set);
-  kern<<<tiles * SPLIT, Cfg::NT, Cfg::LDS_BYTES, s>>>(a);
+  kern<<<tiles * SPLIT, Cfg::NT, 0, s>>>(a);
   if constexpr (SPLIT > 1) {
     const int64_t total4 = static_cast<int64_t>(a.M) * a.N / 4;
     splitk_i8_reduce_kernel<SPLIT, EPI><<<static_cast<int>((total4 + 255) / 256), 256, 0, s>>>(
