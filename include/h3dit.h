@@ -201,6 +201,11 @@ typedef struct h3_run_opts {
                                * (P3 "the int8 path", fused epilogues; bf16 and int8 QKV) where
                                * its tiling allows (h3_qkv_gemm); 0: separate kernel, as the
                                * pages' `--use-slower-unfused-qkv-rope`.  Bit-identical. */
+  int32_t store_branches;     /* 1: the attention and MLP branch outputs y and m are written to
+                               * the workspace (h3_workspace_layout) also where the gate kernel
+                               * sums the products' split-K partials itself; 0: there they are
+                               * not written (nothing downstream reads them).  Results are
+                               * identical either way. */
 } h3_run_opts;
 
 /* Tokens of a geometry (validates it). */
@@ -216,7 +221,9 @@ int32_t h3_workspace_size(const h3_model *m, int32_t n_tokens, const h3_run_opts
  * n1 [N,d], qkvq [N,4d] (q,k after RMSNorm+RoPE), attn [N,2d] (self | cross outputs),
  * y [N,d] (summed output projection), n2 [N,d], h [N,F] (GELU output), m [N,d] (FC2
  * output), hq int8 [N,F], hs float [N, F/1024 or 1].  With int8_linear, n1 and n2 hold the
- * row-quantised AdaLN outputs: int8 [N,d] followed by float [N]. */
+ * row-quantised AdaLN outputs: int8 [N,d] followed by float [N].  y and m hold the branches
+ * only with store_branches = 1, or where the product is not split (the unfused gate, widths
+ * above 4096, the int8 FC2). */
 typedef struct h3_ws_layout {
   size_t n1, qkvq, attn, y, n2, h, m, hq, hs, rope, total;
 } h3_ws_layout;

@@ -62,7 +62,7 @@ def test_block_parity(name, fc2_mode, int8_linear):
     mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
     coords = dit.rope_coords(model.geo.f_lat, model.geo.grid_h, model.geo.grid_w, model.geo.scale)
     x0 = S.normal("test.block.x", (n, d), 1.0)
-    opts = B.make_opts(fc2_mode=fc2_mode, int8_linear=int8_linear)
+    opts = B.make_opts(fc2_mode=fc2_mode, int8_linear=int8_linear, store_branches=True)
     for b in range(w.n_blocks):
         x = x0.to(DEV)
         ws = run_block(model, w, b, x, mod_dev, opts)
@@ -177,7 +177,7 @@ def test_int8_row_split_k_bit_identical_to_unsplit(frames):
     mod, _ = dit.modulation(om["global"], 0.75)
     mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
     x = S.normal("test.block.x3", (n, d), 1.0).to(DEV)
-    opts = B.make_opts(fc2_mode="row")
+    opts = B.make_opts(fc2_mode="row", store_branches=True)
     ws = run_block(model, w, 1, x, mod_dev, opts)
     lay = B.h3_workspace_layout(model.handle, n, opts)
     hq = ws_view(ws, lay.hq, (n, F), torch.int8).clone()

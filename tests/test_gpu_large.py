@@ -163,7 +163,7 @@ def test_block_local_chain_sampled_rows():
     mod, _ = dit.modulation(g, 0.75)
     mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
     coords = dit.rope_coords(geo.f_lat, geo.grid_h, geo.grid_w, geo.scale)
-    opts = B.make_opts()
+    opts = B.make_opts(store_branches=True)
     lay = B.h3_workspace_layout(model.handle, N, opts)
     rows = sample_rows(N, 10, 21)
     rt = torch.as_tensor(rows, device=DEV)

@@ -55,7 +55,7 @@ class h3_geom(C.Structure):
 class h3_run_opts(C.Structure):
     _fields_ = [(n, C.c_int32) for n in
                 ("fc2_mode", "fused_gate_adaln", "fused_cross_block", "qk_norm", "token_reduction",
-                 "int8_linear", "fused_qk_rope")]
+                 "int8_linear", "fused_qk_rope", "store_branches")]
 
 
 class h3_ws_layout(C.Structure):
@@ -239,10 +239,11 @@ def h3_geom_tokens(geom: h3_geom) -> int:
 
 
 def make_opts(fc2_mode="bf16", fused_gate_adaln=True, fused_cross_block=True, qk_norm=True,
-              token_reduction=False, int8_linear=False, fused_qk_rope=True):
+              token_reduction=False, int8_linear=False, fused_qk_rope=True, store_branches=False):
     return h3_run_opts(FC2_MODES[fc2_mode] if isinstance(fc2_mode, str) else fc2_mode,
                        int(fused_gate_adaln), int(fused_cross_block), int(qk_norm),
-                       int(token_reduction), int(int8_linear), int(fused_qk_rope))
+                       int(token_reduction), int(int8_linear), int(fused_qk_rope),
+                       int(store_branches))
 
 
 # ------------------------------------------------------------------ model

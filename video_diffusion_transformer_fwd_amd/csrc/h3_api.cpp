@@ -30,6 +30,7 @@ int32_t check_opts(const h3_run_opts *o) {
     return fail(H3_EINVAL, "fc2_mode must be 0, 1 or 2");
   if (o->int8_linear != 0 && o->int8_linear != 1) return fail(H3_EINVAL, "int8_linear must be 0 or 1");
   if (o->fused_qk_rope != 0 && o->fused_qk_rope != 1) return fail(H3_EINVAL, "fused_qk_rope must be 0 or 1");
+  if (o->store_branches != 0 && o->store_branches != 1) return fail(H3_EINVAL, "store_branches must be 0 or 1");
   return H3_OK;
 }
 
@@ -223,9 +224,9 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
   }
   // y = [O | Oc] [W_o | W_oc]^T + b_o + b_oc.  When the product splits K, its partials go
   // straight to the gate kernel, which sums them exactly as the split-K reduction would (and
-  // still stores y, so the workspace holds the branch either way).
+  // stores y only when asked to: nothing downstream reads it).
   GateY yp{sk.part, 0, static_cast<int64_t>(rows) * d, reinterpret_cast<const bf16_t *>(w.out_b),
-           reinterpret_cast<const bf16_t *>(w.outc_b), y};
+           reinterpret_cast<const bf16_t *>(w.outc_b), o.store_branches ? y : nullptr};
   {
     ProfScope ps(H3_ST_OUT_GEMM, s);
     // (widths above 4096 keep the separate reduction: the gate kernel's registers would spill)
@@ -259,7 +260,7 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
   }
   // m = FC2(h) (bf16 FC2 with K split: partials reduced by the gate kernel, as above)
   GateY mp{sk.part, 0, static_cast<int64_t>(rows) * d, reinterpret_cast<const bf16_t *>(w.fc2_b),
-           nullptr, mo};
+           nullptr, o.store_branches ? mo : nullptr};
   if (o.fc2_mode == H3_FC2_BF16) {
     ProfScope ps(H3_ST_FC2_GEMM, s);
     if (d <= 4096)

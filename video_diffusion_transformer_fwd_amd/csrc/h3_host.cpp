@@ -36,7 +36,7 @@ extern "C" {
 
 const char *h3_last_error(void) { return g_last_error.c_str(); }
 
-int32_t h3_abi_version(void) { return 102; }
+int32_t h3_abi_version(void) { return 103; }
 
 int32_t h3_align_frames(int32_t requested, int32_t *frames) {
   if (!frames) return fail(H3_EINVAL, "h3_align_frames: frames is NULL");
