@@ -78,6 +78,10 @@ def test_gemm_strided_operands():
     (1536, 256, 2, 128),   # cross-attention length
     (5, 1, 1, 64),         # one key: output is that value
     (64, 600, 2, 64),      # keys span several tiles with a ragged tail
+    # more than 256 (query tile, head) pairs: four-wave workgroups; the cases above (fewer)
+    # take the eight-wave workgroups that split the key tiles between two wave groups
+    (1040, 300, 32, 128),
+    (700, 100, 48, 64),
 ])
 def test_attention(nq, nk, H, D):
     rng = np.random.default_rng(nq + 13 * nk + H * D)

@@ -65,16 +65,24 @@ __device__ __forceinline__ int lds_off(int r, int c) {
   return line * 256 + ((u ^ lds_key<D>(line)) << 4);
 }
 
-template <int D, int WAVES>
+// KG key groups: with KG = 2 the waves form WAVES / 2 query groups twice over, each stage holds
+// two 64-key tiles, and the second group of waves takes the second tile of every stage; the
+// groups' partial softmax sums are merged through LDS at the end.
+template <int D, int WAVES, int KG>
 struct AttnCfg {
   static constexpr int NT = 64 * WAVES;
-  static constexpr int BM = 32 * WAVES;                // queries per workgroup
+  static constexpr int QG = WAVES / KG;                // query groups (32 queries each)
+  static constexpr int BM = 32 * QG;                   // queries per workgroup
+  static constexpr int KT = kBlockN * KG;              // keys per stage
   static constexpr int ROW = 2 * D;                    // bytes per staged key row
-  static constexpr int TILE = kBlockN * ROW;           // bytes per K (or V) tile
-  static constexpr int STAGE = 2 * TILE;               // K tile, then V tile
-  static constexpr int LDS = 2 * STAGE;                // two stages (64 KiB at D = 128)
-  static constexpr int LOADS = TILE / (1024 * WAVES);  // DMA instructions per wave per K or V tile
-  static_assert(LOADS >= 1 && TILE % (1024 * WAVES) == 0, "a tile must split over the waves");
+  static constexpr int TILE = KT * ROW;                // bytes per K (or V) stage
+  static constexpr int STAGE = 2 * TILE;               // K rows, then V rows
+  static constexpr int LDS = 2 * STAGE;                // two stages (64 KiB at D = 128, KG = 1)
+  static constexpr int LOADS = TILE / (1024 * WAVES);  // DMA instructions per wave per K or V stage
+  static constexpr int OW = D / 2 + 2;                 // floats per lane handed over by the merge
+  static_assert(KG == 1 || KG == 2, "one or two key groups");
+  static_assert(LOADS >= 1 && TILE % (1024 * WAVES) == 0, "a stage must split over the waves");
+  static_assert(KG == 1 || QG * 64 * OW * 4 <= LDS, "the merge buffer must fit the stages");
 };
 
 // One attention problem; a launch may carry two (blockIdx.z selects), e.g. the self- and the
@@ -94,10 +102,10 @@ struct AttnProblems {
   AttnProblem p[2];
 };
 
-template <int D, int WAVES>
+template <int D, int WAVES, int KG>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kernel(
     AttnProblems probs, float scale_log2) {
-  using Cfg = AttnCfg<D, WAVES>;
+  using Cfg = AttnCfg<D, WAVES, KG>;
   // static (its address known when the kernel is compiled, so constant parts of LDS addresses
   // fold into the instructions' offsets; a dynamic array's base is a link-time symbol)
   __shared__ __align__(16) unsigned char smem[Cfg::LDS];
@@ -113,11 +121,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
   const int64_t ldq = second ? p1.ldq : p0.ldq, ldk = second ? p1.ldk : p0.ldk;
   const int64_t ldv = second ? p1.ldv : p0.ldv, ldo = second ? p1.ldo : p0.ldo;
   const int nq = second ? p1.nq : p0.nq, nk = second ? p1.nk : p0.nk;
-  // (query tile, head) of this workgroup.  Hardware ids go round-robin over the 8 XCDs; with
-  // four-wave workgroups (short sequences) each XCD takes a contiguous run of (tile, head)
+  // (query tile, head) of this workgroup.  Hardware ids go round-robin over the 8 XCDs; for short
+  // sequences (four-wave or key-group workgroups) each XCD takes a contiguous run of (tile, head)
   // pairs instead, so the query tiles of one head share its keys and values in that XCD's L2
   int tile = blockIdx.x, head = blockIdx.y;
-  if constexpr (WAVES == 4) {
+  if constexpr (WAVES == 4 || KG == 2) {
     const int per_plane = gridDim.x * gridDim.y;
     if (per_plane % 8 == 0) {
       int pid = blockIdx.x + gridDim.x * blockIdx.y;
@@ -129,7 +137,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
   if (tile * Cfg::BM >= nq) return;  // this problem has fewer query tiles
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q_base = tile * Cfg::BM + wave * 32;
+  // query group, key group (compile-time 0 with one key group)
+  const int qg = KG == 1 ? wave : wave % Cfg::QG, kh = KG == 1 ? 0 : wave / Cfg::QG;
+  const int q_base = tile * Cfg::BM + qg * 32;
   const int hoff = head * D;
   const int l32 = lane & 31, g = lane >> 5;
 
@@ -174,15 +184,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     koff[j] = static_cast<uint32_t>((r * ldk + hoff + 8 * c) * 2);
     voff[j] = static_cast<uint32_t>((r * ldv + hoff + 8 * c) * 2);
   }
-  const int n_tiles = (nk + kBlockN - 1) / kBlockN;
+  const int n_tiles = (nk + Cfg::KT - 1) / Cfg::KT;  // stages
   // loads tile t into stage S (S a compile-time constant: the LDS destinations are immediates)
   auto issue = [&](int t, auto stage) {
     constexpr int S = decltype(stage)::value;
-    const int kv0 = t * kBlockN;
+    const int kv0 = t * Cfg::KT;
     const unsigned char *kb = reinterpret_cast<const unsigned char *>(K + static_cast<int64_t>(kv0) * ldk);
     const unsigned char *vb = reinterpret_cast<const unsigned char *>(V + static_cast<int64_t>(kv0) * ldv);
     uint32_t ko[Cfg::LOADS], vo[Cfg::LOADS];
-    if (kv0 + kBlockN <= nk) {  // workgroup-uniform
+    if (kv0 + Cfg::KT <= nk) {  // workgroup-uniform
 #pragma unroll
       for (int j = 0; j < Cfg::LOADS; ++j) ko[j] = koff[j], vo[j] = voff[j];
     } else {
@@ -235,15 +245,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     }
   }
 
-  // one key tile out of stage S
-  auto tile_step = [&](int t, auto stage) {
-    constexpr int S = decltype(stage)::value;
-    const int kv0 = t * kBlockN;
-    // tile t has landed (this thread's loads, then every thread's at the barrier), and every
-    // wave is done with the other stage, which the next issue refills
-    lds_dma_barrier<0>();
-    if (t + 1 < n_tiles) issue(t + 1, std::integral_constant<int, S ^ 1>{});
-    const lds_u8 *st = lds + S * Cfg::STAGE;
+  // one 64-key tile: keys kv0 .. kv0+63, K rows at st, V rows at st + TILE
+  auto key_tile = [&](const lds_u8 *st, int kv0) __attribute__((always_inline)) {
 
     // S^T = K Q^T for keys kv0 .. kv0+63 (two 32-key blocks).  The K fragments of step
     // ks + 2 are read while step ks's two MFMAs run (a ring of three), so the LDS latency is
@@ -302,7 +305,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       m_ref = m_new;
     }
-    const float mc = m_ref * scale_log2;
+    // (with two key groups a wave may have seen no key yet (n_k <= 64): then every score and the
+    // reference are -inf, and P must come out 0 rather than 2^(-inf + inf))
+    const float mc = KG == 1 || m_ref != -INFINITY ? m_ref * scale_log2 : 0.f;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -343,10 +348,47 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     }
   };
 
+  // one stage out of LDS stage S: this wave's key group takes its 64-key tile
+  auto stage_step = [&](int t, auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    const int kv0 = t * Cfg::KT + kh * kBlockN;
+    // stage t has landed (this thread's loads, then every thread's at the barrier), and every
+    // wave is done with the other stage, which the next issue refills
+    lds_dma_barrier<0>();
+    if (t + 1 < n_tiles) issue(t + 1, std::integral_constant<int, S ^ 1>{});
+    if (KG == 1 || kv0 < nk) key_tile(lds + S * Cfg::STAGE + kh * kBlockN * Cfg::ROW, kv0);
+  };
+
   if (n_tiles > 0) issue(0, std::integral_constant<int, 0>{});
   for (int t = 0; t < n_tiles; t += 2) {
-    tile_step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) tile_step(t + 1, std::integral_constant<int, 1>{});
+    stage_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) stage_step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  if constexpr (KG == 2) {
+    // merge the key groups: the second group's waves hand (m, l, O) over LDS to the first
+    // group's wave of the same queries, which rescales both to the larger reference
+    float *xch = reinterpret_cast<float *>(smem) + qg * 64 * Cfg::OW;
+    __syncthreads();  // every wave is done with the staged tiles (no copy is in flight)
+    if (kh == 1) {
+      xch[lane] = m_ref;
+      xch[64 + lane] = l_run;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[(2 + db * 16 + i) * 64 + lane] = o[db][i];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = xch[lane], l1 = xch[64 + lane];
+    const float m = fmaxf(m_ref, m1);  // finite: key 0 belongs to the first group
+    const float a0 = __builtin_amdgcn_exp2f((m_ref - m) * scale_log2);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = o[db][i] * a0 + xch[(2 + db * 16 + i) * 64 + lane] * a1;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -367,25 +409,32 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
   }
 }
 
-template <int D, int WAVES>
+template <int D, int WAVES, int KG>
 void launch_cfg(const AttnProblems &pr, int n_problems, int heads, float scale_log2, hipStream_t s) {
-  using Cfg = AttnCfg<D, WAVES>;
+  using Cfg = AttnCfg<D, WAVES, KG>;
   int tiles = 0;
   for (int i = 0; i < n_problems; ++i) tiles = std::max(tiles, (pr.p[i].nq + Cfg::BM - 1) / Cfg::BM);
   dim3 grid(tiles, heads, n_problems), block(Cfg::NT);
-  attention_kernel<D, WAVES><<<grid, block, 0, s>>>(pr, scale_log2);
+  attention_kernel<D, WAVES, KG><<<grid, block, 0, s>>>(pr, scale_log2);
 }
 
+// 8192+ queries: 8-wave workgroups of 256 queries.  Fewer: 128 queries per workgroup, with 4
+// waves (two workgroups per CU) when the (query tile, head) grid of the longest problem covers
+// the 256 CUs, else with 8 waves in two key groups (two waves per SIMD on each occupied CU,
+// every wave half the key tiles).
 void launch_problems(const AttnProblems &pr, int n_problems, int heads, int head_dim, hipStream_t s) {
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
   int nq = 0;
   for (int i = 0; i < n_problems; ++i) nq = std::max(nq, pr.p[i].nq);
+  const bool sparse = static_cast<int64_t>((nq + 127) / 128) * heads <= 256;
   if (head_dim == 128 && nq >= 8192)
-    launch_cfg<128, 8>(pr, n_problems, heads, scale_log2, s);
+    launch_cfg<128, 8, 1>(pr, n_problems, heads, scale_log2, s);
   else if (head_dim == 128)
-    launch_cfg<128, 4>(pr, n_problems, heads, scale_log2, s);
+    sparse ? launch_cfg<128, 8, 2>(pr, n_problems, heads, scale_log2, s)
+           : launch_cfg<128, 4, 1>(pr, n_problems, heads, scale_log2, s);
   else
-    launch_cfg<64, 4>(pr, n_problems, heads, scale_log2, s);
+    sparse ? launch_cfg<64, 8, 2>(pr, n_problems, heads, scale_log2, s)
+           : launch_cfg<64, 4, 1>(pr, n_problems, heads, scale_log2, s);
 }
 
 }  // namespace
