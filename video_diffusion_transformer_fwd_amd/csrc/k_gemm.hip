@@ -87,11 +87,20 @@ struct GemmArgs {
 
 // QKD > 0: the QKV product with heads of QKD channels; columns follow QkMap<BN, QKD> and the
 // epilogue applies the Q/K RMSNorm + RoPE to the q/k heads (bias, no GELU, bf16, unsplit).
-template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
+// KSG = 2 (split-K products only): twice the waves, in two groups over the same WM x WN layout;
+// each group takes half of the 16-wide K steps of every staged slice (two waves per SIMD where
+// one group alone has one), and the second group hands its accumulators to the first through
+// LDS before the partial tile is stored.
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0,
+          int KSG = 1>
+__global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(QKD == 0 || (EPI == H3_EPI_NONE && !OUT_F32 && SPLIT == 1), "QKV epilogue form");
+  static_assert(KSG == 1 || (KSG == 2 && SPLIT > 1), "two K-step groups: split-K partial tiles only");
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
-  constexpr int NT = Cfg::NT, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
+  constexpr int NT = Cfg::NT * KSG, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
+  constexpr int KS_PER = BK / 16 / KSG;  // K steps per slice and wave
+  static_assert(KSG == 1 || WM * WN * TM * TN * 16 * 64 * 4 <= Cfg::LDS_BYTES,
+                "the accumulator hand-over must fit the LDS"); 
   // static (its address is known when the kernel is compiled, so the constant parts of the
   // fragment addresses fold into the LDS instructions' offsets)
   __shared__ __align__(16) unsigned char smem[Cfg::LDS_BYTES];
@@ -127,7 +136,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy targets are scalar
-  const int wm = wave / WN, wn = wave % WN;
+  const int wv = wave % (WM * WN), kg = wave / (WM * WN);     // wave of the layout, K-step group
+  const int wm = wv / WN, wn = wv % WN;
 
   // Staging: direct global -> LDS loads (global_load_lds_dwordx4).  One wave instruction fills
   // 8 consecutive tile rows = 1 KiB of LDS, lane L landing at byte 16 L: row R = R0 + L/8, slot
@@ -183,8 +193,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   // so the chunk 2 ks + fh of that row sits at a_lane ^ 32 ks + 4096 i (+ BM 128 S for stage S),
   // with a_lane the lane's row of block 0 and its swizzled chunk fh; B likewise from b_lane.
   const int fr = lane & 31, fh = lane >> 5;
-  const int a_lane = (wm * TM * 32 + fr) * 128 + ((fh ^ ((fr >> 1) & 7)) << 4);
-  const int b_lane = A_BYTES + (wn * TN * 32 + fr) * 128 + ((fh ^ ((fr >> 1) & 7)) << 4);
+  // (group kg starts at K step kg KS_PER: 32 kg KS_PER is folded into the lane bases)
+  const int a_lane = ((wm * TM * 32 + fr) * 128 + ((fh ^ ((fr >> 1) & 7)) << 4)) ^ (32 * KS_PER * kg);
+  const int b_lane = (A_BYTES + (wn * TN * 32 + fr) * 128 + ((fh ^ ((fr >> 1) & 7)) << 4)) ^ (32 * KS_PER * kg);
   const lds_u8 *lds = (const lds_u8 *)smem;
 
   // NS-stage pipeline: slices kt+1 .. kt+NS-1 stream into LDS while slice kt feeds the MFMAs.
@@ -217,9 +228,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
     for (int j = 0; j < TN; ++j) bfr[0][j] = bfrag(j, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < KS_PER; ++ks) {
       const int cur = ks & 1;
-      if (ks + 1 < BK / 16) {
+      if (ks + 1 < KS_PER) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) af[cur ^ 1][i] = afrag(i, ks + 1);
 #pragma unroll
@@ -232,7 +243,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i], acc[i][j], 0, 0, 0);
       // interleave: one MFMA, one fragment read of the next step, ... so the reads are in flight
       // while this step's MFMAs run
-      if (ks + 1 < BK / 16) {
+      if (ks + 1 < KS_PER) {
 #pragma unroll
         for (int q = 0; q < TM + TN; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -257,6 +268,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
 
   // lane holds C[m_l][n_l + 8q + e], e = 0..3, in accumulator registers 4q + e of each 32x32 block
   const int m_l = lane & 31, n_l = (lane >> 5) * 4;
+  // the second group's accumulators join the first's: float [wave][i][j][r][lane] in the
+  // (now free) LDS, consecutive lanes on consecutive words
+  const float *xch = reinterpret_cast<const float *>(smem) + wv * (TM * TN * 16 * 64);
+  if constexpr (KSG == 2) {
+    float *xw = reinterpret_cast<float *>(smem) + wv * (TM * TN * 16 * 64);
+    __syncthreads();  // every wave is done with the staged slices (no copy is in flight)
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xw[((i * TN + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kg == 1) return;  // no barrier follows; the first group adds them as it stores
+  }
   if constexpr (SPLIT > 1) {
     // split-K: store this K piece's float32 partial tile, row-major [piece][M][N] (N % 4 == 0);
     // a separate reduction launch sums the pieces in order and applies the epilogue
@@ -266,14 +294,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
       const int m = m0 + (wm * TM + i) * 32 + m_l;
       if (m >= g.M) continue;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j) {
+        // (with two K-step groups the second group's block is added here, one block at a
+        // time: adding all of them first would hold a second copy of the accumulators)
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v[r] = acc[i][j][r];
+          if constexpr (KSG == 2) v[r] += xch[((i * TN + j) * 16 + r) * 64 + lane];
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int n = n0 + (wn * TN + j) * 32 + q * 8 + n_l;
           if (n < g.N)
             *reinterpret_cast<float4 *>(part + static_cast<int64_t>(m) * g.N + n) =
-                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
         }
+      }
     }
     return;
   }
@@ -396,12 +433,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0>
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0,
+          int KSG = 1>
 void run_gemm(const GemmArgs &a, hipStream_t s) {
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD>;
-  kern<<<tiles * SPLIT, Cfg::NT, 0, s>>>(a);
+  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD, KSG>;
+  kern<<<tiles * SPLIT, Cfg::NT * KSG, 0, s>>>(a);
 }
 
 // Sums the split-K partials [S][M][N] in piece order and applies the bias / GELU epilogue.
@@ -441,9 +479,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 }
 
 // One product: the tiled GEMM, then (split-K) the ordered reduction with the epilogue.
+// split-K products run with two K-step groups (two waves per SIMD)
 template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int S>
 void run_product(const GemmArgs &a, hipStream_t s) {
-  run_gemm<BM, BN, WM, WN, NS, EPI, OUT_F32, S>(a, s);
+  run_gemm<BM, BN, WM, WN, NS, EPI, OUT_F32, S, 0, (S > 1 ? 2 : 1)>(a, s);
   if constexpr (S > 1) {
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
     splitk_reduce_kernel<EPI, OUT_F32, S><<<static_cast<int>((total / 4 + 255) / 256), 256, 0, s>>>(
@@ -505,8 +544,8 @@ int launch_gemm_bf16_partials(const bf16_t *A, int64_t lda, const bf16_t *B, int
   if (p.split <= 1 || !sc.part || p.part_bytes > sc.part_bytes) return 0;
   GemmArgs a{A, lda, B, ldb, nullptr, 0, M, N, K, nullptr, nullptr, sc.part};
   switch (p.cfg * 8 + p.split) {
-    case 1 * 8 + 2: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 2>(a, s); return 2;
-    case 1 * 8 + 4: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 4>(a, s); return 4;
+    case 1 * 8 + 2: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 2, 0, 2>(a, s); return 2;
+    case 1 * 8 + 4: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 4, 0, 2>(a, s); return 4;
     default: return 0;
   }
 }
