@@ -313,7 +313,9 @@ int32_t h3_token_reduce(int32_t direction, const h3_geom *geom, int32_t d_model,
 
 /* ------------------------------------------------------------------------------------
  * Single operations of the path (the same kernels the block uses), for callers that
- * compose their own block and for per-operation testing.
+ * compose their own block and for per-operation testing.  A row, token, head or column
+ * count of zero is an error (H3_ESHAPE, nothing launched), not an empty no-op; only
+ * h3_euler_step takes n_elems = 0 (returns H3_OK without a launch).
  * ---------------------------------------------------------------------------------- */
 
 enum { H3_EPI_NONE = 0, H3_EPI_GELU = 1 };

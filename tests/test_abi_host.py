@@ -181,6 +181,34 @@ def test_entry_points_reject_bad_arguments_without_launching(lib):
     assert b"alias" in L.h3_last_error()
 
 
+def test_zero_sizes_are_shape_errors_without_launching(lib):
+    # every sized entry point rejects an empty input on the host (H3_ESHAPE, no launch) and
+    # names the offending size; the Euler transition alone takes n_elems = 0 as a no-op.
+    # 16 stands for an aligned device address that is never dereferenced.
+    L, p, E = B.lib(), 16, B.H3_ESHAPE
+
+    def shape_error(rc, *words):
+        assert rc == E
+        msg = L.h3_last_error().decode()
+        for w in words:
+            assert w in msg, msg
+
+    for M, N in ((0, 64), (64, 0)):
+        shape_error(L.h3_gemm_bf16(p, 64, p, 64, p, 64, M, N, 64, None, None, 0, 0, None), "M,N >= 1")
+        shape_error(L.h3_gemm_i8(p, p, p, p, p, p, 128, M, N, 128, 128, 0, None), "M, N >= 1")
+    for nq, nk, h in ((0, 64, 1), (64, 0, 1), (64, 64, 0)):
+        shape_error(L.h3_attention(p, 128, p, 128, p, 128, p, 128, nq, nk, h, 128, None), "n_q, n_k >= 1")
+    shape_error(L.h3_quant_rows(p, p, p, 0, 512, 512, None), "rows >= 1")
+    shape_error(L.h3_gate_adaln(p, None, None, None, p, p, p, 0, 512, None), "rows")
+    shape_error(L.h3_gate_adaln(p, p, p, p, None, None, None, 0, 512, None), "rows")
+    shape_error(L.h3_gate_adaln_quant(p, None, None, None, p, p, p, p, 0, 512, None), "rows")
+    shape_error(L.h3_qk_norm_rope(p, 1024, 0, 512, 128, None, None, 0, p, None), "n_tokens >= 1")
+    for a_q8, K, lda in ((0, 64, 64), (1, 128, 128)):
+        shape_error(L.h3_qkv_gemm(p, lda, p, p, lda, p, p, p, 2048, 0, 512, K, 128, None, None, 0,
+                                  p, a_q8, 1, None, None), "M >= 1")
+    assert L.h3_euler_step(p, p, 1.0, 0.5, 0, None) == B.H3_OK
+
+
 def test_864x480_geometry_and_odd_width_pairing(lib):
     # 864x480 output at 22 frames: a 15 x 27 token grid (odd width) of 6 latent frames
     from video_diffusion_transformer_fwd_amd.runtime import Geometry

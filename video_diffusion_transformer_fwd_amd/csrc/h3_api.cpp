@@ -716,7 +716,7 @@ int32_t h3_attention(const void *Q, int64_t ldq, const void *K, int64_t ldk, con
                      int32_t head_dim, void *stream) {
   if (!Q || !K || !V || !O) return fail(H3_EINVAL, "h3_attention: NULL pointer");
   if (head_dim != 64 && head_dim != 128) return fail(H3_EUNSUPPORTED, "h3_attention: head_dim must be 64 or 128");
-  if (n_q < 1 || n_k < 1 || n_heads < 1 || n_heads > 65535) return fail(H3_ESHAPE, "h3_attention: bad sizes");
+  if (n_q < 1 || n_k < 1 || n_heads < 1 || n_heads > 65535) return fail(H3_ESHAPE, "h3_attention: need n_q, n_k >= 1 and 1 <= n_heads <= 65535");
   const int64_t w = static_cast<int64_t>(n_heads) * head_dim;
   if (ldq < w || ldk < w || ldv < w || ldo < w || ldq % 8 || ldk % 8 || ldv % 8 || ldo % 8)
     return fail(H3_ESHAPE, "h3_attention: strides too small or not multiples of 8");
@@ -733,7 +733,7 @@ int32_t h3_quant_rows(const void *X, void *Q, float *S, int32_t rows, int32_t K,
   if (!X || !Q || !S) return fail(H3_EINVAL, "h3_quant_rows: NULL pointer");
   if (group != K && group != 1024) return fail(H3_EINVAL, "h3_quant_rows: group must be K or 1024");
   if (rows < 1 || K < 512 || K % 512 || (group == 1024 && K % 1024))
-    return fail(H3_ESHAPE, "h3_quant_rows: K must be a multiple of 512 (of 1024 with groups)");
+    return fail(H3_ESHAPE, "h3_quant_rows: need rows >= 1 and K a multiple of 512 (of 1024 with groups)");
   launch_quant_rows(reinterpret_cast<const bf16_t *>(X), reinterpret_cast<int8_t *>(Q), S, rows, K,
                     group, as_stream(stream));
   return check_launch("h3_quant_rows");
@@ -745,7 +745,7 @@ int32_t h3_gemm_i8(const void *QA, const float *SA, const void *QW, const float 
   if (!QA || !SA || !QW || !SW || !bias || !C) return fail(H3_EINVAL, "h3_gemm_i8: NULL pointer");
   if (group != K && group != 1024) return fail(H3_EINVAL, "h3_gemm_i8: group must be K or 1024");
   if (M < 1 || N < 1 || K < 128 || K % 128 || (group == 1024 && K % 1024))
-    return fail(H3_ESHAPE, "h3_gemm_i8: K must be a multiple of 128 (of 1024 with groups)");
+    return fail(H3_ESHAPE, "h3_gemm_i8: need M, N >= 1 and K a multiple of 128 (of 1024 with groups)");
   if (ldc < N) return fail(H3_ESHAPE, "h3_gemm_i8: ldc < N");
   if (epilogue != H3_EPI_NONE && epilogue != H3_EPI_GELU) return fail(H3_EINVAL, "h3_gemm_i8: bad epilogue");
   launch_gemm_i8(reinterpret_cast<const int8_t *>(QA), SA, reinterpret_cast<const int8_t *>(QW), SW,
@@ -798,7 +798,7 @@ int32_t h3_qk_norm_rope(void *qkvq, int64_t ld, int32_t n_tokens, int32_t d_mode
     return fail(H3_EINVAL, "h3_qk_norm_rope: NULL pointer");
   if (head_dim != 64 && head_dim != 128) return fail(H3_EUNSUPPORTED, "h3_qk_norm_rope: head_dim must be 64 or 128");
   if (n_tokens < 1 || d_model < 512 || d_model % 512 || d_model % head_dim)
-    return fail(H3_ESHAPE, "h3_qk_norm_rope: d_model must be a multiple of 512 and of head_dim");
+    return fail(H3_ESHAPE, "h3_qk_norm_rope: need n_tokens >= 1 and d_model a multiple of 512 and of head_dim");
   if (ld < 2 * d_model || ld % 8) return fail(H3_ESHAPE, "h3_qk_norm_rope: ld too small or not a multiple of 8");
   launch_qk_norm_rope(reinterpret_cast<bf16_t *>(qkvq), ld, n_tokens, d_model, head_dim,
                       reinterpret_cast<const bf16_t *>(q_gamma), reinterpret_cast<const bf16_t *>(k_gamma),
