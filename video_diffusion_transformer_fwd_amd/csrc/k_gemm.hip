@@ -21,13 +21,15 @@
 // Tile shapes are chosen per problem by plan_gemm (measured on random bf16 operands): 384x192
 // tiles (8 waves of 96x96, two per SIMD, two LDS stages) for the wide QKV / FC1 products,
 // 256x256 tiles with 8 waves of 128x64 for the narrow products at large M, and 192x192 tiles
-// (4 waves, three LDS stages) with K split in two for the narrow (N = d) products of the
-// 1536-token workload and in four at 768 tokens.
+// (three LDS stages) with K split in two for the narrow (N = d) products of the 1536-token
+// workload and in four at 768 tokens, run by 8 waves in two K-step groups (KSG below).
 //
 // Split-K (S pieces of K per tile in separate workgroups): each piece stores its float32 partial
 // tile with plain stores; a second launch sums the S partials in piece order 0..S-1 and applies
-// the epilogue, so the result is deterministic and no device-scope fence (which would write
-// back and invalidate L2 under every workgroup) is needed.
+// the epilogue (for the block's out-projection and FC2 that launch is the gated-residual kernel
+// that consumes the product, with the same sum), so the result is deterministic and no
+// device-scope fence (which would write back and invalidate L2 under every workgroup) is
+// needed.
 //
 // Workgroup order is XCD-aware: consecutive hardware ids land on different XCDs, so ids are
 // regrouped so that each XCD walks a contiguous band of tiles, visited in groups of 8 tile
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
   constexpr int NT = Cfg::NT * KSG, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
   constexpr int KS_PER = BK / 16 / KSG;  // K steps per slice and wave
   static_assert(KSG == 1 || WM * WN * TM * TN * 16 * 64 * 4 <= Cfg::LDS_BYTES,
-                "the accumulator hand-over must fit the LDS"); 
+                "the accumulator hand-over must fit the LDS");
   // static (its address is known when the kernel is compiled, so the constant parts of the
   // fragment addresses fold into the LDS instructions' offsets)
   __shared__ __align__(16) unsigned char smem[Cfg::LDS_BYTES];
