@@ -107,8 +107,8 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus N > 1 is not "
-                                   "supported (the multi-GPU sequence split is a design note)"}))
+        print(json.dumps({"error": "runs on one GPU only: --gpus N > 1 is not supported (the "
+                                   "multi-GPU sequence split is designed, not implemented)"}))
         sys.exit(2)
     import torch
     from video_diffusion_transformer_fwd_amd import binding as B
