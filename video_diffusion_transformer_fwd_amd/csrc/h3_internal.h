@@ -262,11 +262,11 @@ WsPlan plan_workspace(const Model &m, int32_t n_tokens, const h3_run_opts &o);
 
 // ---------------------------------------------------------------- kernel launchers
 // All launchers assume validated arguments and enqueue on `s`.
-// Tile configuration and split-K choice of a bf16 product; part_bytes is the float32 partial
-// buffer [split][M][N] a split-K launch needs.
+// Tile configuration and split-K choice of a bf16 or int8 product; part_bytes is the float32
+// (int32 for int8) partial buffer [split][M][N] a split-K launch needs.
 struct GemmPlan {
-  int cfg;    // 0: 128x128, 1: 192x192, 2: 256x256, 3: 128x256, 4: 384x192 output tiles
-  int split;  // pieces of K in separate workgroups (1, 2, 3 or 4)
+  int cfg;    // 0: 128x128, 1: 192x192, 2: 256x256, 3: 128x256 (int8 grouped only), 4: 384x192
+  int split;  // pieces of K in separate workgroups (1, 2 or 4)
   size_t part_bytes;
 };
 GemmPlan plan_gemm(int M, int N, int K);

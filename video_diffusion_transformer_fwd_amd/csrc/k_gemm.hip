@@ -500,7 +500,6 @@ void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
     case 1 * 8 + 1: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
     case 1 * 8 + 2: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s); break;
     case 1 * 8 + 4: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 4>(a, s); break;
-    case 3 * 8 + 1: run_product<128, 256, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
     default: run_product<128, 128, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
   }
 }
@@ -532,10 +531,7 @@ GemmPlan plan_gemm(int M, int N, int K) {
     p.cfg = 1;
     p.split = 4;
   }
-  if (p.split > 1 && (K % (64 * p.split) != 0 || N % 4 != 0 || K / p.split < 1024)) {
-    p.split = 1;
-    if (p.cfg == 2 && M < 4096) p.cfg = 3;
-  }
+  if (p.split > 1 && (K % (64 * p.split) != 0 || N % 4 != 0 || K / p.split < 1024)) p.split = 1;
   if (p.split > 1) p.part_bytes = static_cast<size_t>(p.split) * M * N * sizeof(float);
   return p;
 }
@@ -556,10 +552,8 @@ void launch_gemm_bf16(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb
                       int64_t ldc, int M, int N, int K, const bf16_t *bias, const bf16_t *bias2,
                       int epilogue, int out_f32, hipStream_t s, const SplitScratch &sc) {
   GemmPlan p = plan_gemm(M, N, K);
-  if (p.split > 1 && (!sc.part || p.part_bytes > sc.part_bytes)) {
+  if (p.split > 1 && (!sc.part || p.part_bytes > sc.part_bytes))
     p.split = 1;  // no split-K scratch: run the whole K per tile
-    if (p.cfg == 2 && M < 4096) p.cfg = 3;
-  }
   GemmArgs a{A, lda, B, ldb, C, ldc, M, N, K, bias, bias2, sc.part};
   if (out_f32)
     gemm_dispatch<H3_EPI_NONE, 1>(p, a, s);
@@ -576,7 +570,6 @@ void qkv_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
     case 4: run_gemm<384, 192, 4, 2, 2, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
     case 2: run_gemm<256, 256, 2, 4, 2, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
     case 1: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
-    case 3: run_gemm<128, 256, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
     default: run_gemm<128, 128, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
   }
 }
