@@ -14,8 +14,6 @@ Distributions (the workloads' description: weights N(0, 0.02) in bf16, latent N(
 """
 from __future__ import annotations
 
-import concurrent.futures as cf
-import os
 from dataclasses import dataclass, field
 
 import torch
@@ -173,33 +171,3 @@ def latent(w: Workload, n_tokens: int, seed: int = 0) -> torch.Tensor:
 def context(w: Workload, seed: int = 0) -> torch.Tensor:
     """Text context [L_ctx, d] bf16, N(0, 1)."""
     return normal("context", (w.ctx_len, w.d_model), 1.0, seed=seed)
-
-
-def all_block_weights(w: Workload, seed: int = 0, workers: int | None = None, sink=None):
-    """Draw every block's tensors in parallel threads.
-
-    ``sink(b, name, tensor)`` receives each tensor as soon as it is drawn (e.g. to copy it
-    to the GPU and drop the CPU copy); without a sink a list of per-block dicts is returned.
-    """
-    workers = workers or min(16, max(1, len(os.sched_getaffinity(0))))
-    jobs = [(b, name) for b in range(w.n_blocks) for name in _BLOCK]
-    result = [dict() for _ in range(w.n_blocks)]
-
-    def work(job):
-        b, name = job
-        t = block_tensor(w, b, name, seed)
-        if sink is not None:
-            sink(b, name, t)
-            return None
-        result[b][name] = t
-        return None
-
-    prev = torch.get_num_threads()
-    torch.set_num_threads(1)
-    try:
-        with cf.ThreadPoolExecutor(workers) as ex:
-            for _ in ex.map(work, jobs):
-                pass
-    finally:
-        torch.set_num_threads(prev)
-    return None if sink is not None else result
