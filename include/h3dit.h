@@ -169,7 +169,9 @@ typedef struct h3_block_weights {
 typedef struct h3_model h3_model;
 
 /* Copies the dims and pointer tables (not the tensors, which stay caller-owned and must
- * outlive the model).  H3_EINVAL on NULL weights, H3_ESHAPE on unsupported dims. */
+ * outlive the model).  H3_EINVAL on NULL weights, H3_ESHAPE on unsupported dims (also when
+ * the FFN weight [F, d] or the context [L_ctx, d], bf16, spans 4 GiB or more: the products
+ * address each operand through 32-bit byte offsets). */
 int32_t h3_model_create(const h3_dims *dims, const h3_global_weights *g,
                         const h3_block_weights *blocks, int32_t n_blocks, h3_model **out);
 void h3_model_destroy(h3_model *m);
@@ -212,7 +214,9 @@ typedef struct h3_run_opts {
 int32_t h3_geom_tokens(const h3_geom *geom, int32_t *n_tokens);
 
 /* Bytes of workspace h3_dit_block_fwd / h3_dit_forward / h3_modulation /
- * h3_prepare_context need for n_tokens full-resolution tokens and these options. */
+ * h3_prepare_context need for n_tokens full-resolution tokens and these options.  Token
+ * counts whose FC2 input [n_tokens, F] (bf16) spans 4 GiB or more are refused (H3_ESHAPE),
+ * here and by the block and forward calls. */
 int32_t h3_workspace_size(const h3_model *m, int32_t n_tokens, const h3_run_opts *o,
                           size_t *bytes);
 
@@ -324,7 +328,8 @@ enum { H3_EPI_NONE = 0, H3_EPI_GELU = 1 };
  * [M, K], row stride lda elements), B (device, bf16 [N, K], row stride ldb), bias / bias2
  * (device, bf16 [N] or NULL).  out_f32 = 0: C bf16 [M, N] (stride ldc), epilogue
  * H3_EPI_GELU applies exact-erf GELU after the bias; out_f32 = 1: C float [M, N].
- * K % 64 == 0, M, N >= 1, strides >= row widths and multiples of 8. */
+ * K % 64 == 0, M, N >= 1, strides >= row widths and multiples of 8, and each operand
+ * ((rows - 1) * ld + K elements) under 4 GiB (H3_ESHAPE otherwise). */
 int32_t h3_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
                      int64_t ldc, int32_t M, int32_t N, int32_t K, const void *bias,
                      const void *bias2, int32_t epilogue, int32_t out_f32, void *stream);
@@ -349,8 +354,9 @@ int32_t h3_quant_rows(const void *X, void *Q, float *S, int32_t rows, int32_t K,
  * float(acc_g) * SA[r,g]) * SW[n]) + bias[n]), groups ascending, each float operation
  * rounded (no fused multiply-add).  QA int8 [M, K], QW int8 [N, K], SA float [M, K/group],
  * SW float [N], bias bf16 [N], C bf16 [M, ldc].  group = K (K % 128 == 0) or 1024
- * (K % 1024 == 0).  epilogue: H3_EPI_NONE, or H3_EPI_GELU (exact-erf GELU of the dequantised value before the
- * bf16 rounding: the int8 FC1 of P3 "the int8 path"). */
+ * (K % 1024 == 0); QA and QW each under 4 GiB.  epilogue: H3_EPI_NONE, or H3_EPI_GELU
+ * (exact-erf GELU of the dequantised value before the bf16 rounding: the int8 FC1 of P3 "the
+ * int8 path"). */
 int32_t h3_gemm_i8(const void *QA, const float *SA, const void *QW, const float *SW,
                    const void *bias, void *C, int64_t ldc, int32_t M, int32_t N, int32_t K,
                    int32_t group, int32_t epilogue, void *stream);
@@ -403,7 +409,7 @@ int32_t h3_qk_norm_rope(void *qkvq, int64_t ld, int32_t n_tokens, int32_t d_mode
  * epilogue when its tiling allows it (not for tiles that split K, nor for a C or table that is
  * not 16-byte aligned; *fused_used, if not NULL, says which ran); fused = 0, or no fused form: the product, then h3_qk_norm_rope.  The two are
  * bit-identical.  Errors: H3_EINVAL (NULL pointers, flags), H3_EUNSUPPORTED (head_dim not 64
- * or 128), H3_ESHAPE (sizes, strides). */
+ * or 128), H3_ESHAPE (sizes, strides, an A or W operand of 4 GiB or more). */
 int32_t h3_qkv_gemm(const void *A, int64_t lda, const float *SA, const void *W, int64_t ldw,
                     const float *SW, const void *bias, void *C, int64_t ldc, int32_t M,
                     int32_t d_model, int32_t K, int32_t head_dim, const void *q_gamma,

@@ -158,6 +158,43 @@ def test_model_create_validates_before_any_launch(lib):
     assert e.value.code == B.H3_EINVAL
 
 
+def test_operands_of_4_gib_or_more_are_refused(lib):
+    # the products copy operand tiles through 32-bit byte offsets from each operand's base, so
+    # an operand ((rows - 1) * ld + K elements) must stay under 4 GiB; the entry points refuse
+    # larger ones on the host, at exactly the boundary
+    L, p, E = B.lib(), 16, B.H3_ESHAPE
+    # bf16 product: A rows at stride 2^15 elements; 2^16 + 1 rows reach 2^32 + 128 bytes
+    assert L.h3_gemm_bf16(p, 1 << 15, p, 64, p, 64, (1 << 16) + 1, 64, 64, None, None, 0, 0, None) == E
+    assert b"4 GiB" in L.h3_last_error()
+    assert L.h3_gemm_bf16(p, 64, p, 1 << 15, p, (1 << 17) + 8, 64, (1 << 16) + 1, 64, None, None,
+                          0, 0, None) == E
+    # int8 product: M * K bytes with K = 1024 reaches 2^32 at M = 2^22
+    assert L.h3_gemm_i8(p, p, p, p, p, p, 128, 1 << 22, 128, 1024, 1024, 0, None) == E
+    assert b"4 GiB" in L.h3_last_error()
+    # QKV product (bf16 A at stride 2^15)
+    assert L.h3_qkv_gemm(p, 1 << 15, None, p, 64, None, p, p, 2048, (1 << 16) + 1, 512, 64, 128,
+                         None, None, 0, p, 0, 1, None, None) == E
+    assert b"4 GiB" in L.h3_last_error()
+    g = B.h3_global_weights(*[1 + i for i in range(len(B.GLOBAL_FIELDS))])  # never dereferenced
+    blk = B.h3_block_weights(*([64] * 15 + [None, None]))
+    for bad in [B.h3_dims(512, 8, 1 << 22, 32, 128, 2), B.h3_dims(512, 8, 2048, 1 << 22, 128, 2)]:
+        with pytest.raises(B.H3Error) as e:
+            B.h3_model_create(bad, g, [blk, blk])
+        assert e.value.code == E and "4 GiB" in str(e.value)
+    # tokens: the FC2 input [n, 2048] bf16 reaches 2^32 bytes at n = 2^20
+    m = B.h3_model_create(B.h3_dims(512, 8, 2048, 32, 128, 2), g, [blk, blk])
+    opts = B.make_opts()
+    assert B.h3_workspace_size(m, (1 << 20) - 1, opts) > 0
+    for n in (1 << 20, (1 << 31) - 1):
+        with pytest.raises(B.H3Error) as e:
+            B.h3_workspace_size(m, n, opts)
+        assert e.value.code == E and "4 GiB" in str(e.value)
+        with pytest.raises(B.H3Error) as e:
+            B.h3_workspace_layout(m, n, opts)
+        assert e.value.code == E
+    B.h3_model_destroy(m)
+
+
 def test_entry_points_reject_bad_arguments_without_launching(lib):
     # all of these fail validation on the host, before any device call
     L = B.lib()

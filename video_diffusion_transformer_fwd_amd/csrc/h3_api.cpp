@@ -18,6 +18,12 @@ namespace {
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
+// The products copy their operand tiles through 32-bit byte offsets from the operand's base:
+// a [rows, K] operand at row stride ld (elements of esize bytes) must span less than 4 GiB.
+bool fits_u32(int64_t rows, int64_t ld, int64_t K, int64_t esize) {
+  return ((rows - 1) * ld + K) * esize < (int64_t{1} << 32);
+}
+
 bool supported_width(int d) {
   const int v = d / 512;
   return d % 512 == 0 && (v == 1 || v == 2 || v == 3 || v == 4 || v == 5 || v == 6 || v == 8 ||
@@ -106,6 +112,16 @@ namespace {
 
 int32_t validate_model(const h3_model *m) {
   if (!m) return fail(H3_EINVAL, "model is NULL");
+  return H3_OK;
+}
+
+// Token counts of a block: its largest activation operands are the FC2 input [n, ffn_dim] and
+// the out-projection input [n, 2 d_model] (bf16), each addressed within 4 GiB.
+int32_t check_tokens(const h3_model *m, int32_t n, const char *who) {
+  if (n < 1) return fail(H3_ESHAPE, std::string(who) + ": n_tokens must be >= 1");
+  const int64_t f = m->dims.ffn_dim, d2 = 2 * static_cast<int64_t>(m->dims.d_model);
+  if (!fits_u32(n, f, f, 2) || !fits_u32(n, d2, d2, 2))
+    return fail(H3_ESHAPE, std::string(who) + ": n_tokens x ffn_dim spans 4 GiB or more");
   return H3_OK;
 }
 
@@ -336,6 +352,8 @@ int32_t h3_model_create(const h3_dims *dims, const h3_global_weights *g,
   if (dm.ffn_dim < 1024 || dm.ffn_dim % 1024)
     return fail(H3_ESHAPE, "h3_model_create: ffn_dim must be a positive multiple of 1024");
   if (dm.ctx_len < 1) return fail(H3_ESHAPE, "h3_model_create: ctx_len must be >= 1");
+  if (!fits_u32(dm.ffn_dim, dm.d_model, dm.d_model, 2) || !fits_u32(dm.ctx_len, dm.d_model, dm.d_model, 2))
+    return fail(H3_ESHAPE, "h3_model_create: ffn_dim x d_model or ctx_len x d_model spans 4 GiB or more");
   if (dm.latent_ch < 64 || dm.latent_ch % 64)
     return fail(H3_ESHAPE, "h3_model_create: latent_ch must be a positive multiple of 64");
   const void *gp[] = {g->t1_w, g->t1_b, g->t2_w, g->t2_b, g->mod_w, g->mod_b, g->fin_w,
@@ -377,7 +395,7 @@ int32_t h3_workspace_size(const h3_model *m, int32_t n_tokens, const h3_run_opts
   if (int32_t e = validate_model(m)) return e;
   if (int32_t e = check_opts(o)) return e;
   if (!bytes) return fail(H3_EINVAL, "h3_workspace_size: bytes is NULL");
-  if (n_tokens < 1) return fail(H3_ESHAPE, "h3_workspace_size: n_tokens must be >= 1");
+  if (int32_t e = check_tokens(m, n_tokens, "h3_workspace_size")) return e;
   *bytes = plan_workspace(*m, n_tokens, *o).total;
   return H3_OK;
 }
@@ -387,7 +405,7 @@ int32_t h3_workspace_layout(const h3_model *m, int32_t n_tokens, const h3_run_op
   if (int32_t e = validate_model(m)) return e;
   if (int32_t e = check_opts(o)) return e;
   if (!layout) return fail(H3_EINVAL, "h3_workspace_layout: layout is NULL");
-  if (n_tokens < 1) return fail(H3_ESHAPE, "h3_workspace_layout: n_tokens must be >= 1");
+  if (int32_t e = check_tokens(m, n_tokens, "h3_workspace_layout")) return e;
   const WsPlan p = plan_workspace(*m, n_tokens, *o);
   layout->n1 = p.n1; layout->qkvq = p.qkvq; layout->attn = p.attn; layout->y = p.y;
   layout->n2 = p.n2; layout->h = p.h; layout->m = p.m; layout->hq = p.hq; layout->hs = p.hs;
@@ -469,6 +487,7 @@ int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
   if (block < 0 || block >= m->dims.n_blocks) return fail(H3_EINVAL, "h3_dit_block_fwd: bad block index");
   int32_t n = 0;
   if (int32_t e = h3_geom_tokens(geom, &n)) return e;
+  if (int32_t e = check_tokens(m, n, "h3_dit_block_fwd")) return e;
   if (!x || !mod || !ctx_kv) return fail(H3_EINVAL, "h3_dit_block_fwd: NULL x, mod or ctx_kv");
   if (n1_next && !mod_next) return fail(H3_EINVAL, "h3_dit_block_fwd: n1_next needs mod_next");
   if (int32_t e = check_block_int8(m->blocks[block], *o, "h3_dit_block_fwd")) return e;
@@ -501,6 +520,7 @@ static int32_t forward_impl(const h3_model *m, const h3_geom *geom, const h3_run
   if (!geom || geom->paired) return fail(H3_EINVAL, "h3_dit_forward: geom must be the full grid");
   int32_t n = 0;
   if (int32_t e = h3_geom_tokens(geom, &n)) return e;
+  if (int32_t e = check_tokens(m, n, "h3_dit_forward")) return e;
   if (!latent || !velocity || !active || !ctx_kv) return fail(H3_EINVAL, "h3_dit_forward: NULL pointer");
   if (!std::isfinite(sigma)) return fail(H3_EINVAL, "h3_dit_forward: sigma must be finite");
   const int nb = m->dims.n_blocks;
@@ -703,6 +723,8 @@ int32_t h3_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, voi
   if (M < 1 || N < 1 || K < 64 || K % 64) return fail(H3_ESHAPE, "h3_gemm_bf16: need M,N >= 1 and K % 64 == 0");
   if (lda < K || ldb < K || ldc < N || lda % 8 || ldb % 8)
     return fail(H3_ESHAPE, "h3_gemm_bf16: strides too small or not multiples of 8");
+  if (!fits_u32(M, lda, K, 2) || !fits_u32(N, ldb, K, 2))
+    return fail(H3_ESHAPE, "h3_gemm_bf16: an operand spans 4 GiB or more");
   if (epilogue != H3_EPI_NONE && epilogue != H3_EPI_GELU) return fail(H3_EINVAL, "h3_gemm_bf16: bad epilogue");
   if (out_f32 && epilogue != H3_EPI_NONE) return fail(H3_EUNSUPPORTED, "h3_gemm_bf16: GELU with float output");
   launch_gemm_bf16(reinterpret_cast<const bf16_t *>(A), lda, reinterpret_cast<const bf16_t *>(B), ldb,
@@ -747,6 +769,8 @@ int32_t h3_gemm_i8(const void *QA, const float *SA, const void *QW, const float 
   if (M < 1 || N < 1 || K < 128 || K % 128 || (group == 1024 && K % 1024))
     return fail(H3_ESHAPE, "h3_gemm_i8: need M, N >= 1 and K a multiple of 128 (of 1024 with groups)");
   if (ldc < N) return fail(H3_ESHAPE, "h3_gemm_i8: ldc < N");
+  if (!fits_u32(M, K, K, 1) || !fits_u32(N, K, K, 1))
+    return fail(H3_ESHAPE, "h3_gemm_i8: an operand spans 4 GiB or more");
   if (epilogue != H3_EPI_NONE && epilogue != H3_EPI_GELU) return fail(H3_EINVAL, "h3_gemm_i8: bad epilogue");
   launch_gemm_i8(reinterpret_cast<const int8_t *>(QA), SA, reinterpret_cast<const int8_t *>(QW), SW,
                  reinterpret_cast<const bf16_t *>(bias), reinterpret_cast<bf16_t *>(C), ldc, M, N, K,
@@ -826,6 +850,8 @@ int32_t h3_qkv_gemm(const void *A, int64_t lda, const float *SA, const void *W, 
     if (K < 64 || K % 64 || lda < K || ldw < K || lda % 8 || ldw % 8)
       return fail(H3_ESHAPE, "h3_qkv_gemm: need K % 64 == 0, lda, ldw >= K and multiples of 8");
   }
+  if (!fits_u32(M, lda, K, a_q8 ? 1 : 2) || !fits_u32(4 * static_cast<int64_t>(d_model), ldw, K, a_q8 ? 1 : 2))
+    return fail(H3_ESHAPE, "h3_qkv_gemm: an operand spans 4 GiB or more");
   const hipStream_t s = as_stream(stream);
   const QkEpi qe{reinterpret_cast<const bf16_t *>(q_gamma), reinterpret_cast<const bf16_t *>(k_gamma),
                  reinterpret_cast<const float2 *>(table), d_model, qk_norm};
