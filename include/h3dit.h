@@ -113,7 +113,8 @@ int32_t h3_select_layers(const uint16_t *mod_table, int32_t n_blocks, int32_t d_
  * (= before the head).  Reduced token j of row (f, h) pairs full tokens at columns 2j and
  * 2j+1 (an odd last column pairs with itself).  pairs (host, int32[2 * n_reduced], may be
  * NULL) receives (src0, src1) per reduced token; *n_reduced = f_lat*grid_h*ceil(grid_w/2).
- * n_active > 3, all sizes >= 1, else H3_EINVAL. */
+ * n_active > 3, all sizes >= 1, else H3_EINVAL; more than 2^24 full-grid tokens: H3_ESHAPE
+ * (the cap of h3_geom_tokens). */
 int32_t h3_token_plan(int32_t f_lat, int32_t grid_h, int32_t grid_w, int32_t eval_index,
                       int32_t n_active, int32_t *merge_after, int32_t *restore_before,
                       int32_t *pairs, int32_t *n_reduced);

@@ -125,6 +125,17 @@ def test_geometry_validation(lib):
     assert B.h3_geom_tokens(B.make_geom(6, 16, 16, 1.0, 1)) == 768
     assert B.h3_geom_tokens(B.make_geom(61, 24, 42, 1.0)) == 61488
     assert B.h3_geom_tokens(B.make_geom(1, 15, 27, 1.0, 1)) == 15 * 14
+    # the largest widths: paired columns are counted without int32 overflow
+    for paired in (0, 1):
+        with pytest.raises(B.H3Error) as e:
+            B.h3_geom_tokens(B.make_geom(1, 1, 2 ** 31 - 1, 1.0, paired))
+        assert e.value.code == B.H3_ESHAPE
+    assert B.h3_geom_tokens(B.make_geom(1, 1, 2 ** 25, 1.0, 1)) == 2 ** 24
+    L = B.lib()
+    out = [ctypes.c_int32() for _ in range(3)]
+    for f, h, w in ((1, 1, 2 ** 31 - 1), (2 ** 10, 2 ** 10, 2 ** 10)):
+        assert L.h3_token_plan(f, h, w, 0, 45, *[ctypes.byref(o) for o in out[:2]], None,
+                               ctypes.byref(out[2])) == B.H3_ESHAPE
     for bad in [B.make_geom(0, 8, 8, 1.0), B.make_geom(2, 8, 8, 0.3), B.make_geom(2, 8, 8, 1.0, 2)]:
         with pytest.raises(B.H3Error):
             B.h3_geom_tokens(bad)

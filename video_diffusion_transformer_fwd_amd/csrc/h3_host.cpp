@@ -145,6 +145,8 @@ int32_t h3_token_plan(int32_t f_lat, int32_t grid_h, int32_t grid_w, int32_t eva
     return fail(H3_EINVAL, "h3_token_plan: NULL output");
   if (f_lat < 1 || grid_h < 1 || grid_w < 1 || eval_index < 0)
     return fail(H3_EINVAL, "h3_token_plan: bad geometry");
+  if (static_cast<int64_t>(f_lat) * grid_h * grid_w > (1 << 24))
+    return fail(H3_ESHAPE, "h3_token_plan: too many tokens");  // the cap of h3_geom_tokens
   if (n_active <= 3) return fail(H3_EINVAL, "h3_token_plan: needs more than 3 active blocks");
   *merge_after = 3;
   int32_t r = eval_index < 10 ? 40 : 30;
@@ -173,7 +175,7 @@ int32_t h3_geom_tokens(const h3_geom *geom, int32_t *n_tokens) {
     return fail(H3_EINVAL, "h3_geom_tokens: rope_spatial_scale must be 1 or 0.5");
   if (geom->paired != 0 && geom->paired != 1)
     return fail(H3_EINVAL, "h3_geom_tokens: paired must be 0 or 1");
-  int64_t w = geom->paired ? (geom->grid_w + 1) / 2 : geom->grid_w;
+  const int64_t w = geom->paired ? (static_cast<int64_t>(geom->grid_w) + 1) / 2 : geom->grid_w;
   int64_t n = static_cast<int64_t>(geom->f_lat) * geom->grid_h * w;
   if (n > (1 << 24)) return fail(H3_ESHAPE, "h3_geom_tokens: too many tokens");
   *n_tokens = static_cast<int32_t>(n);
