@@ -91,8 +91,8 @@ int32_t h3_token_grid(int32_t width, int32_t height, int32_t reference_rope,
  *   fresh  (host, uint8[steps]): 1 iff i % r == 0 or i == steps - 1, r = reuse, or
  *          core_reuse when that is > 1 (then: the steps whose core runs fresh).
  *   n_fresh: number of fresh evaluations (of the core, with core_reuse > 1).
- * steps >= 1, reuse >= 1, 1 <= core_reuse <= 6 (H3_EINVAL); reuse > 1 with core_reuse > 1
- * is H3_EINVAL. */
+ * 1 <= steps <= 2^20, reuse >= 1, 1 <= core_reuse <= 6 (H3_EINVAL); reuse > 1 with
+ * core_reuse > 1 is H3_EINVAL. */
 int32_t h3_schedule(int32_t steps, int32_t reuse, int32_t core_reuse, float *sigmas,
                     uint8_t *fresh, int32_t *n_fresh);
 

@@ -91,6 +91,12 @@ def test_schedule_matches_oracle_bit_exact(lib):
     with pytest.raises(B.H3Error) as e:
         B.h3_schedule(20, 1, 7)
     assert e.value.code == B.H3_EINVAL
+    # the longest schedule is accepted; one step more is refused
+    sig, fresh, nf = B.h3_schedule(1 << 20, 1, 1)
+    assert nf == 1 << 20 and sig[0] == 1.0 and sig[-1] == 0.0 and sig[1 << 19] == 0.5
+    with pytest.raises(B.H3Error) as e:
+        B.h3_schedule((1 << 20) + 1, 1, 1)
+    assert e.value.code == B.H3_EINVAL
 
 
 def test_select_layers_matches_oracle_on_synthetic_tables(lib):

@@ -86,6 +86,7 @@ int32_t h3_schedule(int32_t steps, int32_t reuse, int32_t core_reuse, float *sig
   if (reuse > 1 && core_reuse > 1)
     return fail(H3_EINVAL, "h3_schedule: --reuse and --core-reuse are mutually exclusive");
   if (core_reuse > 6) return fail(H3_EINVAL, "h3_schedule: core_reuse must be at most 6");
+  if (steps > (1 << 20)) return fail(H3_EINVAL, "h3_schedule: steps must be at most 2^20");
   const float n = static_cast<float>(steps);
   for (int32_t i = 0; i <= steps; ++i) sigmas[i] = static_cast<float>(steps - i) / n;
   // whole-velocity reuse (reuse > 1) or core-residual reuse (core_reuse > 1): the same rule
