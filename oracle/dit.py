@@ -233,12 +233,23 @@ def quantize_weight(w):
 
 
 def int8_accumulate(qa, qw, group=None):
-    """Exact integer products per K group: acc[g, r, n] = sum_{k in g} qa[r,k] qw[n,k] (int64)."""
+    """Exact integer products per K group: acc[g, r, n] = sum_{k in g} qa[r,k] qw[n,k] (int64).
+
+    Each group's sum is one float64 matrix product.  It is exact: every product of two codes
+    in [-127, 127] and every partial sum of at most 2^39 of them is an integer below 2^53 in
+    magnitude, so no addition rounds, whatever order the product sums in.
+    """
     r, k = qa.shape
     g = k if group is None else group
-    a = qa.astype(np.int64).reshape(r, k // g, g)
-    w = qw.astype(np.int64).reshape(qw.shape[0], k // g, g)
-    return np.einsum("rgk,ngk->grn", a, w)
+    if k > (1 << 39):
+        raise ValueError("K too large for an exact float64 sum")
+    a = qa.astype(np.float64)
+    w = qw.astype(np.float64)
+    out = np.empty((k // g, r, qw.shape[0]), dtype=np.int64)
+    for gi in range(k // g):
+        sl = slice(gi * g, (gi + 1) * g)
+        out[gi] = (a[:, sl] @ w[:, sl].T).astype(np.int64)
+    return out
 
 
 def dequant(acc, sa, sw, bias):
@@ -439,13 +450,15 @@ def euler_step(x, v, sigma_cur, sigma_next):
 
 
 def denoise(latent0, model, steps, reuse, active, geom, n_heads, qk_norm=True,
-            fc2_mode="bf16", token_reduction=False, int8_linear=False, core_reuse=1):
+            fc2_mode="bf16", token_reduction=False, int8_linear=False, core_reuse=1,
+            velocities=None):
     """The Euler loop: ``steps`` transitions, fresh evaluations per ``host.schedule``.
 
     Skipped steps reuse the last fresh velocity (P3 "aggressive levers": reuse extrapolates
     the skipped transitions).  With ``core_reuse`` > 1 every step evaluates the patch and the
     head and only the marked steps run the core (``dit_forward_cached``).  Returns (x_N,
-    number of fresh (core) evaluations).
+    number of fresh (core) evaluations).  ``velocities`` (a list), when given, receives the
+    velocity of every fresh evaluation in order.
     """
     sig, fresh = host.schedule(steps, reuse, core_reuse)
     x = np.asarray(latent0, dtype=np.float64)
@@ -460,5 +473,7 @@ def denoise(latent0, model, steps, reuse, active, geom, n_heads, qk_norm=True,
             v = dit_forward(x, model, float(sig[i]), active, geom, n_heads, ev, qk_norm,
                             fc2_mode, token_reduction, int8_linear=int8_linear)
             ev += 1
+            if velocities is not None:
+                velocities.append(v)
         x = euler_step(x, v, sig[i], sig[i + 1])
     return x, ev

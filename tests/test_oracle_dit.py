@@ -302,6 +302,26 @@ def test_int8_accumulate_exact():
     np.testing.assert_array_equal(full[0], acc.sum(0))
 
 
+def test_int8_accumulate_exact_at_the_extremes():
+    # the largest sums an FC2 row can reach (every code +-127 over 20480 channels) and sums
+    # that cancel to small values: integer brute force with Python ints
+    k = 20480
+    qa = np.full((2, k), 127, dtype=np.int8)
+    qa[1, ::2] = -127
+    qw = np.full((3, k), -127, dtype=np.int8)
+    qw[1] = 127
+    qw[2, 1::3] = 1
+    acc = dit.int8_accumulate(qa, qw, 1024)
+    for r in range(2):
+        for n in range(3):
+            for g in range(k // 1024):
+                ref = sum(int(qa[r, c]) * int(qw[n, c]) for c in range(1024 * g, 1024 * g + 1024))
+                assert acc[g, r, n] == ref
+    full = dit.int8_accumulate(qa, qw)
+    assert full[0, 0, 0] == -127 * 127 * k and full[0, 0, 1] == 127 * 127 * k
+    assert full.dtype == np.int64
+
+
 def test_dequant_fixed_order_float32():
     acc = RNG.integers(-10 ** 7, 10 ** 7, size=(3, 2, 4))
     sa = RNG.random(size=(2, 3)).astype(np.float32)
