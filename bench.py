@@ -69,36 +69,53 @@ def traffic_for(kernel_src: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float):
-    """Oracle (float64 NumPy) on a bounded sample: whole blocks of one fresh evaluation."""
-    import numpy as np
-    import threadpoolctl
-    from oracle import dit
-    from video_diffusion_transformer_fwd_amd import synthetic as S
-    from video_diffusion_transformer_fwd_amd.runtime import Geometry
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    geo = Geometry(w)
+
+def cpu_baseline(w, budget_s: float):
+    """Oracle (float64 NumPy) on a bounded sample: the first blocks of one fresh evaluation,
+    in order, until about ``budget_s`` seconds of oracle time are spent.  Geometry and active
+    list come from the oracle's own host logic."""
+    import threadpoolctl
+    from oracle import dit, host
+    from video_diffusion_transformer_fwd_amd import synthetic as S
+
+    f_lat = host.latent_frames(host.align_frames(w.frames))
+    gh, gw, scale = host.token_grid(w.width, w.height)
+    n = host.n_tokens(f_lat, gh, gw)
     to64 = lambda t: t.to("cpu").double().numpy()
     g = {k: to64(v) for k, v in S.global_weights(w).items()}
+    active = host.select_layers(g["mod_table"], w.n_active)
     ctx = to64(S.context(w))
     mod, _ = dit.modulation(g, 1.0)
-    coords = dit.rope_coords(geo.f_lat, geo.grid_h, geo.grid_w, geo.scale)
-    x = dit.patch_embed(to64(S.latent(w, geo.n_tokens)), g)
+    coords = dit.rope_coords(f_lat, gh, gw, scale)
+    x = dit.patch_embed(to64(S.latent(w, n)), g)
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
     done, t_used = 0, 0.0
-    while done < w.n_blocks:
-        blk = {k: to64(v) for k, v in S.block_weights(w, done).items()}
+    while done < len(active):
+        b = active[done]
+        blk = {k: to64(v) for k, v in S.block_weights(w, b).items()}
         t0 = time.perf_counter()
-        x = dit.block_forward(x, blk, mod[done], ctx, coords, w.n_heads)
+        x = dit.block_forward(x, blk, mod[b], ctx, coords, w.n_heads, fc2_mode=w.fc2_mode,
+                              int8_linear=w.int8_linear)
         t_used += time.perf_counter() - t0
         done += 1
         if t_used >= budget_s:
             break
-    return {"value": geo.n_tokens * done / t_used, "unit": "tokens*blocks/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} of the {w.n_blocks} blocks of one fresh evaluation at "
-                      f"{w.name} ({geo.n_tokens} tokens), float64 NumPy, {t_used:.1f} s"}
+    return {"value": round(n * done / t_used, 1), "unit": "tokens·blocks/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"sampled, not the full loop: {done} of the {len(active)} active blocks of "
+                      f"one fresh evaluation at {w.name} ({n} full-resolution tokens, sigma 1), "
+                      f"float64 NumPy oracle, {t_used:.1f} s of oracle time"}
 
 
 def main():
@@ -181,9 +198,18 @@ def main():
     fc1_flops_total = sum(2.0 * r * w.d_model * w.ffn_dim for r in timed_rows)
     fc1_flops = fc1_flops_total / max(fc1_launches, 1)
     achieved = fc1_flops_total / (fc1_ms * 1e-3) / 1e12 if fc1_launches else 0.0
+    # algorithmic operations of the timed forwards, split by the matrix-core type each product
+    # runs on: QKV + cross Q (2 r d 4d), attention (4 r^2 d + 4 r L d), output projections
+    # (4 r d^2), FC1 (2 r d F), FC2 (2 r F d)
     d_, L_, F_ = w.d_model, w.ctx_len, w.ffn_dim
-    fwd_flops_total = sum(2 * r * d_ * 4 * d_ + 4 * r * r * d_ + 4 * r * L_ * d_ + 4 * r * d_ * d_
-                          + 4 * r * d_ * F_ for r in timed_rows)
+    ops = {"bf16": 0.0, "int8": 0.0}
+    for r in timed_rows:
+        ops["int8" if w.int8_linear else "bf16"] += 2.0 * r * d_ * 4 * d_ + 2.0 * r * d_ * F_
+        ops["bf16"] += 4.0 * r * r * d_ + 4.0 * r * L_ * d_ + 4.0 * r * d_ * d_
+        ops["int8" if w.fc2_mode != "bf16" else "bf16"] += 2.0 * r * F_ * d_
+    # time-weighted fraction of the matrix-core peaks: each product's operations over its own
+    # type's peak, summed, over the elapsed time
+    mfma_frac = (ops["bf16"] / PEAK_BF16_TFLOPS + ops["int8"] / PEAK_INT8_TOPS) / 1e12 / elapsed
     actual_tok_blocks = sum(timed_rows) / elapsed
     peak = PEAK_INT8_TOPS if w.int8_linear else PEAK_BF16_TFLOPS
     out = {
@@ -206,7 +232,11 @@ def main():
                    "token_reduction": w.token_reduction},
         "ms_per_fresh_eval": round(elapsed * 1e3 / max(n_evals, 1), 3),
         "actual_tokens_blocks_per_s": round(actual_tok_blocks, 1),
-        "mfma_frac_forward": round(fwd_flops_total / elapsed / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "mfma_frac_forward": round(mfma_frac, 4),
+        "forward_ops": {"bf16_tflop": round(ops["bf16"] / 1e12, 3),
+                        "int8_top": round(ops["int8"] / 1e12, 3),
+                        "bf16_tflops": round(ops["bf16"] / 1e12 / elapsed, 1),
+                        "int8_tops": round(ops["int8"] / 1e12 / elapsed, 1)},
         "roofline": {"bound": "mfma",
                      "kernel": ("fc1_gemm (int8 GEMM + dequant + GELU epilogue)" if w.int8_linear
                                 else "fc1_gemm (bf16 GEMM + GELU epilogue)"),

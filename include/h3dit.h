@@ -274,7 +274,13 @@ int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
                          const float *mod, const float *mod_next, const void *ctx_kv,
                          void *ws, size_t ws_bytes, void *stream);
 
-/* One fresh denoiser evaluation: latent (device, float [N, C]) at sigma -> velocity
+/* One fresh denoiser evaluation (P2 §2: `--steps N` runs N complete passes of the denoiser,
+ * one per fresh step; P3 "DiT fusions and memory": modulation, patch, the active blocks with
+ * the gate + AdaLN fusions, final AdaLN and the velocity head; P3 "aggressive levers": the
+ * token pairing after the third active block and the bypass restore): timestep modulation,
+ * patch embedding, the active blocks (h3_dit_block_fwd, with each MLP gate fused with the
+ * next block's AdaLN), the token-pairing merge / restore when o->token_reduction is set, the
+ * final AdaLN and the head.  latent (device, float [N, C]) at sigma -> velocity
  * (device, float [N, C]).  geom: the full grid (paired = 0).  active (host, int32
  * [n_active]): ascending block indices (h3_select_layers).  eval_index: 0-based count of
  * fresh evaluations before this one (selects the token-pairing restore point).
@@ -328,7 +334,9 @@ enum { H3_EPI_NONE = 0, H3_EPI_GELU = 1 };
 /* C = A B^T + bias (+ bias2), bf16 MFMA with float32 accumulation.  A (device, bf16
  * [M, K], row stride lda elements), B (device, bf16 [N, K], row stride ldb), bias / bias2
  * (device, bf16 [N] or NULL).  out_f32 = 0: C bf16 [M, N] (stride ldc), epilogue
- * H3_EPI_GELU applies exact-erf GELU after the bias; out_f32 = 1: C float [M, N].
+ * H3_EPI_GELU applies GELU after the bias; out_f32 = 1: C float [M, N].  GELU is the erf
+ * form x * Phi(x), with erfc evaluated by Abramowitz & Stegun formula 7.1.26 (absolute error
+ * of x * Phi(x) at most 3.7e-7 over [-12, 12], far below the bf16 rounding of the output).
  * K % 64 == 0, M, N >= 1, strides >= row widths and multiples of 8, and each operand
  * ((rows - 1) * ld + K elements) under 4 GiB (H3_ESHAPE otherwise). */
 int32_t h3_gemm_bf16(const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
@@ -356,8 +364,8 @@ int32_t h3_quant_rows(const void *X, void *Q, float *S, int32_t rows, int32_t K,
  * rounded (no fused multiply-add).  QA int8 [M, K], QW int8 [N, K], SA float [M, K/group],
  * SW float [N], bias bf16 [N], C bf16 [M, ldc].  group = K (K % 128 == 0) or 1024
  * (K % 1024 == 0); QA and QW each under 4 GiB.  epilogue: H3_EPI_NONE, or H3_EPI_GELU
- * (exact-erf GELU of the dequantised value before the bf16 rounding: the int8 FC1 of P3 "the
- * int8 path"). */
+ * (the GELU of h3_gemm_bf16 -- erf form, A&S 7.1.26, absolute error <= 3.7e-7 -- applied to
+ * the dequantised value before the bf16 rounding: the int8 FC1 of P3 "the int8 path"). */
 int32_t h3_gemm_i8(const void *QA, const float *SA, const void *QW, const float *SW,
                    const void *bias, void *C, int64_t ldc, int32_t M, int32_t N, int32_t K,
                    int32_t group, int32_t epilogue, void *stream);

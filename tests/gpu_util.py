@@ -44,3 +44,27 @@ def assert_close(got, ref, rel=1e-2, elem=3e-2, what=""):
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw bytes of a tensor for bit-identity checks."""
     return t.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+
+
+class zero_gates:
+    """Context manager: the model's residual gates (rows g1 and g2 of the shared modulation
+    projection, of its bias and of every block's table) are zero on the device inside, so
+    every block leaves the residual stream as it is; the weights are restored on exit."""
+
+    def __init__(self, model):
+        self.m = model
+
+    def __enter__(self):
+        d, gw = self.m.w.d_model, self.m.gw
+        self.saved = {k: gw[k].clone() for k in ("mod_w", "mod_b", "mod_table")}
+        for r in (2, 5):
+            gw["mod_w"][r * d:(r + 1) * d].zero_()
+            gw["mod_b"][r * d:(r + 1) * d].zero_()
+            gw["mod_table"][:, r].zero_()
+        return self.m
+
+    def __exit__(self, *exc):
+        for k, v in self.saved.items():
+            self.m.gw[k].copy_(v)
+        torch.cuda.synchronize()
+        return False

@@ -194,7 +194,10 @@ def test_operands_of_4_gib_or_more_are_refused(lib):
     assert b"4 GiB" in L.h3_last_error()
     g = B.h3_global_weights(*[1 + i for i in range(len(B.GLOBAL_FIELDS))])  # never dereferenced
     blk = B.h3_block_weights(*([64] * 15 + [None, None]))
-    for bad in [B.h3_dims(512, 8, 1 << 22, 32, 128, 2), B.h3_dims(512, 8, 2048, 1 << 22, 128, 2)]:
+    # FFN and context widths, and the latent channels (patch weight [d, C], head weight [C, d]):
+    # 512 x 2^22 bf16 is exactly 4 GiB
+    for bad in [B.h3_dims(512, 8, 1 << 22, 32, 128, 2), B.h3_dims(512, 8, 2048, 1 << 22, 128, 2),
+                B.h3_dims(512, 8, 2048, 32, 1 << 22, 2)]:
         with pytest.raises(B.H3Error) as e:
             B.h3_model_create(bad, g, [blk, blk])
         assert e.value.code == E and "4 GiB" in str(e.value)
@@ -209,6 +212,14 @@ def test_operands_of_4_gib_or_more_are_refused(lib):
         with pytest.raises(B.H3Error) as e:
             B.h3_workspace_layout(m, n, opts)
         assert e.value.code == E
+    B.h3_model_destroy(m)
+    # a wide latent whose weights fit: the tokens are then bounded by the bf16 latent [n, C]
+    # as well (n * 2^21 * 2 bytes reaches 4 GiB at n = 1024)
+    m = B.h3_model_create(B.h3_dims(512, 8, 2048, 32, 1 << 21, 2), g, [blk, blk])
+    assert B.h3_workspace_size(m, 1023, opts) > 0
+    with pytest.raises(B.H3Error) as e:
+        B.h3_workspace_size(m, 1024, opts)
+    assert e.value.code == E and "latent_ch" in str(e.value)
     B.h3_model_destroy(m)
 
 

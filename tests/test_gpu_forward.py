@@ -11,8 +11,8 @@ import pytest
 import torch
 
 from oracle import dit, host
-from tests.gpu_util import DEV, assert_close, bits, f64, rel_l2
-from tests.oracle_model import oracle_model
+from tests.gpu_util import DEV, assert_close, bits, f64, rel_l2, zero_gates
+from tests.oracle_model import oracle_active, oracle_geom, oracle_model
 from video_diffusion_transformer_fwd_amd import binding as B
 from video_diffusion_transformer_fwd_amd import synthetic as S
 from video_diffusion_transformer_fwd_amd.runtime import DiTModel
@@ -27,13 +27,13 @@ TR_SMALL = S.Workload("tr_160x128_5f", 160, 128, 5, 512, 8, 2048, 32, 32, steps=
 
 
 def loop_parity(w, model, om, opts_kw, steps, reuse, active):
-    geo = model.geo
+    geo = oracle_geom(w)
     lat0 = model.initial_latent()
     x = lat0.clone()
     opts = model.opts(**opts_kw)
     ev = model.denoise(x, steps, reuse, active, opts)
     torch.cuda.synchronize()
-    ref, ev_ref = dit.denoise(f64(lat0), om, steps, reuse, active, geo.as_dict(), w.n_heads,
+    ref, ev_ref = dit.denoise(f64(lat0), om, steps, reuse, active, geo, w.n_heads,
                               fc2_mode=opts_kw.get("fc2_mode", "bf16"),
                               token_reduction=opts_kw.get("token_reduction", False),
                               int8_linear=opts_kw.get("int8_linear", False))
@@ -46,42 +46,79 @@ def loop_parity(w, model, om, opts_kw, steps, reuse, active):
     return r1, r2
 
 
+# Bar on the blocks' own contribution at the small workload.  There the two blocks move the
+# velocity by only ~5% of its norm (the latent by ~2%), so the whole-output bars alone would
+# pass a forward that skipped them.  The contribution c = v - v(zero gates) is gated instead,
+# relative to the oracle's c: a skipped block gives 1, a sign error 2.  Its floor is the bf16
+# residual stream: the GPU stores x + g*y rounded to bf16 (2^-9 relative of |x|, not of |g*y|),
+# which relative to a contribution ~20x smaller than x is ~1e-2.
+CONTRIB_REL = 4e-2
+
+
 def test_tiny_forward_and_loop():
     w = S.WORKLOADS["tiny_256sq_5f"]
     model = DiTModel(w)
     om = oracle_model(w)
-    geo = model.geo
-    assert (geo.f_lat, geo.grid_h, geo.grid_w, geo.scale, geo.n_tokens) == (2, 8, 8, 0.5, 128)
+    geo = oracle_geom(w)
+    assert (geo["f_lat"], geo["grid_h"], geo["grid_w"], geo["scale"], geo["n"]) == (2, 8, 8, 0.5, 128)
+    g = model.geo
+    assert (g.f_lat, g.grid_h, g.grid_w, g.scale, g.n_tokens) == (2, 8, 8, 0.5, 128)
+    assert oracle_active(w, om) == [0, 1]
     lat = model.initial_latent()
     for sigma, ev in [(1.0, 0), (0.5, 3)]:
-        v = model.forward(lat, sigma, eval_index=ev)
+        v = model.forward(lat, sigma, eval_index=ev).clone()
+        with zero_gates(model):
+            v0 = model.forward(lat, sigma, eval_index=ev).clone()
         torch.cuda.synchronize()
-        ref = dit.dit_forward(f64(lat), om, sigma, [0, 1], geo.as_dict(), w.n_heads)
+        ref = dit.dit_forward(f64(lat), om, sigma, [0, 1], geo, w.n_heads)
+        ref0 = dit.dit_forward(f64(lat), om, sigma, [], geo, w.n_heads)
         assert_close(f64(v), ref, rel=2e-2, elem=8e-2, what=f"velocity sigma={sigma}")
-    loop_parity(w, model, om, {}, w.steps, w.reuse, [0, 1])
-    # int8 FC2 modes through the whole evaluation
+        rc = rel_l2(f64(v) - f64(v0), ref - ref0)
+        print(f"sigma={sigma}: velocity rel-L2 {rel_l2(f64(v), ref):.2e}, blocks' contribution "
+              f"rel-L2 {rc:.2e} (contribution / velocity {rel_l2(ref0, ref):.2e})")
+        assert rc <= CONTRIB_REL, rc
+    # the Euler loop, whole and as the blocks' contribution
+    lat0 = model.initial_latent()
+    x = lat0.clone()
+    model.denoise(x, w.steps, w.reuse, [0, 1])
+    x0 = lat0.clone()
+    with zero_gates(model):
+        model.denoise(x0, w.steps, w.reuse, [0, 1])
+    ref, _ = dit.denoise(f64(lat0), om, w.steps, w.reuse, [0, 1], geo, w.n_heads)
+    ref0, _ = dit.denoise(f64(lat0), om, w.steps, w.reuse, [], geo, w.n_heads)
+    r1 = rel_l2(f64(x), ref)
+    r2 = rel_l2(f64(x) - f64(lat0), ref - f64(lat0))
+    rc = rel_l2(f64(x) - f64(x0), ref - ref0)
+    print(f"loop: latent {r1:.2e}, x_N - x_0 {r2:.2e}, blocks' contribution {rc:.2e}")
+    assert r1 < 5e-2 and r2 < 5e-2 and rc <= CONTRIB_REL, (r1, r2, rc)
+    # int8 FC2 modes through the whole evaluation, also as the blocks' contribution
     model8 = DiTModel(w, with_int8=True)
+    with zero_gates(model8):
+        v0 = model8.forward(lat, 1.0).clone()
+    ref0 = dit.dit_forward(f64(lat), om, 1.0, [], geo, w.n_heads)
     for mode in ("row", "grouped"):
         v = model8.forward(lat, 1.0, opts=model8.opts(fc2_mode=mode))
         torch.cuda.synchronize()
-        ref = dit.dit_forward(f64(lat), om, 1.0, [0, 1], geo.as_dict(), w.n_heads, fc2_mode=mode)
+        ref = dit.dit_forward(f64(lat), om, 1.0, [0, 1], geo, w.n_heads, fc2_mode=mode)
         assert rel_l2(f64(v), ref) < 2e-2
+        rc = rel_l2(f64(v) - f64(v0), ref - ref0)
+        assert rc <= CONTRIB_REL, (mode, rc)
 
 
 def test_token_reduction_forward_and_loop():
     w = TR_SMALL
     model = DiTModel(w)
     om = oracle_model(w)
-    active = model.active()
-    assert active == host.select_layers(om["global"]["mod_table"], w.layers)
+    active = oracle_active(w, om)
+    assert model.active() == active
     lat = model.initial_latent()
     for ev in (0, 10):   # restore before the head / before active position 30
         v = model.forward(lat, 0.6, active, eval_index=ev)
         torch.cuda.synchronize()
-        ref = dit.dit_forward(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads,
+        ref = dit.dit_forward(f64(lat), om, 0.6, active, oracle_geom(w), w.n_heads,
                               eval_index=ev, token_reduction=True)
         assert_close(f64(v), ref, rel=2e-2, elem=8e-2, what=f"token-reduced velocity eval {ev}")
-        ref_full = dit.dit_forward(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads)
+        ref_full = dit.dit_forward(f64(lat), om, 0.6, active, oracle_geom(w), w.n_heads)
         assert rel_l2(ref, ref_full) > 2 * rel_l2(f64(v), ref), "pairing must change the result"
     loop_parity(w, model, om, {"token_reduction": True}, w.steps, 1, active)
     loop_parity(w, model, om, {"token_reduction": True}, 5, 2, active)
@@ -171,12 +208,13 @@ def test_int8_path_forward_and_loop():
     w = dataclasses.replace(TR_SMALL, fc2_mode="grouped", int8_linear=True, steps=6)
     model = DiTModel(w)
     om = oracle_model(w)
-    active = model.active()
+    active = oracle_active(w, om)
+    assert model.active() == active
     lat = model.initial_latent()
     for tr in (False, True):
         v = model.forward(lat, 0.6, active, eval_index=3, opts=model.opts(token_reduction=tr))
         torch.cuda.synchronize()
-        ref = dit.dit_forward(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads, eval_index=3,
+        ref = dit.dit_forward(f64(lat), om, 0.6, active, oracle_geom(w), w.n_heads, eval_index=3,
                               fc2_mode="grouped", token_reduction=tr, int8_linear=True)
         assert_close(f64(v), ref, rel=2e-2, elem=8e-2, what=f"int8 velocity token_reduction={tr}")
     loop_parity(w, model, om, {"fc2_mode": "grouped", "int8_linear": True, "token_reduction": True},
@@ -188,7 +226,8 @@ def test_core_reuse_cached_forward(tr):
     w = TR_SMALL
     model = DiTModel(w)
     om = oracle_model(w)
-    active = model.active()
+    active = oracle_active(w, om)
+    assert model.active() == active
     lat = model.initial_latent()
     n, d = model.geo.n_tokens, w.d_model
     opts = model.opts(token_reduction=tr)
@@ -199,9 +238,9 @@ def test_core_reuse_cached_forward(tr):
     # the fresh cached evaluation is the forward, bit for bit
     assert np.array_equal(bits(v_fresh), bits(v_plain))
     tr_ref = {}
-    v_ref = dit.dit_forward(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads,
+    v_ref = dit.dit_forward(f64(lat), om, 0.6, active, oracle_geom(w), w.n_heads,
                             eval_index=2, token_reduction=tr, trace=tr_ref)
-    _, d_ref = dit.dit_forward_cached(f64(lat), om, 0.6, active, model.geo.as_dict(), w.n_heads,
+    _, d_ref = dit.dit_forward_cached(f64(lat), om, 0.6, active, oracle_geom(w), w.n_heads,
                                       eval_index=2, token_reduction=tr)
     # the delta is a small difference of two bf16 streams: besides 2e-2 of its own norm it
     # carries the bf16 rounding of every residual update of the stream, about sqrt(blocks)
@@ -218,7 +257,7 @@ def test_core_reuse_cached_forward(tr):
     lat2 = lat * 0.8
     v2 = model.forward_cached(lat2, 0.35, False, delta, active, 2, opts)
     torch.cuda.synchronize()
-    ref2, _ = dit.dit_forward_cached(f64(lat2), om, 0.35, active, model.geo.as_dict(), w.n_heads,
+    ref2, _ = dit.dit_forward_cached(f64(lat2), om, 0.35, active, oracle_geom(w), w.n_heads,
                                      core_delta=f64(delta))
     assert_close(f64(v2), ref2, rel=2e-2, elem=8e-2, what="reused velocity")
 
@@ -231,7 +270,7 @@ def test_core_reuse_loop():
     x = lat0.clone()
     ev = model.denoise(x, 7, 1, [0, 1], model.opts(), core_reuse=3)
     torch.cuda.synchronize()
-    ref, ev_ref = dit.denoise(f64(lat0), om, 7, 1, [0, 1], model.geo.as_dict(), w.n_heads,
+    ref, ev_ref = dit.denoise(f64(lat0), om, 7, 1, [0, 1], oracle_geom(w), w.n_heads,
                               core_reuse=3)
     assert ev == ev_ref == 3
     r1 = rel_l2(f64(x), ref)

@@ -123,6 +123,59 @@ def test_attention_long_queries_short_keys(nk):
     assert_close(f64(O)[rows], ref.reshape(-1, H * D), rel=1e-2, elem=3e-2, what=f"attention nk={nk}")
 
 
+def planted_scores(nq, nk, H, D, tiles, seed):
+    """Attention inputs whose scores jump far above the running maximum in later key tiles.
+
+    Early keys are small (scores ~0).  For the even queries, which carry the planted
+    direction, the key planted in the first tile of ``tiles`` scores 11 log2 units above them
+    (2^11 times the softmax weight) and one in a second tile 9 more; odd queries see no jump,
+    so within one wave some lanes move their softmax reference and others keep it.  Both jumps
+    exceed the kernel's lazy threshold (8 log2 units), so each rescales the running sum and
+    output, and what was accumulated before a jump keeps a weight that matters (the ~600
+    small keys against 2^11 after one jump, the first planted key against 2^9 after the
+    second): a wrong, missing or inverted rescale moves the output by O(1), about 10^-2 of
+    which the test tolerates.  Returns Q, K, V as [n, H*D] bf16 on the device.
+    """
+    rng = np.random.default_rng(seed)
+    c = np.log2(np.e) / np.sqrt(D)
+    u = rng.choice([-1.0, 1.0], size=(H, D))
+    a = np.where(np.arange(nq) % 2 == 0, 2.0, 0.0)
+    q = a[:, None, None] * u[None] + 0.3 * rng.standard_normal((nq, H, D))
+    k = 0.05 * rng.standard_normal((nk, H, D))
+    for j, t in enumerate(tiles):
+        k[64 * t + 7 + 3 * j] = u * ((11.0 + 9.0 * j) / c) / (2.0 * D)
+    v = rng.standard_normal((nk, H, D))
+    return tuple(bf16_dev(x.reshape(x.shape[0], H * D)) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("nq,nk,H,D,tiles", [
+    (600, 700, 2, 128, (5,)),      # two key groups; the jump in the second group's tile
+    (600, 700, 2, 128, (4,)),      # ... in the first group's tile
+    (600, 700, 2, 128, (2, 6)),    # two jumps, one in each group
+    (600, 256, 2, 128, (3,)),      # cross-attention length, two key groups
+    (1040, 700, 32, 128, (5,)),    # four-wave workgroups
+    (1040, 256, 32, 128, (1, 3)),  # four-wave, cross-attention length, two jumps
+    (600, 600, 2, 64, (5,)),       # head dim 64, two key groups
+    (600, 600, 2, 64, (4,)),
+    (700, 600, 48, 64, (2, 5)),    # head dim 64, four-wave workgroups
+    (8192, 700, 2, 128, (5,)),     # eight-wave workgroups (sampled rows)
+    (8200, 512, 2, 128, (2, 7)),   # eight-wave, ragged queries, two jumps
+])
+def test_attention_softmax_rescale(nq, nk, H, D, tiles):
+    Q, K, V = planted_scores(nq, nk, H, D, tiles, seed=nq + nk + sum(tiles))
+    O = torch.empty((nq, H * D), dtype=torch.bfloat16, device=DEV)
+    B.h3_attention(Q, K, V, O, nq, nk, H, D)
+    sync()
+    rows = np.arange(nq) if nq <= 2048 else np.concatenate([np.arange(0, 64), np.arange(4096, 4160),
+                                                             np.arange(nq - 64, nq)])
+    q, k, v = (f64(t).reshape(-1, H, D) for t in (Q, K, V))
+    ref = dit.attention(q[rows], k, v)
+    # the planted keys hold most but not all of the weight of the even queries
+    sc = (k[:, 0] @ q[0, 0]) * np.log2(np.e) / np.sqrt(D)
+    assert sc.max() - sc[:64].max() > 10.0
+    assert_close(f64(O)[rows], ref.reshape(-1, H * D), rel=1e-2, elem=3e-2, what="rescaled attention")
+
+
 def test_attention_strided_views_of_qkvq():
     # the block's layout: q, k, v, qc as column slices of one [N, 4d] buffer, output into [N, 2d]
     rng = np.random.default_rng(11)

@@ -13,7 +13,9 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libh3dit.so")
+# H3DIT_LIB names another build of the same library (the host-sanitized copy that the CPU
+# tests load); unset, the in-tree build is loaded
+LIB_PATH = os.environ.get("H3DIT_LIB") or os.path.join(_PKG, "libh3dit.so")
 
 H3_OK, H3_EINVAL, H3_ESHAPE, H3_EUNSUPPORTED, H3_EWORKSPACE, H3_EHIP = 0, -1, -2, -3, -4, -5
 H3_FC2_BF16, H3_FC2_INT8_ROW, H3_FC2_INT8_GROUPED = 0, 1, 2

@@ -116,12 +116,16 @@ int32_t validate_model(const h3_model *m) {
 }
 
 // Token counts of a block: its largest activation operands are the FC2 input [n, ffn_dim] and
-// the out-projection input [n, 2 d_model] (bf16), each addressed within 4 GiB.
+// the out-projection input [n, 2 d_model] (bf16), each addressed within 4 GiB; the patch
+// product's input, the bf16 latent [n, latent_ch], likewise.
 int32_t check_tokens(const h3_model *m, int32_t n, const char *who) {
   if (n < 1) return fail(H3_ESHAPE, std::string(who) + ": n_tokens must be >= 1");
   const int64_t f = m->dims.ffn_dim, d2 = 2 * static_cast<int64_t>(m->dims.d_model);
   if (!fits_u32(n, f, f, 2) || !fits_u32(n, d2, d2, 2))
     return fail(H3_ESHAPE, std::string(who) + ": n_tokens x ffn_dim spans 4 GiB or more");
+  const int64_t c = m->dims.latent_ch;
+  if (!fits_u32(n, c, c, 2))
+    return fail(H3_ESHAPE, std::string(who) + ": n_tokens x latent_ch spans 4 GiB or more");
   return H3_OK;
 }
 
@@ -356,6 +360,9 @@ int32_t h3_model_create(const h3_dims *dims, const h3_global_weights *g,
     return fail(H3_ESHAPE, "h3_model_create: ffn_dim x d_model or ctx_len x d_model spans 4 GiB or more");
   if (dm.latent_ch < 64 || dm.latent_ch % 64)
     return fail(H3_ESHAPE, "h3_model_create: latent_ch must be a positive multiple of 64");
+  // the patch weight [d, C] and the head weight [C, d] are product operands too
+  if (!fits_u32(dm.d_model, dm.latent_ch, dm.latent_ch, 2) || !fits_u32(dm.latent_ch, dm.d_model, dm.d_model, 2))
+    return fail(H3_ESHAPE, "h3_model_create: latent_ch x d_model spans 4 GiB or more");
   const void *gp[] = {g->t1_w, g->t1_b, g->t2_w, g->t2_b, g->mod_w, g->mod_b, g->fin_w,
                       g->fin_b, g->fin_t, g->mod_table, g->patch_w, g->patch_b, g->head_w,
                       g->head_b};

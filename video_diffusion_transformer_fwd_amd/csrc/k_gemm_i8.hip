@@ -19,8 +19,9 @@
 // second launch adds the S partials (integer addition: exact in any order) and dequantises, so
 // the result equals the unsplit product bit for bit.  Grouped mode folds each group's int32
 // sums into a float32 total in group order inside the kernel and is never split (the float
-// fold order is fixed).  The dequantising epilogue (optionally followed by the exact-erf GELU
-// of the bf16 product) runs from an LDS band in a rolled loop, as in the bf16 product.
+// fold order is fixed).  The dequantising epilogue, optionally followed by the bf16 product's
+// GELU (erf form, erfc by A&S 7.1.26), runs from an LDS band in a rolled loop, as in the bf16
+// product.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
