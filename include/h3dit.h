@@ -209,6 +209,14 @@ typedef struct h3_run_opts {
                                * sums the products' split-K partials itself; 0: there they are
                                * not written (nothing downstream reads them).  Results are
                                * identical either way. */
+  int32_t fused_head_adaln;   /* 1: the final AdaLN runs inside the velocity head's product, applied
+                               * to the residual rows as its tiles are staged (P3 "DiT fusions and
+                               * memory": the final heads apply AdaLN while loading their
+                               * projection tiles; h3_head_adaln_gemm), where the head's tiling
+                               * allows it (latent_ch < 192); the last block's MLP gate then
+                               * stores no AdaLN.  0: the last block's MLP gate computes the
+                               * final AdaLN (or the AdaLN kernel, after a bypass restore or a
+                               * cached core) and the head reads it.  Bit-identical. */
 } h3_run_opts;
 
 /* Tokens of a geometry (validates it). */
@@ -390,6 +398,22 @@ int32_t h3_gate_adaln(const void *x, const void *y, const float *gate, void *x_o
 int32_t h3_gate_adaln_quant(const void *x, const void *y, const float *gate, void *x_out,
                             const float *shift, const float *scale, void *q_out, float *s_out,
                             int32_t rows, int32_t d_model, void *stream);
+
+/* The velocity head with the final AdaLN applied while its tiles are staged (P3 "DiT fusions and
+ * memory": the final BF16 heads apply AdaLN while loading their projection tiles):
+ *   out = AdaLN(x; shift, scale) W^T + bias, float32,
+ * with AdaLN as h3_gate_adaln computes it (n = bf16(LN(x) (1 + scale) + shift)).  The staged
+ * tile holds exactly the bf16 values h3_gate_adaln would store, and the product runs as
+ * h3_gemm_bf16 runs it, so the result equals h3_gate_adaln (into a bf16 buffer) followed by
+ * h3_gemm_bf16 (out_f32 = 1) bit for bit.  x (device, bf16 [rows, d_model], 16-byte aligned);
+ * shift, scale (device, float [d_model], 16-byte aligned); W (device, bf16 [n_out, d_model]);
+ * bias (device, bf16 [n_out] or NULL); out (device, float [rows, n_out]).  d_model as in
+ * h3_dims; n_out a positive multiple of 8 (H3_ESHAPE) and below 192, the widths at which the
+ * plain product takes the 128x128 tiles reproduced here (H3_EUNSUPPORTED above); x and W under
+ * 4 GiB (H3_ESHAPE). */
+int32_t h3_head_adaln_gemm(const void *x, const float *shift, const float *scale, const void *W,
+                           const void *bias, float *out, int32_t rows, int32_t d_model,
+                           int32_t n_out, void *stream);
 
 /* RoPE table of a geometry: table (device, float2 [n_tokens, head_dim/2]) = (cos, sin) of
  * coord * 10000^(-2j/D_axis) for the [t | h | w] channel slices of D - 4 floor(D/6),

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
     for s in syms:
         assert hasattr(raw, s), f"{s} declared in h3dit.h but not exported"
     assert set(syms) == set(B.SIGNATURES), "binding signatures out of sync with the header"
-    assert lib.h3_abi_version() == 103
+    assert lib.h3_abi_version() == 104
 
 
 def test_align_frames_matches_oracle(lib):

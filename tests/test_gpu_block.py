@@ -18,7 +18,7 @@ import torch
 
 from oracle import dit
 from tests.gpu_util import DEV, assert_close, bits, f64, rel_l2
-from tests.oracle_model import oracle_model
+from tests.oracle_model import oracle_geom, oracle_model
 from video_diffusion_transformer_fwd_amd import binding as B
 from video_diffusion_transformer_fwd_amd import synthetic as S
 from video_diffusion_transformer_fwd_amd.runtime import DiTModel
@@ -60,7 +60,9 @@ def test_block_parity(name, fc2_mode, int8_linear):
     sigma = 0.75
     mod, fin = dit.modulation(om["global"], sigma)
     mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
-    coords = dit.rope_coords(model.geo.f_lat, model.geo.grid_h, model.geo.grid_w, model.geo.scale)
+    geo = oracle_geom(w)
+    assert geo["n"] == n
+    coords = dit.rope_coords(geo["f_lat"], geo["grid_h"], geo["grid_w"], geo["scale"])
     x0 = S.normal("test.block.x", (n, d), 1.0)
     opts = B.make_opts(fc2_mode=fc2_mode, int8_linear=int8_linear, store_branches=True)
     for b in range(w.n_blocks):

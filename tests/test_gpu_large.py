@@ -12,6 +12,7 @@ import torch
 
 from oracle import dit
 from tests.gpu_util import DEV, assert_close, f64
+from tests.oracle_model import oracle_geom, oracle_latent, oracle_model
 from video_diffusion_transformer_fwd_amd import binding as B
 from video_diffusion_transformer_fwd_amd import synthetic as S
 
@@ -126,7 +127,8 @@ def test_forward_full_size_zero_gates_and_fused_identity():
     assert model.geo.n_tokens == N
     lat = model.initial_latent()
     v1 = model.forward(lat, 1.0).clone()
-    v2 = model.forward(lat, 1.0, opts=model.opts(fused_gate_adaln=False, fused_cross_block=False)).clone()
+    v2 = model.forward(lat, 1.0, opts=model.opts(fused_gate_adaln=False, fused_cross_block=False,
+                                                 fused_qk_rope=False, fused_head_adaln=False)).clone()
     torch.cuda.synchronize()
     assert torch.equal(v1.view(torch.int32), v2.view(torch.int32)), "fused and unfused forwards differ"
     assert torch.isfinite(v1).all()
@@ -137,10 +139,12 @@ def test_forward_full_size_zero_gates_and_fused_identity():
         model.gw["mod_table"][:, r].zero_()
     v0 = model.forward(lat, 1.0)
     torch.cuda.synchronize()
-    g = {k: f64(model.gw[k]) for k in model.gw}
+    # the oracle's weights from the seeded generator (the zeroed gate rows do not enter the head)
+    g = oracle_model(w, blocks=[])["global"]
     _, fin = dit.modulation(g, 1.0)
-    rows = torch.as_tensor(sample_rows(N, 256, 11), device=DEV)
-    ref = dit.final_head(dit.patch_embed(f64(lat[rows]), g), g, fin)
+    rows_np = sample_rows(N, 256, 11)
+    rows = torch.as_tensor(rows_np, device=DEV)
+    ref = dit.final_head(dit.patch_embed(oracle_latent(w)[rows_np], g), g, fin)
     assert_close(f64(v0[rows]), ref, rel=2e-2, elem=8e-2, what="zero-gate velocity rows")
     model.close()
 
@@ -159,10 +163,12 @@ def test_block_local_chain_sampled_rows():
     d, H, F = w.d_model, w.n_heads, w.ffn_dim
     Dh = d // H
     geo = model.geo
-    g = {k: f64(model.gw[k]) for k in model.gw}
+    og = oracle_geom(w)
+    assert og["n"] == N == geo.n_tokens
+    g = oracle_model(w, blocks=[])["global"]
     mod, _ = dit.modulation(g, 0.75)
     mod_dev = torch.tensor(mod, dtype=torch.float32, device=DEV)
-    coords = dit.rope_coords(geo.f_lat, geo.grid_h, geo.grid_w, geo.scale)
+    coords = dit.rope_coords(og["f_lat"], og["grid_h"], og["grid_w"], og["scale"])
     opts = B.make_opts(store_branches=True)
     lay = B.h3_workspace_layout(model.handle, N, opts)
     rows = sample_rows(N, 10, 21)

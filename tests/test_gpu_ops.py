@@ -222,6 +222,47 @@ def test_gate_adaln_fused_bit_identical_and_oracle(rows, d):
     assert_close(f64(n_only), dit.adaln(f64(x), f64(sh), f64(sc)), rel=6e-3, elem=2e-2, what="adaln")
 
 
+@pytest.mark.parametrize("rows,d,n_out", [
+    (1536, 3072, 128),   # the 512x512x22 head: two waves per AdaLN row (even d/512, few rows)
+    (300, 512, 128),     # one wave per row (odd d/512), ragged last tile
+    (1000, 1536, 64),    # one wave per row, narrower head
+    (2430, 3072, 8),     # the 864x480 token count, a head of one 8-wide tile column
+    (17000, 1024, 128),  # one wave per row because of the row count (even d/512)
+    (61488, 5120, 128),  # the 768x1344 head
+])
+def test_head_adaln_gemm_bit_identical_to_adaln_then_product(rows, d, n_out):
+    # the final AdaLN applied while the head product stages its tiles equals the AdaLN kernel
+    # followed by the product, bit for bit; and the oracle's AdaLN + head
+    rng = np.random.default_rng(rows + d + n_out)
+    x = randn_bf16(rng, (rows, d), 1.5)
+    vec = lambda: torch.tensor(rng.standard_normal(d) * 0.2, dtype=torch.float32, device=DEV)
+    sh, sc = vec(), vec()
+    W = randn_bf16(rng, (n_out, d), 0.02)
+    b = randn_bf16(rng, (n_out,), 0.02)
+    fused = torch.empty((rows, n_out), dtype=torch.float32, device=DEV)
+    B.h3_head_adaln_gemm(x, sh, sc, W, b, fused)
+    n = torch.empty_like(x)
+    B.h3_gate_adaln(x, None, None, None, sh, sc, n)
+    plain = torch.empty_like(fused)
+    B.h3_gemm_bf16(n, W, plain, bias=b)
+    sync()
+    assert np.array_equal(bits(fused), bits(plain)), "fused head differs from AdaLN + product"
+    rows_s = np.arange(rows) if rows <= 4096 else np.concatenate([np.arange(64), rng.integers(64, rows, 128),
+                                                                  np.arange(rows - 64, rows)])
+    ref = dit.linear(dit.adaln(f64(x)[rows_s], f64(sh), f64(sc)), f64(W), f64(b))
+    assert_close(f64(fused)[rows_s], ref, rel=1e-2, elem=3e-2, what="head")
+
+
+def test_head_adaln_gemm_refuses_wide_heads():
+    x = torch.zeros((64, 512), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros(512, dtype=torch.float32, device=DEV)
+    W = torch.zeros((192, 512), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((64, 192), dtype=torch.float32, device=DEV)
+    with pytest.raises(B.H3Error) as e:
+        B.h3_head_adaln_gemm(x, v, v, W, None, out)
+    assert e.value.code == B.H3_EUNSUPPORTED
+
+
 def test_zero_gate_leaves_residual_bit_exact():
     rng = np.random.default_rng(2)
     x = randn_bf16(rng, (40, 3072))

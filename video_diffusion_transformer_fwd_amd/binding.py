@@ -57,7 +57,7 @@ class h3_geom(C.Structure):
 class h3_run_opts(C.Structure):
     _fields_ = [(n, C.c_int32) for n in
                 ("fc2_mode", "fused_gate_adaln", "fused_cross_block", "qk_norm", "token_reduction",
-                 "int8_linear", "fused_qk_rope", "store_branches")]
+                 "int8_linear", "fused_qk_rope", "store_branches", "fused_head_adaln")]
 
 
 class h3_ws_layout(C.Structure):
@@ -105,6 +105,7 @@ SIGNATURES = {
     "h3_gemm_i8": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32, _I32, _VP]),
     "h3_gate_adaln": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
     "h3_gate_adaln_quant": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _VP]),
+    "h3_head_adaln_gemm": (_I32, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     "h3_rope_table": (_I32, [C.POINTER(h3_geom), _I32, _VP, _VP]),
     "h3_qk_norm_rope": (_I32, [_VP, _I64, _I32, _I32, _I32, _VP, _VP, _I32, _VP, _VP]),
     "h3_qkv_gemm": (_I32, [_VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32,
@@ -241,11 +242,12 @@ def h3_geom_tokens(geom: h3_geom) -> int:
 
 
 def make_opts(fc2_mode="bf16", fused_gate_adaln=True, fused_cross_block=True, qk_norm=True,
-              token_reduction=False, int8_linear=False, fused_qk_rope=True, store_branches=False):
+              token_reduction=False, int8_linear=False, fused_qk_rope=True, store_branches=False,
+              fused_head_adaln=True):
     return h3_run_opts(FC2_MODES[fc2_mode] if isinstance(fc2_mode, str) else fc2_mode,
                        int(fused_gate_adaln), int(fused_cross_block), int(qk_norm),
                        int(token_reduction), int(int8_linear), int(fused_qk_rope),
-                       int(store_branches))
+                       int(store_branches), int(fused_head_adaln))
 
 
 # ------------------------------------------------------------------ model
@@ -388,6 +390,18 @@ def h3_gate_adaln_quant(x, y, gate, x_out, shift, scale, q_out, s_out, stream=No
                                      ptr(x_out, "bf16"), ptr(shift, "f32"), ptr(scale, "f32"),
                                      ptr(q_out, "i8"), ptr(s_out, "f32"), rows, d,
                                      stream_handle(stream)))
+
+
+def h3_head_adaln_gemm(x, shift, scale, W, bias, out, stream=None):
+    rows, d = x.shape
+    n_out = W.shape[0]
+    # the entry point takes dense rows: x [rows, d], W [n_out, d], out [rows, n_out]
+    if x.stride(0) != d or W.shape[1] != d or W.stride(0) != d or tuple(out.shape) != (rows, n_out) \
+            or out.stride(0) != n_out:
+        raise ValueError("h3_head_adaln_gemm: x, W and out must be dense [rows, d], [n_out, d], [rows, n_out]")
+    _check(lib().h3_head_adaln_gemm(ptr(x, "bf16"), ptr(shift, "f32"), ptr(scale, "f32"),
+                                    ptr(W, "bf16"), ptr(bias, "bf16"), ptr(out, "f32"), rows, d,
+                                    n_out, stream_handle(stream)))
 
 
 def h3_rope_table(geom, head_dim, table, stream=None):

@@ -11,6 +11,7 @@
 
 #include "h3_internal.h"
 
+
 struct h3_model : h3::Model {};
 
 namespace h3 {
@@ -37,6 +38,8 @@ int32_t check_opts(const h3_run_opts *o) {
   if (o->int8_linear != 0 && o->int8_linear != 1) return fail(H3_EINVAL, "int8_linear must be 0 or 1");
   if (o->fused_qk_rope != 0 && o->fused_qk_rope != 1) return fail(H3_EINVAL, "fused_qk_rope must be 0 or 1");
   if (o->store_branches != 0 && o->store_branches != 1) return fail(H3_EINVAL, "store_branches must be 0 or 1");
+  if (o->fused_head_adaln != 0 && o->fused_head_adaln != 1)
+    return fail(H3_EINVAL, "fused_head_adaln must be 0 or 1");
   return H3_OK;
 }
 
@@ -317,11 +320,14 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
   return check_launch("h3_dit_block_fwd");
 }
 
-int32_t run_modulation(const h3_model *m, float sigma, float *mod, float *mod_final, char *ws,
-                       const WsPlan &p, hipStream_t s) {
+// Modulation intermediates (tmp, (256 + 8 d) floats): the sinusoid e [256], the two hidden
+// activations [d] each and the shared projection [6 d]; each is written in full before it is read.
+size_t modulation_tmp_bytes(int d) { return (256 + 8 * static_cast<size_t>(d)) * sizeof(float); }
+
+int32_t run_modulation(const h3_model *m, float sigma, float *mod, float *mod_final, float *tmp,
+                       hipStream_t s) {
   const int d = m->dims.d_model, nb = m->dims.n_blocks;
   const h3_global_weights &g = m->g;
-  float *tmp = reinterpret_cast<float *>(ws + p.tmp);
   float *e = tmp, *h1 = tmp + 256, *u = h1 + d, *Mv = u + d;
   launch_timestep_sinusoid(sigma, e, s);
   launch_gemv(reinterpret_cast<const bf16_t *>(g.t1_w), e, reinterpret_cast<const bf16_t *>(g.t1_b),
@@ -482,7 +488,8 @@ int32_t h3_modulation(const h3_model *m, float sigma, float *mod, float *mod_fin
   h3_run_opts o{};
   const WsPlan p = plan_workspace(*m, 1, o);
   if (!ws || ws_bytes < p.total) return fail(H3_EWORKSPACE, "h3_modulation: workspace too small");
-  return run_modulation(m, sigma, mod, mod_final, reinterpret_cast<char *>(ws), p, as_stream(stream));
+  return run_modulation(m, sigma, mod, mod_final, reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + p.tmp),
+                        as_stream(stream));
 }
 
 int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
@@ -511,7 +518,31 @@ int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
 
 namespace {
 enum CoreMode { kCorePlain = 0, kCoreFresh = 1, kCoreReuse = 2 };
+
+// The velocity head v = AdaLN_final(x) W_h^T + b_h, float32 [n, C].  n_final: the final AdaLN,
+// already stored (the last block's MLP gate computed it), or NULL: then it is formed here,
+// inside the head product's tile loads when o.fused_head_adaln is set and the product has
+// that form, else by the AdaLN kernel into `scratch` (bf16 [n, d]) before the product.
+void run_head(const h3_model *m, const h3_run_opts &o, const bf16_t *x, const bf16_t *n_final,
+              const float *fin, float *velocity, int n, void *scratch, hipStream_t s) {
+  const int d = m->dims.d_model, C = m->dims.latent_ch;
+  const bf16_t *hw = reinterpret_cast<const bf16_t *>(m->g.head_w);
+  const bf16_t *hb = reinterpret_cast<const bf16_t *>(m->g.head_b);
+  if (!n_final && o.fused_head_adaln && head_adaln_gemm_fits(x, d, fin, fin + d, n, C, d)) {
+    ProfScope ps(H3_ST_HEAD, s);
+    launch_head_adaln_gemm(x, d, fin, fin + d, hw, d, hb, velocity, C, n, C, d, s);
+    return;
+  }
+  if (!n_final) {
+    ProfScope ps(H3_ST_ADALN, s);
+    launch_gate_adaln(x, nullptr, nullptr, nullptr, fin, fin + d, reinterpret_cast<bf16_t *>(scratch),
+                      n, d, s);
+    n_final = reinterpret_cast<const bf16_t *>(scratch);
+  }
+  ProfScope ps(H3_ST_HEAD, s);
+  launch_gemm_bf16(n_final, d, hw, d, velocity, C, n, C, d, hb, nullptr, H3_EPI_NONE, 1, s);
 }
+}  // namespace
 
 // One evaluation.  kCorePlain: the forward.  kCoreFresh: the forward, and core_delta =
 // x_L - x_0 (stream after the last active block minus the patch embedding).  kCoreReuse:
@@ -564,7 +595,7 @@ static int32_t forward_impl(const h3_model *m, const h3_geom *geom, const h3_run
 
   {
     ProfScope ps(H3_ST_MODULATION, s);
-    if (int32_t e = run_modulation(m, sigma, mod, fin, w, p, s)) return e;
+    if (int32_t e = run_modulation(m, sigma, mod, fin, reinterpret_cast<float *>(w + p.tmp), s)) return e;
   }
   {
     // patch embedding: x = bf16(latent) W_p^T + b_p
@@ -578,14 +609,7 @@ static int32_t forward_impl(const h3_model *m, const h3_geom *geom, const h3_run
   if (core_mode == kCoreReuse) {
     // cached core: x = bf16(x_0 + delta); final AdaLN of this sigma; head
     launch_core_apply(x, core_delta, x, nd, s);
-    bf16_t *nh = reinterpret_cast<bf16_t *>(w + p.n1b);
-    {
-      ProfScope ps(H3_ST_ADALN, s);
-      launch_gate_adaln(x, nullptr, nullptr, nullptr, fin, fin + d, nh, n, d, s);
-    }
-    ProfScope ps(H3_ST_HEAD, s);
-    launch_gemm_bf16(nh, d, reinterpret_cast<const bf16_t *>(m->g.head_w), d, velocity, C, n, C, d,
-                     reinterpret_cast<const bf16_t *>(m->g.head_b), nullptr, H3_EPI_NONE, 1, s);
+    run_head(m, *o, x, nullptr, fin, velocity, n, w + p.n1b, s);
     return check_launch("h3_dit_forward_cached");
   }
   if (core_mode == kCoreFresh) {
@@ -633,7 +657,7 @@ static int32_t forward_impl(const h3_model *m, const h3_geom *geom, const h3_run
     if (!last && !token_op_next) {
       mnext = mod + static_cast<size_t>(active[pos + 1]) * 6 * d;
       n1n = n1_other;
-    } else if (last && !restore_before_head) {
+    } else if (last && !restore_before_head && !o->fused_head_adaln) {
       mnext = fin;
       n1n = n1_other;
     }
@@ -655,20 +679,14 @@ static int32_t forward_impl(const h3_model *m, const h3_geom *geom, const h3_run
         launch_token_reduce(1, *geom, d, xr, x, x, s);
       }
       cur = x; rows = n;
-      ProfScope ps(H3_ST_ADALN, s);
-      launch_gate_adaln(x, nullptr, nullptr, nullptr, fin, fin + d, reinterpret_cast<bf16_t *>(n1),
-                        rows, d, s);
-      n1_valid = true;
+      n1_valid = false;
     }
   }
   if (core_mode == kCoreFresh) launch_core_delta(x, x0, core_delta, nd, s);
-  // head: velocity = AdaLN_final(x) W_h^T + b_h, float32
-  {
-    ProfScope ps(H3_ST_HEAD, s);
-    launch_gemm_bf16(reinterpret_cast<const bf16_t *>(n1), d,
-                     reinterpret_cast<const bf16_t *>(m->g.head_w), d, velocity, C, n, C, d,
-                     reinterpret_cast<const bf16_t *>(m->g.head_b), nullptr, H3_EPI_NONE, 1, s);
-  }
+  // head: velocity = AdaLN_final(x) W_h^T + b_h, float32 (n1 holds the final AdaLN when the
+  // last block's MLP gate computed it)
+  run_head(m, *o, x, n1_valid ? reinterpret_cast<const bf16_t *>(n1) : nullptr, fin, velocity, n,
+           n1_other, s);
   return check_launch("h3_dit_forward");
 }
 
@@ -811,6 +829,25 @@ int32_t h3_gate_adaln_quant(const void *x, const void *y, const float *gate, voi
                     reinterpret_cast<bf16_t *>(x_out), shift, scale, nullptr, rows, d_model,
                     as_stream(stream), reinterpret_cast<int8_t *>(q_out), s_out);
   return check_launch("h3_gate_adaln_quant");
+}
+
+int32_t h3_head_adaln_gemm(const void *x, const float *shift, const float *scale, const void *W,
+                           const void *bias, float *out, int32_t rows, int32_t d_model,
+                           int32_t n_out, void *stream) {
+  if (!x || !shift || !scale || !W || !out) return fail(H3_EINVAL, "h3_head_adaln_gemm: NULL pointer");
+  if (rows < 1) return fail(H3_ESHAPE, "h3_head_adaln_gemm: rows must be >= 1");
+  if (!supported_width(d_model)) return fail(H3_ESHAPE, "h3_head_adaln_gemm: unsupported d_model");
+  if (n_out < 1 || n_out % 8) return fail(H3_ESHAPE, "h3_head_adaln_gemm: n_out must be a positive multiple of 8");
+  if (!fits_u32(rows, d_model, d_model, 2) || !fits_u32(n_out, d_model, d_model, 2))
+    return fail(H3_ESHAPE, "h3_head_adaln_gemm: an operand spans 4 GiB or more");
+  const bf16_t *xb = reinterpret_cast<const bf16_t *>(x);
+  if (!head_adaln_gemm_fits(xb, d_model, shift, scale, rows, n_out, d_model))
+    return fail(H3_EUNSUPPORTED,
+                "h3_head_adaln_gemm: no fused form (n_out >= 192, or x / shift / scale not 16-byte aligned)");
+  launch_head_adaln_gemm(xb, d_model, shift, scale, reinterpret_cast<const bf16_t *>(W), d_model,
+                         reinterpret_cast<const bf16_t *>(bias), out, n_out, rows, n_out, d_model,
+                         as_stream(stream));
+  return check_launch("h3_head_adaln_gemm");
 }
 
 int32_t h3_rope_table(const h3_geom *geom, int32_t head_dim, void *table, void *stream) {

@@ -32,6 +32,8 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 // s_waitcnt immediate that waits until at most `vm` vector-memory operations are outstanding
 // (expcnt and lgkmcnt left unconstrained): vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14.
 constexpr int waitcnt_vm(int vm) { return (vm & 15) | (7 << 4) | (15 << 8) | ((vm >> 4) << 14); }
+// The same, and every LDS / scalar-memory operation done (lgkmcnt, bits 11:8, = 0).
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | ((vm >> 4) << 14); }
 
 // Waits for this thread's direct-to-LDS loads down to `VM` outstanding, then meets the other
 // waves at a barrier; afterwards every wave sees the LDS bytes those loads wrote.
@@ -40,6 +42,27 @@ __device__ __forceinline__ void lds_dma_barrier() {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
   __builtin_amdgcn_s_barrier();
 }
+// As lds_dma_barrier, for waves that also wrote LDS themselves (ds_write) since the last barrier.
+template <int VM>
+__device__ __forceinline__ void lds_dma_write_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
+  __builtin_amdgcn_s_barrier();
+}
+
+// xor butterfly over the wave: lanes i and i^o add the same two values (commutative), so every
+// lane ends with the identical total.  The AdaLN row statistics of every kernel use this sum.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Waves per row of the AdaLN row kernels for `rows` rows of width d: two below 16384 rows
+// when d / 512 is even (twice the waves in flight), else one.  The row statistics' summation
+// order depends on it, so every kernel that must reproduce an AdaLN bit for bit asks here.
+inline int adaln_waves_per_row(int rows, int d) { return (rows >= 16384 || (d / 512) % 2) ? 1 : 2; }
+
+constexpr float kLnEps = 1e-6f;
 
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   h3_bf16x2_t r;
@@ -293,6 +316,19 @@ void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const f
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
                     hipStream_t s, const SplitScratch &scratch = SplitScratch(),
                     int epilogue = H3_EPI_NONE);
+// The velocity head with the final AdaLN applied while the A tiles are staged:
+// out = float(AdaLN(x; shift, scale) W^T + bias), float32 [M, N] at row stride ldo, x bf16
+// [M, d] at stride ldx, shift / scale float [d], W bf16 [N, d].  Bit-identical to
+// launch_gate_adaln (AdaLN only) into a bf16 buffer followed by launch_gemm_bf16 with a float32
+// output.  Returns 1 when launched, 0 when there is no such form (it needs N < 192, where the
+// plain product takes 128x128 unsplit tiles; 16-byte aligned x, shift, scale; 8 | ldx): nothing
+// is launched then.
+int launch_head_adaln_gemm(const bf16_t *x, int64_t ldx, const float *shift, const float *scale,
+                           const bf16_t *W, int64_t ldw, const bf16_t *bias, float *out,
+                           int64_t ldo, int M, int N, int d, hipStream_t s);
+// Whether launch_head_adaln_gemm has a fused form for these arguments.
+bool head_adaln_gemm_fits(const bf16_t *x, int64_t ldx, const float *shift, const float *scale,
+                          int M, int N, int d);
 // The QKV product [q | k | v | qc] = A W^T + bias (N = 4d) with the Q/K RMSNorm + RoPE of
 // launch_qk_norm_rope applied in the product's epilogue (QkEpi; table rows are the M tokens),
 // bit-identical to the product followed by that kernel.  Returns 1 when launched, 0 when the

@@ -45,6 +45,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
@@ -85,7 +86,70 @@ struct GemmArgs {
   const bf16_t *bias, *bias2;
   float *part;  // split-K partials [S][M][N]
   QkEpi qk;     // QKV product with the Q/K RMSNorm + RoPE epilogue (QKD > 0)
+  // ALN > 0: AdaLN shift and scale [K] applied to the A rows as they are staged
+  const float *aln_shift = nullptr, *aln_scale = nullptr;
 };
+
+// ALN > 0 (the velocity head): A is the residual stream x [M, K = d] and the staged A tile is
+// the final AdaLN of it, n = bf16(((x - mean) rstd) (1 + scale) + shift), formed while the tile
+// is loaded (registers -> transform -> LDS) instead of read from a stored n.  The row statistics
+// are computed first, for the tile's rows, in the exact order of the AdaLN row kernel with ALN
+// waves per row (aln_row_stats), and the transform is that kernel's expression, so the staged
+// values are the bits the AdaLN kernel stores and the product equals AdaLN + product bit for bit.
+template <int ALN>
+__device__ __forceinline__ void aln_row_stats(const bf16_t *__restrict__ x, int64_t ldx, int d,
+                                              int row, int lane, float &mean, float &rstd) {
+#pragma clang fp contract(off)
+  // thread t of the AdaLN kernel's row holds the 8-channel chunks (i * 64 ALN + t) * 8; its
+  // waves' butterfly totals are added wave 0 first.  This wave plays those ALN waves in turn.
+  const bf16_t *xr = x + static_cast<int64_t>(row) * ldx;
+  const int vpl = d / (512 * ALN);
+  float tot[ALN];
+#pragma unroll
+  for (int h = 0; h < ALN; ++h) {
+    float sum = 0.f;
+    for (int i = 0; i < vpl; ++i) {
+      float v[8];
+      unpack8(*reinterpret_cast<const uint4 *>(xr + (i * 64 * ALN + h * 64 + lane) * 8), v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sum += v[k];
+    }
+    tot[h] = wave_sum(sum);
+  }
+  float ssum = tot[0];
+  if constexpr (ALN == 2) ssum = tot[0] + tot[1];
+  mean = ssum / static_cast<float>(d);
+#pragma unroll
+  for (int h = 0; h < ALN; ++h) {
+    float q = 0.f;
+    for (int i = 0; i < vpl; ++i) {
+      float v[8];
+      unpack8(*reinterpret_cast<const uint4 *>(xr + (i * 64 * ALN + h * 64 + lane) * 8), v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float c = v[k] - mean;
+        q += c * c;
+      }
+    }
+    tot[h] = wave_sum(q);
+  }
+  float qsum = tot[0];
+  if constexpr (ALN == 2) qsum = tot[0] + tot[1];
+  rstd = 1.0f / sqrtf(qsum / static_cast<float>(d) + kLnEps);
+}
+// One staged 8-channel chunk of the AdaLN output: the AdaLN row kernel's expression.
+__device__ __forceinline__ uint4 aln_chunk(const uint4 &xv, float mean, float rstd,
+                                           const float4 &sh0, const float4 &sh1, const float4 &sc0,
+                                           const float4 &sc1) {
+#pragma clang fp contract(off)
+  float v[8], o[8];
+  unpack8(xv, v);
+  const float sh[8] = {sh0.x, sh0.y, sh0.z, sh0.w, sh1.x, sh1.y, sh1.z, sh1.w};
+  const float sc[8] = {sc0.x, sc0.y, sc0.z, sc0.w, sc1.x, sc1.y, sc1.z, sc1.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = ((v[k] - mean) * rstd) * (1.0f + sc[k]) + sh[k];
+  return pack8(o);
+}
 
 // QKD > 0: the QKV product with heads of QKD channels; columns follow QkMap<BN, QKD> and the
 // epilogue applies the Q/K RMSNorm + RoPE to the q/k heads (bias, no GELU, bf16, unsplit).
@@ -94,9 +158,10 @@ struct GemmArgs {
 // one group alone has one), and the second group hands its accumulators to the first through
 // LDS before the partial tile is stored.
 template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0,
-          int KSG = 1>
+          int KSG = 1, int ALN = 0>
 __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(QKD == 0 || (EPI == H3_EPI_NONE && !OUT_F32 && SPLIT == 1), "QKV epilogue form");
+  static_assert(ALN == 0 || (QKD == 0 && KSG == 1 && SPLIT == 1 && NS == 3), "AdaLN A operand form");
   static_assert(KSG == 1 || (KSG == 2 && SPLIT > 1), "two K-step groups: split-K partial tiles only");
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT * KSG, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
@@ -105,7 +170,7 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
                 "the accumulator hand-over must fit the LDS");
   // static (its address is known when the kernel is compiled, so the constant parts of the
   // fragment addresses fold into the LDS instructions' offsets)
-  __shared__ __align__(16) unsigned char smem[Cfg::LDS_BYTES];
+  __shared__ __align__(16) unsigned char smem[Cfg::LDS_BYTES + (ALN > 0 ? 2 * BM * 4 : 0)];
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int tile_id = blockIdx.x / SPLIT;
@@ -170,18 +235,62 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
     }
   }
   constexpr int A_BYTES = NS * BM * 128;  // the B stages start here
+  // with ALN the A rows (the first LOADS_A row blocks of each wave) go through registers
+  constexpr int LOADS_A = ALN > 0 ? BM / 8 / NW : 0;
+  constexpr int LOADS_B = LOADS - LOADS_A;  // direct-to-LDS copies per wave per K slice
+  static_assert(ALN == 0 || (BM / 8) % NW == 0, "A row blocks must split evenly over waves");
   // copies K slice kt into stage S (a compile-time constant: the LDS targets are scalar)
   auto issue_slice = [&](int kt, auto stage) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     const uint32_t kb = static_cast<uint32_t>(kt * BK * 2);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
+    for (int i = LOADS_A; i < LOADS; ++i) {
       const int R0 = (i * NW + wave) * 8;
       const unsigned char *base = (R0 < BM ? abase : bbase) + kb;  // uniform
       const unsigned char *src = base + goff[i];
       lds_u8 *dst = (lds_u8 *)smem +
                     (R0 < BM ? S * BM * 128 + R0 * 128 : A_BYTES + S * BN * 128 + (R0 - BM) * 128);
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(dst), 16, 0, 0);
+    }
+  };
+
+  // ALN: row statistics of the tile's A rows (rows past M repeat row M - 1), then the A slices
+  // are loaded into registers (aload) and written to LDS transformed (astore)
+  float *s_stat = reinterpret_cast<float *>(smem + Cfg::LDS_BYTES);  // mean [BM], rstd [BM]
+  uint4 areg[LOADS_A > 0 ? LOADS_A : 1];
+  float4 ash[LOADS_A > 0 ? LOADS_A : 1][2], asc[LOADS_A > 0 ? LOADS_A : 1][2];
+  if constexpr (ALN > 0) {
+    for (int r = wave; r < BM; r += NW) {
+      float mean, rstd;
+      aln_row_stats<ALN>(g.A, g.lda, g.K, min(m0 + r, g.M - 1), lane, mean, rstd);
+      if (lane == 0) {
+        s_stat[r] = mean;
+        s_stat[BM + r] = rstd;
+      }
+    }
+    __syncthreads();
+  }
+  auto aload = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t kb = static_cast<uint32_t>(kt * BK * 2);
+#pragma unroll
+    for (int i = 0; i < LOADS_A; ++i) {
+      const int R = (i * NW + wave) * 8 + (lane >> 3);
+      const int col = kbeg + kt * BK + ((lane & 7) ^ ((R >> 1) & 7)) * 8;
+      areg[i] = *reinterpret_cast<const uint4 *>(abase + kb + goff[i]);
+      ash[i][0] = *reinterpret_cast<const float4 *>(g.aln_shift + col);
+      ash[i][1] = *reinterpret_cast<const float4 *>(g.aln_shift + col + 4);
+      asc[i][0] = *reinterpret_cast<const float4 *>(g.aln_scale + col);
+      asc[i][1] = *reinterpret_cast<const float4 *>(g.aln_scale + col + 4);
+    }
+  };
+  auto astore = [&](auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+#pragma unroll
+    for (int i = 0; i < LOADS_A; ++i) {
+      const int R = (i * NW + wave) * 8 + (lane >> 3);
+      const uint4 o = aln_chunk(areg[i], s_stat[R], s_stat[BM + R], ash[i][0], ash[i][1], asc[i][0], asc[i][1]);
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4_t *>(
+          (lds_u8 *)smem + S * BM * 128 + R * 128 + (lane & 7) * 16) = u32x4_t{o.x, o.y, o.z, o.w};
     }
   };
 
@@ -203,18 +312,33 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
   // NS-stage pipeline: slices kt+1 .. kt+NS-1 stream into LDS while slice kt feeds the MFMAs.
   // The K loop is unrolled over the stages, so each stage's offsets are compile-time constants.
   const int KT = kc / BK;
-  issue_slice(0, std::integral_constant<int, 0>{});
-  if constexpr (NS == 3)
-    if (KT > 1) issue_slice(1, std::integral_constant<int, 1>{});
-  if (KT >= NS - 1)
-    lds_dma_barrier<LOADS * (NS - 2)>();
-  else
-    lds_dma_barrier<0>();
+  if constexpr (ALN > 0) {
+    aload(0);
+    issue_slice(0, std::integral_constant<int, 0>{});
+    astore(std::integral_constant<int, 0>{});
+    if (KT > 1) {
+      aload(1);
+      issue_slice(1, std::integral_constant<int, 1>{});
+      astore(std::integral_constant<int, 1>{});
+    }
+    lds_dma_write_barrier<0>();
+  } else {
+    issue_slice(0, std::integral_constant<int, 0>{});
+    if constexpr (NS == 3)
+      if (KT > 1) issue_slice(1, std::integral_constant<int, 1>{});
+    if (KT >= NS - 1)
+      lds_dma_barrier<LOADS * (NS - 2)>();
+    else
+      lds_dma_barrier<0>();
+  }
 
   auto slice = [&](int kt, auto stage) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     const bool more = kt + NS - 1 < KT;
-    if (more) issue_slice(kt + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+    if (more) {
+      if constexpr (ALN > 0) aload(kt + NS - 1);
+      issue_slice(kt + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+    }
     auto afrag = [&](int i, int ks) {
       return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
           lds + ((a_lane ^ (32 * ks)) + S * BM * 128 + i * 4096));
@@ -256,10 +380,20 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
     }
     // slice kt+1 must be complete (later slices may still be in flight); every wave must be
     // done reading stage S before the next slice refills it
-    if (more)
-      lds_dma_barrier<LOADS * (NS - 2)>();
-    else
-      lds_dma_barrier<0>();
+    if constexpr (ALN > 0) {
+      // the A rows of slice kt + NS - 1, transformed into the stage this slice's loads target
+      // (its registers have landed: the loads were issued before this slice's MFMAs)
+      if (more) astore(std::integral_constant<int, (S + NS - 1) % NS>{});
+      if (more)
+        lds_dma_write_barrier<LOADS_B * (NS - 2)>();
+      else
+        lds_dma_write_barrier<0>();
+    } else {
+      if (more)
+        lds_dma_barrier<LOADS * (NS - 2)>();
+      else
+        lds_dma_barrier<0>();
+    }
   };
   for (int kt = 0; kt < KT; kt += NS) {
     slice(kt, std::integral_constant<int, 0>{});
@@ -436,11 +570,11 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0,
-          int KSG = 1>
+          int KSG = 1, int ALN = 0>
 void run_gemm(const GemmArgs &a, hipStream_t s) {
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD, KSG>;
+  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD, KSG, ALN>;
   kern<<<tiles * SPLIT, Cfg::NT * KSG, 0, s>>>(a);
 }
 
@@ -574,6 +708,31 @@ void qkv_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
   }
 }
 }  // namespace
+
+bool head_adaln_gemm_fits(const bf16_t *x, int64_t ldx, const float *shift, const float *scale,
+                          int M, int N, int d) {
+  // below 192 columns the plain product always takes the 128x128 unsplit tiles reproduced here
+  const GemmPlan p = plan_gemm(M, N, d);
+  return N < 192 && p.cfg == 0 && p.split == 1 && d % (512 * adaln_waves_per_row(M, d)) == 0 &&
+         ldx % 8 == 0 &&
+         reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(shift) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(scale) % 16 == 0;
+}
+
+int launch_head_adaln_gemm(const bf16_t *x, int64_t ldx, const float *shift, const float *scale,
+                           const bf16_t *W, int64_t ldw, const bf16_t *bias, float *out,
+                           int64_t ldo, int M, int N, int d, hipStream_t s) {
+  if (!head_adaln_gemm_fits(x, ldx, shift, scale, M, N, d)) return 0;
+  const int wpr = adaln_waves_per_row(M, d);
+  GemmArgs a{x, ldx, W, ldw, out, ldo, M, N, d, bias, nullptr, nullptr};
+  a.aln_shift = shift;
+  a.aln_scale = scale;
+  if (wpr == 2)
+    run_gemm<128, 128, 2, 2, 3, H3_EPI_NONE, 1, 1, 0, 1, 2>(a, s);
+  else
+    run_gemm<128, 128, 2, 2, 3, H3_EPI_NONE, 1, 1, 0, 1, 1>(a, s);
+  return 1;
+}
 
 int launch_gemm_bf16_qkv(const bf16_t *A, int64_t lda, const bf16_t *W, int64_t ldw,
                          const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int d, int K,

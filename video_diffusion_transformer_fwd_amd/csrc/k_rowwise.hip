@@ -18,15 +18,6 @@ namespace h3 {
 
 namespace {
 
-constexpr float kLnEps = 1e-6f;
-
-__device__ __forceinline__ float wave_sum(float v) {
-  // xor butterfly: lanes i and i^o add the same two values (commutative), so every lane ends
-  // with the identical total.
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -254,7 +245,7 @@ void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf
   // anyway and the second wave's LDS exchange only costs: measured at 61,488 rows)
   const dim3 grid1((rows + 3) / 4), block1(256), grid2(rows), block2(128);
   const int v512 = d / 512;
-  if (rows >= 16384 || v512 % 2) {
+  if (adaln_waves_per_row(rows, d) == 1) {
     switch (v512) {
 #define H3_CASE1(V)                                                                         \
   case V:                                                                                   \
