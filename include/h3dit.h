@@ -264,6 +264,17 @@ int32_t h3_quantize_linear_weights(const h3_model *m, void *stream);
 int32_t h3_modulation(const h3_model *m, float sigma, float *mod, float *mod_final, void *ws,
                       size_t ws_bytes, void *stream);
 
+/* h3_modulation without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, hosts that forbid allocation): the modulation MLP's
+ * intermediates (256 + 8 d_model floats) live in a static device buffer of 264 KiB inside the
+ * library, one per GPU, held until the process ends; nothing is allocated.  Same kernels and
+ * results as h3_modulation (bit for bit).  d_model <= 8192 (H3_ESHAPE above that).  Every
+ * intermediate is written before it is read, so the buffer needs no clearing; calls that
+ * overlap on one GPU (several streams or host threads at once) race on the buffer and must be
+ * serialised by the caller.  mod, mod_final as in h3_modulation. */
+int32_t h3_modulation_noalloc(const h3_model *m, float sigma, float *mod, float *mod_final,
+                              void *stream);
+
 /* One DiT block on the residual stream (P3 "DiT fusions and memory"):
  *   n1 = AdaLN(x; sh1, sc1) (or the caller's n1_in);  [q|k|v|qc] = n1 W_qkvq^T + b;
  *   q,k <- RoPE(RMSNorm(q)), RoPE(RMSNorm(k));  O = softmax(q k^T / sqrt(D)) v per head;

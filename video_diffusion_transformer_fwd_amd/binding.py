@@ -89,6 +89,7 @@ SIGNATURES = {
     "h3_quantize_fc2_weights": (_I32, [_VP, _VP]),
     "h3_quantize_linear_weights": (_I32, [_VP, _VP]),
     "h3_modulation": (_I32, [_VP, _F, _VP, _VP, _VP, _SZ, _VP]),
+    "h3_modulation_noalloc": (_I32, [_VP, _F, _VP, _VP, _VP]),
     "h3_dit_block_fwd": (_I32, [_VP, _I32, C.POINTER(h3_geom), C.POINTER(h3_run_opts), _VP, _VP,
                                 _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "h3_dit_forward": (_I32, [_VP, C.POINTER(h3_geom), C.POINTER(h3_run_opts), _VP, _F, _PI32,
@@ -289,6 +290,11 @@ def h3_quantize_linear_weights(m, stream=None):
 def h3_modulation(m, sigma, mod, mod_final, ws, stream=None):
     _check(lib().h3_modulation(m, sigma, ptr(mod, "f32"), ptr(mod_final, "f32"), ptr(ws), ws.numel() * ws.element_size(),
                                stream_handle(stream)))
+
+
+def h3_modulation_noalloc(m, sigma, mod, mod_final, stream=None):
+    _check(lib().h3_modulation_noalloc(m, sigma, ptr(mod, "f32"), ptr(mod_final, "f32"),
+                                       stream_handle(stream)))
 
 
 def h3_dit_block_fwd(m, block, geom, opts, x, n1_in, n1_next, mod, mod_next, ctx_kv, ws, stream=None):

@@ -5,12 +5,19 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
 
 #include "h3_internal.h"
 
+// Device scratch of h3_modulation_noalloc, for callers that cannot allocate device memory:
+// every GPU the library runs on holds one copy of it until the process ends.  Host code never
+// passes this name to a kernel (on the host it is only a stand-in for the symbol): it uses the
+// device address looked up once per device (static_scratch below).
+constexpr size_t kStaticScratchBytes = 264 * 1024;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 struct h3_model : h3::Model {};
 
@@ -490,6 +497,50 @@ int32_t h3_modulation(const h3_model *m, float sigma, float *mod, float *mod_fin
   if (!ws || ws_bytes < p.total) return fail(H3_EWORKSPACE, "h3_modulation: workspace too small");
   return run_modulation(m, sigma, mod, mod_final, reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + p.tmp),
                         as_stream(stream));
+}
+
+}  // extern "C"
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on the first call on each
+// device (with that device current) and kept.
+int32_t static_scratch(void **out, const char *who) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(H3_EHIP, std::string(who) + ": no current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(H3_EHIP, std::string(who) + ": device address of the static scratch: " +
+                               hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return H3_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t h3_modulation_noalloc(const h3_model *m, float sigma, float *mod, float *mod_final,
+                              void *stream) {
+  if (int32_t e = validate_model(m)) return e;
+  if (!mod || !mod_final) return fail(H3_EINVAL, "h3_modulation_noalloc: NULL output");
+  if (!std::isfinite(sigma)) return fail(H3_EINVAL, "h3_modulation_noalloc: sigma must be finite");
+  const size_t need = modulation_tmp_bytes(m->dims.d_model);
+  if (need > kStaticScratchBytes)
+    return fail(H3_ESHAPE, "h3_modulation_noalloc: d_model " + std::to_string(m->dims.d_model) +
+                               " needs " + std::to_string(need) + " bytes of scratch, above the " +
+                               std::to_string(kStaticScratchBytes) + "-byte static buffer");
+  void *sp = nullptr;
+  if (int32_t e = static_scratch(&sp, "h3_modulation_noalloc")) return e;
+  return run_modulation(m, sigma, mod, mod_final, reinterpret_cast<float *>(sp), as_stream(stream));
 }
 
 int32_t h3_dit_block_fwd(const h3_model *m, int32_t block, const h3_geom *geom,
