@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times), the "
                          "reference for scaling HBM byte counters")
+    ap.add_argument("--calibrate-mfma", choices=("bf16", "int8"), default=None,
+                    help="only run the matrix-core probe (dense MFMA rate at the running clock)")
+    ap.add_argument("--membound", action="store_true",
+                    help="only time the memory-bound kernels one by one at the workload's sizes")
     return ap.parse_args()
 
 
@@ -56,15 +60,121 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": mib * 2 ** 20, "copies": 5}))
 
 
-def traffic_for(kernel_src: str):
-    """HBM bytes per launch from the committed counter summary, if taken on this source."""
+def calibrate_mfma(kind: str):
+    """Times the matrix-core probe: two workgroups of four waves per CU, each wave issuing
+    rounds of eight independent 32x32 MFMAs with no memory traffic.  Prints the sustained rate
+    and the clock it implies (1024 bf16 FLOP, or 2048 int8 OP, per SIMD per cycle)."""
+    import torch
+    from video_diffusion_transformer_fwd_amd import binding as B
+    int8 = kind == "int8"
+    wgs, iters = 512, 40000
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+    B.h3_mfma_probe(int8, 100, wgs, out)
+    torch.cuda.synchronize()
+    per_instr = 65536.0 if int8 else 32768.0
+    ops = wgs * 4 * iters * 8 * per_instr
+    res = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.h3_mfma_probe(int8, iters, wgs, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        res.append(ms)
+    ms = sorted(res)[len(res) // 2]
+    rate = ops / (ms * 1e-3) / 1e12
+    simds, per_clk = 1024, (2048.0 if int8 else 1024.0)
+    print(json.dumps({"calibrate_mfma": kind, "ms": round(ms, 3), "ops_per_launch": ops,
+                      "rate_tops": round(rate, 1), "peak_spec_tops": PEAK_INT8_TOPS if int8 else PEAK_BF16_TFLOPS,
+                      "implied_clock_ghz": round(rate * 1e12 / (simds * per_clk) / 1e9, 3)}))
+
+
+def membound(w):
+    """The memory-bound kernels of the path, one at a time at the workload's sizes, through the
+    op-level entry points: median of 5 launches (HIP events), algorithmic bytes / time.  Inputs
+    are random device tensors; a plain device copy of the residual stream's size is the
+    reference rate."""
+    import torch
+    from video_diffusion_transformer_fwd_amd import binding as B
+    from video_diffusion_transformer_fwd_amd.runtime import Geometry
+    geo = Geometry(w)
+    n, d, F, C, D = geo.n_tokens, w.d_model, w.ffn_dim, w.latent_ch, w.head_dim
+    dev = "cuda"
+    bf = lambda *shape: torch.randn(*shape, device=dev).to(torch.bfloat16)
+    f32 = lambda *shape, s=0.2: torch.randn(*shape, device=dev) * s
+    x, y, xo, nn_ = bf(n, d), bf(n, d), bf(n, d), torch.empty(n, d, dtype=torch.bfloat16, device=dev)
+    gate, sh, sc = f32(d), f32(d), f32(d)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    out = []
+
+    def report(name, ms, nbytes):
+        rec = {"kernel": name, "us": round(ms * 1e3, 1), "bytes": int(nbytes),
+               "gb_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "frac_of_8tb": round(nbytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
+        out.append(rec)
+        print(json.dumps(rec), flush=True)
+
+    src = bf(n, d)
+    dst = torch.empty_like(src)
+    report("device copy (torch copy_) of [N, d] bf16", timed(lambda: dst.copy_(src)), 4 * n * d)
+    report("gate_adaln fused: x' = x + g y, AdaLN(x')",
+           timed(lambda: B.h3_gate_adaln(x, y, gate, xo, sh, sc, nn_)), 8 * n * d)
+    report("adaln", timed(lambda: B.h3_gate_adaln(x, None, None, None, sh, sc, nn_)), 4 * n * d)
+    report("gate only", timed(lambda: B.h3_gate_adaln(x, y, gate, xo, None, None, None)), 6 * n * d)
+    h = bf(n, F)
+    q8 = torch.empty(n, F, dtype=torch.int8, device=dev)
+    s_row = torch.empty(n, 1, dtype=torch.float32, device=dev)
+    report("quant_rows (row scale) of the FC2 input [N, F]",
+           timed(lambda: B.h3_quant_rows(h, q8, s_row, F)), 3 * n * F + 4 * n)
+    s_grp = torch.empty(n, F // 1024, dtype=torch.float32, device=dev)
+    report("quant_rows (1024-channel groups) of [N, F]",
+           timed(lambda: B.h3_quant_rows(h, q8, s_grp, 1024)), 3 * n * F + 4 * n * (F // 1024))
+    del h, q8
+    qkvq = bf(n, 4 * d)
+    table = torch.empty(n, D // 2, 2, dtype=torch.float32, device=dev)
+    B.h3_rope_table(geo.geom, D, table)
+    gq = (1 + 0.02 * torch.randn(D, device=dev)).to(torch.bfloat16)
+    gk = (1 + 0.02 * torch.randn(D, device=dev)).to(torch.bfloat16)
+    report("qk_norm_rope (unfused) on the q, k columns of [N, 4d]",
+           timed(lambda: B.h3_qk_norm_rope(qkvq, n, d, D, gq, gk, True, table)),
+           8 * n * d + n * (D // 2) * 8)
+    del qkvq
+    nr = geo.f_lat * geo.grid_h * ((geo.grid_w + 1) // 2)
+    xr = torch.empty(nr, d, dtype=torch.bfloat16, device=dev)
+    report("token merge [N, d] -> [N_r, d]", timed(lambda: B.h3_token_reduce(0, geo.geom, d, x, None, xr)),
+           2 * n * d + 2 * nr * d)
+    xs = x.clone()
+    report("token restore (bypass, in place)", timed(lambda: B.h3_token_reduce(1, geo.geom, d, xr, xs, xs)),
+           2 * nr * d + 4 * n * d)
+    lat, vel = f32(n, C, s=1.0), f32(n, C, s=1.0)
+    report("euler step [N, C] float32", timed(lambda: B.h3_euler_step(lat, vel, 0.75, 0.5)), 12 * n * C)
+    print(json.dumps({"membound": w.name, "tokens": n, "d_model": d, "ffn": F, "kernels": out}))
+
+
+def traffic_for(kernel_src: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if taken on this source and
+    this workload."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     src = open(os.path.join(ROOT, "video_diffusion_transformer_fwd_amd", "csrc", kernel_src), "rb").read()
-    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest() or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -122,6 +232,13 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.calibrate_mfma:
+        calibrate_mfma(args.calibrate_mfma)
+        return
+    if args.membound:
+        from video_diffusion_transformer_fwd_amd import synthetic as S
+        membound(S.WORKLOADS[args.workload])
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "runs on one GPU only: --gpus N > 1 is not supported (the "
@@ -245,7 +362,7 @@ def main():
                      "frac": round(achieved / peak, 4),
                      "flops_per_launch": fc1_flops, "avg_launch_ms": round(fc1_avg_ms, 5),
                      "launches": fc1_launches,
-                     "traffic": None if w.int8_linear else traffic_for("k_gemm.hip")},
+                     "traffic": None if w.int8_linear else traffic_for("k_gemm.hip", w.name)},
     }
     if not args.no_cpu:
         del model

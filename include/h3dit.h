@@ -460,6 +460,14 @@ int32_t h3_qkv_gemm(const void *A, int64_t lda, const float *SA, const void *W, 
                     const void *k_gamma, int32_t qk_norm, const void *table, int32_t a_q8,
                     int32_t fused, int32_t *fused_used, void *stream);
 
+/* Matrix-core throughput probe (measurement only, not part of the path): `workgroups`
+ * workgroups of four waves, each wave issuing `iters` rounds of eight independent 32x32 MFMAs
+ * on register operands -- bf16 (v_mfma_f32_32x32x16_bf16, 32768 FLOP each) or, with int8 = 1,
+ * int8 (v_mfma_i32_32x32x32_i8, 65536 OP each) -- with no memory traffic in the loop.  Timing
+ * it gives the dense matrix-core rate the GPU sustains at its running clock.  out (device,
+ * float [workgroups * 256]) receives per-thread sums.  iters >= 1, 1 <= workgroups <= 2^20. */
+int32_t h3_mfma_probe(int32_t int8, int32_t iters, int32_t workgroups, float *out, void *stream);
+
 /* ------------------------------------------------------------------------------------
  * Per-stage timing (HIP events recorded on the launch stream around every launch of the
  * selected stages).  One session per process; not thread-safe.  Inside a block the self- and

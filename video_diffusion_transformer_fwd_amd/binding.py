@@ -111,6 +111,7 @@ SIGNATURES = {
     "h3_qk_norm_rope": (_I32, [_VP, _I64, _I32, _I32, _I32, _VP, _VP, _I32, _VP, _VP]),
     "h3_qkv_gemm": (_I32, [_VP, _I64, _VP, _VP, _I64, _VP, _VP, _VP, _I64, _I32, _I32, _I32, _I32,
                            _VP, _VP, _I32, _VP, _I32, _I32, _PI32, _VP]),
+    "h3_mfma_probe": (_I32, [_I32, _I32, _I32, _VP, _VP]),
     "h3_profile_begin": (_I32, [C.c_uint32, _I32]),
     "h3_profile_end": (_I32, [C.POINTER(C.c_double), _PI32]),
 }
@@ -419,6 +420,12 @@ def h3_qk_norm_rope(qkvq, n_tokens, d_model, head_dim, q_gamma, k_gamma, qk_norm
     _check(lib().h3_qk_norm_rope(ptr(qkvq, "bf16"), qkvq.stride(0), n_tokens, d_model, head_dim,
                                  ptr(q_gamma, "bf16"), ptr(k_gamma, "bf16"), int(qk_norm), ptr(table, "f32"),
                                  stream_handle(stream)))
+
+
+def h3_mfma_probe(int8, iters, workgroups, out, stream=None):
+    if out.numel() < workgroups * 256:
+        raise ValueError("h3_mfma_probe: out needs workgroups * 256 floats")
+    _check(lib().h3_mfma_probe(int(int8), iters, workgroups, ptr(out, "f32"), stream_handle(stream)))
 
 
 def h3_profile_begin(stages, max_launches=100000):

@@ -30,7 +30,7 @@ COMMON = [
 ]
 
 SOURCES = ["h3_host.cpp", "h3_api.cpp", "h3_profile.cpp", "k_rowwise.hip", "k_gemm.hip", "k_gemm_i8.hip",
-           "k_attn.hip"]
+           "k_attn.hip", "k_probe.hip"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -901,6 +901,15 @@ int32_t h3_head_adaln_gemm(const void *x, const float *shift, const float *scale
   return check_launch("h3_head_adaln_gemm");
 }
 
+int32_t h3_mfma_probe(int32_t int8, int32_t iters, int32_t workgroups, float *out, void *stream) {
+  if (int8 != 0 && int8 != 1) return fail(H3_EINVAL, "h3_mfma_probe: int8 must be 0 or 1");
+  if (!out) return fail(H3_EINVAL, "h3_mfma_probe: out is NULL");
+  if (iters < 1 || workgroups < 1 || workgroups > (1 << 20))
+    return fail(H3_ESHAPE, "h3_mfma_probe: iters must be >= 1 and workgroups in [1, 2^20]");
+  launch_mfma_probe(int8, iters, workgroups, out, as_stream(stream));
+  return check_launch("h3_mfma_probe");
+}
+
 int32_t h3_rope_table(const h3_geom *geom, int32_t head_dim, void *table, void *stream) {
   int32_t n = 0;
   if (int32_t e = h3_geom_tokens(geom, &n)) return e;

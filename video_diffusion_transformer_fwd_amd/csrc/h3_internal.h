@@ -326,6 +326,9 @@ void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const f
 int launch_head_adaln_gemm(const bf16_t *x, int64_t ldx, const float *shift, const float *scale,
                            const bf16_t *W, int64_t ldw, const bf16_t *bias, float *out,
                            int64_t ldo, int M, int N, int d, hipStream_t s);
+// Matrix-core probe: `workgroups` workgroups of four waves, each wave issuing `iters` rounds of
+// eight independent 32x32 bf16 (int8 = 0) or int8 (int8 = 1) MFMAs; out: float [workgroups * 256].
+void launch_mfma_probe(int int8, int iters, int workgroups, float *out, hipStream_t s);
 // Whether launch_head_adaln_gemm has a fused form for these arguments.
 bool head_adaln_gemm_fits(const bf16_t *x, int64_t ldx, const float *shift, const float *scale,
                           int M, int N, int d);
