@@ -1,0 +1,92 @@
+"""GPU parity of the whole denoise loop at full depth against the oracle, at the 512x512x22-frame
+shape (1536 tokens, d = 3072, 50 blocks):
+
+  * 512sq_22f       --steps 4 --reuse 1, all 50 blocks, bf16 FC2 (P2 §2: the four-pass run);
+  * 512sq_22f_int8  the same loop with the per-row int8 FC2 (P2 §4, P4 §4);
+  * 512sq_22f_tr    --steps 20 --layers 45 --reuse 2 with token pairing (P2 §4, P3
+                    "aggressive levers"): 11 fresh evaluations, 1536 -> 768 tokens.
+
+The oracle's loops are stored by ``tests/golden/make_full_depth.py`` (float64 oracle on the same
+seeded model; minutes of CPU per loop).  Bars: the velocity of every fresh evaluation within
+rel-L2 2e-2 of the oracle's on its own trajectory; the latent after the loop and the part the
+loop changed, x_N - x_0, within 5e-2.  So that the bars are known to resolve the blocks, the
+oracle's loop without any block (patch -> head on every evaluation: what zero gates give) must
+lie at least 5 times the GPU's error away from the oracle's loop.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dit
+from tests.golden import make_full_depth as golden
+from tests.gpu_util import f64, rel_l2
+from tests.oracle_model import oracle_active, oracle_geom, oracle_model
+from video_diffusion_transformer_fwd_amd import binding as B
+from video_diffusion_transformer_fwd_amd import synthetic as S
+from video_diffusion_transformer_fwd_amd.runtime import DiTModel
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("512sq_22f", "512sq_22f_int8", "512sq_22f_tr")
+
+
+@pytest.fixture(scope="module")
+def model():
+    # one resident model serves the three loops: they share the shape, the seed and so every
+    # weight; the int8 FC2 copies are made once
+    m = DiTModel(S.WORKLOADS["512sq_22f"], with_int8=True)
+    yield m
+    m.close()
+
+
+@pytest.fixture(scope="module")
+def oracle_globals():
+    return oracle_model(S.WORKLOADS["512sq_22f"], blocks=[])
+
+
+def run_loop(model, w, active, opts):
+    """The GPU loop through h3_dit_forward / h3_euler_step, keeping each fresh velocity."""
+    sig, fresh, _ = B.h3_schedule(w.steps, w.reuse, 1)
+    lat0 = model.initial_latent()
+    x = lat0.clone()
+    v = torch.empty((model.geo.n_tokens, w.latent_ch), dtype=torch.float32, device=model.device)
+    vel, ev = [], 0
+    for i in range(w.steps):
+        if fresh[i]:
+            model.forward(x, float(sig[i]), active, ev, opts, v)
+            ev += 1
+            vel.append(f64(v))
+        B.h3_euler_step(x, v, float(sig[i]), float(sig[i + 1]))
+    torch.cuda.synchronize()
+    return f64(lat0), f64(x), vel
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_depth_loop(model, oracle_globals, name):
+    rec = golden.load(name)
+    if rec is None:
+        pytest.fail(f"tests/golden/full_depth_{name}.npz is missing: run tests/golden/make_full_depth.py")
+    vel_ref, x_ref, meta = rec
+    w = S.WORKLOADS[name]
+    geo = oracle_geom(w)
+    active = oracle_active(w, oracle_globals)
+    assert meta["active"] == active and meta["n_fresh"] == len(vel_ref)
+    assert (model.geo.f_lat, model.geo.grid_h, model.geo.grid_w, model.geo.n_tokens) == \
+        (geo["f_lat"], geo["grid_h"], geo["grid_w"], geo["n"])
+    assert model.active(w.n_active) == active
+    opts = model.opts(fc2_mode=w.fc2_mode, token_reduction=w.token_reduction)
+    lat0, x, vel = run_loop(model, w, active, opts)
+    assert len(vel) == len(vel_ref)
+    assert np.isfinite(x).all()
+    errs = [rel_l2(g, r) for g, r in zip(vel, vel_ref)]
+    e_lat = rel_l2(x, x_ref)
+    e_delta = rel_l2(x - lat0, x_ref - lat0)
+    print(f"{name}: velocity rel-L2 per evaluation {['%.2e' % e for e in errs]}, "
+          f"latent {e_lat:.2e}, x_N - x_0 {e_delta:.2e}")
+    assert max(errs) <= 2e-2, errs
+    assert e_lat <= 5e-2 and e_delta <= 5e-2, (e_lat, e_delta)
+    # the loop with no block at all, from the oracle: far outside the GPU's error
+    x0_ref, _ = dit.denoise(lat0, oracle_globals, w.steps, w.reuse, [], geo, w.n_heads)
+    d_lat, d_delta = rel_l2(x0_ref, x_ref), rel_l2(x0_ref - lat0, x_ref - lat0)
+    print(f"{name}: no-block loop vs oracle: latent {d_lat:.2e}, x_N - x_0 {d_delta:.2e}")
+    assert d_lat >= 5 * e_lat and d_delta >= 5 * e_delta, (d_lat, e_lat, d_delta, e_delta)
