@@ -7,11 +7,18 @@ shape (1536 tokens, d = 3072, 50 blocks):
                     "aggressive levers"): 11 fresh evaluations, 1536 -> 768 tokens.
 
 The oracle's loops are stored by ``tests/golden/make_full_depth.py`` (float64 oracle on the same
-seeded model; minutes of CPU per loop).  Bars: the velocity of every fresh evaluation within
-rel-L2 2e-2 of the oracle's on its own trajectory; the latent after the loop and the part the
-loop changed, x_N - x_0, within 5e-2.  So that the bars are known to resolve the blocks, the
-oracle's loop without any block (patch -> head on every evaluation: what zero gates give) must
-lie at least 5 times the GPU's error away from the oracle's loop.
+seeded model; minutes of CPU per loop).  Bars: the latent after the loop and the part the loop
+changed, x_N - x_0, within rel-L2 5e-2; the velocity of every fresh evaluation within 2e-2 of
+the oracle's on its own trajectory (5e-2 with the int8 FC2, below).  So that the bars are known
+to resolve the blocks, the oracle's loop without any block (patch -> head on every evaluation:
+what zero gates give) must lie at least 5 times the GPU's error away from the oracle's loop.
+
+The int8 FC2's quantiser is discontinuous in its input: the GPU quantises the bf16 FC2 input it
+stores, the oracle its float64 one, and bf16 rounding moves h / s by up to ~127 * 2^-9 ~ 0.25 of
+a step, so a share of the codes differ by one step.  Over 50 blocks that leaves the velocities
+2.7-3.0e-2 apart -- as far as the oracle's own int8 loop is from its bf16 loop (2.4-2.6e-2) --
+so there the per-evaluation velocity takes the loop's 5e-2 bar.  The int8 arithmetic itself is
+checked bit for bit on identical inputs and per block at 2e-2 elsewhere.
 """
 import numpy as np
 import pytest
@@ -20,7 +27,7 @@ import torch
 from oracle import dit
 from tests.golden import make_full_depth as golden
 from tests.gpu_util import f64, rel_l2
-from tests.oracle_model import oracle_active, oracle_geom, oracle_model
+from tests.oracle_model import oracle_active, oracle_geom, oracle_latent, oracle_model
 from video_diffusion_transformer_fwd_amd import binding as B
 from video_diffusion_transformer_fwd_amd import synthetic as S
 from video_diffusion_transformer_fwd_amd.runtime import DiTModel
@@ -28,6 +35,7 @@ from video_diffusion_transformer_fwd_amd.runtime import DiTModel
 pytestmark = pytest.mark.gpu
 
 NAMES = ("512sq_22f", "512sq_22f_int8", "512sq_22f_tr")
+VELOCITY_BAR = {"512sq_22f": 2e-2, "512sq_22f_int8": 5e-2, "512sq_22f_tr": 2e-2}
 
 
 @pytest.fixture(scope="module")
@@ -83,10 +91,13 @@ def test_full_depth_loop(model, oracle_globals, name):
     e_delta = rel_l2(x - lat0, x_ref - lat0)
     print(f"{name}: velocity rel-L2 per evaluation {['%.2e' % e for e in errs]}, "
           f"latent {e_lat:.2e}, x_N - x_0 {e_delta:.2e}")
-    assert max(errs) <= 2e-2, errs
+    assert max(errs) <= VELOCITY_BAR[name], errs
     assert e_lat <= 5e-2 and e_delta <= 5e-2, (e_lat, e_delta)
-    # the loop with no block at all, from the oracle: far outside the GPU's error
-    x0_ref, _ = dit.denoise(lat0, oracle_globals, w.steps, w.reuse, [], geo, w.n_heads)
+    # the loop with no block at all, from the oracle (its own copy of the seeded latent): far
+    # outside the GPU's error
+    lat_o = oracle_latent(w)
+    assert np.array_equal(lat_o, lat0)
+    x0_ref, _ = dit.denoise(lat_o, oracle_globals, w.steps, w.reuse, [], geo, w.n_heads)
     d_lat, d_delta = rel_l2(x0_ref, x_ref), rel_l2(x0_ref - lat0, x_ref - lat0)
     print(f"{name}: no-block loop vs oracle: latent {d_lat:.2e}, x_N - x_0 {d_delta:.2e}")
     assert d_lat >= 5 * e_lat and d_delta >= 5 * e_delta, (d_lat, e_lat, d_delta, e_delta)
