@@ -44,6 +44,9 @@ def parse():
                     help="only run the matrix-core probe (dense MFMA rate at the running clock)")
     ap.add_argument("--membound", action="store_true",
                     help="only time the memory-bound kernels one by one at the workload's sizes")
+    ap.add_argument("--vendor-gemm", default=None, metavar="M,N,K",
+                    help="only time one bf16 product of this shape with h3_gemm_bf16 and with "
+                         "PyTorch's F.linear (the vendor library), for comparison")
     return ap.parse_args()
 
 
@@ -165,6 +168,35 @@ def membound(w):
     print(json.dumps({"membound": w.name, "tokens": n, "d_model": d, "ffn": F, "kernels": out}))
 
 
+def vendor_gemm(shape: str):
+    """One product C = A W^T + b ([M, K] x [N, K]) by h3_gemm_bf16 and by torch F.linear (which
+    dispatches to the vendor GEMM library on this platform): median of 5 launches each."""
+    import torch
+    import torch.nn.functional as F
+    from video_diffusion_transformer_fwd_amd import binding as B
+    M, N, K = (int(v) for v in shape.split(","))
+    A = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+    W = (torch.randn(N, K, device="cuda") * 0.02).to(torch.bfloat16)
+    b = (torch.randn(N, device="cuda") * 0.02).to(torch.bfloat16)
+    C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    res = {}
+    for name, fn in (("h3_gemm_bf16", lambda: B.h3_gemm_bf16(A, W, C, bias=b)),
+                     ("torch F.linear", lambda: F.linear(A, W, b))):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[2]
+        res[name] = {"ms": round(ms, 4), "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+    print(json.dumps({"vendor_gemm": [M, N, K], **res}))
+
+
 def traffic_for(kernel_src: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if taken on this source and
     this workload."""
@@ -235,6 +267,9 @@ def main():
         return
     if args.calibrate_mfma:
         calibrate_mfma(args.calibrate_mfma)
+        return
+    if args.vendor_gemm:
+        vendor_gemm(args.vendor_gemm)
         return
     if args.membound:
         from video_diffusion_transformer_fwd_amd import synthetic as S

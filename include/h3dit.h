@@ -209,14 +209,15 @@ typedef struct h3_run_opts {
                                * sums the products' split-K partials itself; 0: there they are
                                * not written (nothing downstream reads them).  Results are
                                * identical either way. */
-  int32_t fused_head_adaln;   /* 1: the final AdaLN runs inside the velocity head's product, applied
-                               * to the residual rows as its tiles are staged (P3 "DiT fusions and
+  int32_t fused_head_adaln;   /* Where the final AdaLN is not already computed by the last block's
+                               * MLP gate (after a bypass restore before the head, or for a cached
+                               * core): 1: it runs inside the velocity head's product, applied to
+                               * the residual rows as its tiles are staged (P3 "DiT fusions and
                                * memory": the final heads apply AdaLN while loading their
                                * projection tiles; h3_head_adaln_gemm), where the head's tiling
-                               * allows it (latent_ch < 192); the last block's MLP gate then
-                               * stores no AdaLN.  0: the last block's MLP gate computes the
-                               * final AdaLN (or the AdaLN kernel, after a bypass restore or a
-                               * cached core) and the head reads it.  Bit-identical. */
+                               * allows it (latent_ch < 192); 0: the AdaLN kernel, then the head.
+                               * Bit-identical.  The fused form is the slower of the two at these
+                               * sizes (few tiles; measured), so callers leave it 0. */
 } h3_run_opts;
 
 /* Tokens of a geometry (validates it). */

@@ -267,7 +267,7 @@ def test_core_reuse_cached_forward(tr):
     torch.cuda.synchronize()
     assert rel_l2(f64(v_reuse), f64(v_fresh)) < 1e-3
     # the final AdaLN inside the head product or as its own kernel: the same bits
-    opts_u = model.opts(token_reduction=tr, fused_head_adaln=False)
+    opts_u = model.opts(token_reduction=tr, fused_head_adaln=True)
     v_reuse_u = model.forward_cached(lat, 0.6, False, delta, active, 2, opts_u)
     v_plain_u = model.forward(lat, 0.6, active, 2, opts_u)
     torch.cuda.synchronize()

@@ -245,7 +245,7 @@ def h3_geom_tokens(geom: h3_geom) -> int:
 
 def make_opts(fc2_mode="bf16", fused_gate_adaln=True, fused_cross_block=True, qk_norm=True,
               token_reduction=False, int8_linear=False, fused_qk_rope=True, store_branches=False,
-              fused_head_adaln=True):
+              fused_head_adaln=False):
     return h3_run_opts(FC2_MODES[fc2_mode] if isinstance(fc2_mode, str) else fc2_mode,
                        int(fused_gate_adaln), int(fused_cross_block), int(qk_norm),
                        int(token_reduction), int(int8_linear), int(fused_qk_rope),

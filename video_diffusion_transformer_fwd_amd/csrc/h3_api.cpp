@@ -571,9 +571,10 @@ namespace {
 enum CoreMode { kCorePlain = 0, kCoreFresh = 1, kCoreReuse = 2 };
 
 // The velocity head v = AdaLN_final(x) W_h^T + b_h, float32 [n, C].  n_final: the final AdaLN,
-// already stored (the last block's MLP gate computed it), or NULL: then it is formed here,
-// inside the head product's tile loads when o.fused_head_adaln is set and the product has
-// that form, else by the AdaLN kernel into `scratch` (bf16 [n, d]) before the product.
+// already stored (the last block's MLP gate computed it, which costs nothing extra), or NULL
+// (after a bypass restore before the head, or for a cached core): then it is formed here,
+// inside the head product's tile loads when o.fused_head_adaln is set and the product has that
+// form, else by the AdaLN kernel into `scratch` (bf16 [n, d]) before the product.
 void run_head(const h3_model *m, const h3_run_opts &o, const bf16_t *x, const bf16_t *n_final,
               const float *fin, float *velocity, int n, void *scratch, hipStream_t s) {
   const int d = m->dims.d_model, C = m->dims.latent_ch;
@@ -708,7 +709,7 @@ static int32_t forward_impl(const h3_model *m, const h3_geom *geom, const h3_run
     if (!last && !token_op_next) {
       mnext = mod + static_cast<size_t>(active[pos + 1]) * 6 * d;
       n1n = n1_other;
-    } else if (last && !restore_before_head && !o->fused_head_adaln) {
+    } else if (last && !restore_before_head) {
       mnext = fin;
       n1n = n1_other;
     }
