@@ -157,12 +157,20 @@ __device__ __forceinline__ uint4 aln_chunk(const uint4 &xv, float mean, float rs
 // each group takes half of the 16-wide K steps of every staged slice (two waves per SIMD where
 // one group alone has one), and the second group hands its accumulators to the first through
 // LDS before the partial tile is stored.
+// XBO (the K loop without ALN): the MFMAs of every slice's last K step are issued after the
+// slice's barrier, from fragments already in registers, so the matrix cores stay busy while
+// the next slice's first fragments are read.  XBO = 1 issues them before the next slice's
+// copies, XBO = 2 after them.  Measured in the 512x512x22f denoise step (weights streaming from
+// HBM): the 192x192 split-K products gain most with 1 (-5.6%), the 384x192 products with 2
+// (-2%; with 1 they lose 2%), and the 256x256 products of 61,488 rows with 2.  Every
+// accumulator sees its K steps in the same order either way, so the results do not change.
 template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0,
-          int KSG = 1, int ALN = 0>
+          int KSG = 1, int ALN = 0, int XBO = 1>
 __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(QKD == 0 || (EPI == H3_EPI_NONE && !OUT_F32 && SPLIT == 1), "QKV epilogue form");
   static_assert(ALN == 0 || (QKD == 0 && KSG == 1 && SPLIT == 1 && NS == 3), "AdaLN A operand form");
   static_assert(KSG == 1 || (KSG == 2 && SPLIT > 1), "two K-step groups: split-K partial tiles only");
+  static_assert(XBO == 1 || XBO == 2, "cross-barrier order");
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT * KSG, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
   constexpr int KS_PER = BK / 16 / KSG;  // K steps per slice and wave
@@ -332,13 +340,21 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
       lds_dma_barrier<0>();
   }
 
+  // without ALN the last K step of each slice is held across the slice's barrier (XBO above);
+  // fragment buffer 1 holds that step (KS_PER is even), buffer 0 the next slice's first step
+  constexpr bool XB = ALN == 0;
+  static_assert(KS_PER % 2 == 0, "the last K step's fragments must sit in buffer 1");
+  bf16x8_t af[2][TM], bfr[2][TN];
+  auto held_step = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[1][j], af[1][i], acc[i][j], 0, 0, 0);
+  };
   auto slice = [&](int kt, auto stage) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
     const bool more = kt + NS - 1 < KT;
-    if (more) {
-      if constexpr (ALN > 0) aload(kt + NS - 1);
-      issue_slice(kt + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
-    }
     auto afrag = [&](int i, int ks) {
       return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
           lds + ((a_lane ^ (32 * ks)) + S * BM * 128 + i * 4096));
@@ -347,14 +363,28 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
       return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
           lds + ((b_lane ^ (32 * ks)) + S * BN * 128 + j * 4096));
     };
-    bf16x8_t af[2][TM], bfr[2][TN];
+    if constexpr (!XB) {
+      if (more) {
+        aload(kt + NS - 1);
+        issue_slice(kt + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+      }
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) af[0][i] = afrag(i, 0);
 #pragma unroll
     for (int j = 0; j < TN; ++j) bfr[0][j] = bfrag(j, 0);
+    if constexpr (XB && XBO == 1) {
+      if (kt > 0) held_step();
+      if (more) issue_slice(kt + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+    } else if constexpr (XB) {
+      if (more) issue_slice(kt + NS - 1, std::integral_constant<int, (S + NS - 1) % NS>{});
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt > 0) held_step();
+    }
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int KS_MMA = XB ? KS_PER - 1 : KS_PER;  // K steps whose MFMAs issue in this slice
 #pragma unroll
-    for (int ks = 0; ks < KS_PER; ++ks) {
+    for (int ks = 0; ks < KS_MMA; ++ks) {
       const int cur = ks & 1;
       if (ks + 1 < KS_PER) {
 #pragma unroll
@@ -379,7 +409,8 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
       }
     }
     // slice kt+1 must be complete (later slices may still be in flight); every wave must be
-    // done reading stage S before the next slice refills it
+    // done reading stage S before the next slice refills it (with XB that includes the held
+    // step's fragment reads, hence the LDS-count wait)
     if constexpr (ALN > 0) {
       // the A rows of slice kt + NS - 1, transformed into the stage this slice's loads target
       // (its registers have landed: the loads were issued before this slice's MFMAs)
@@ -390,9 +421,9 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
         lds_dma_write_barrier<0>();
     } else {
       if (more)
-        lds_dma_barrier<LOADS * (NS - 2)>();
+        lds_dma_write_barrier<LOADS * (NS - 2)>();
       else
-        lds_dma_barrier<0>();
+        lds_dma_write_barrier<0>();
     }
   };
   for (int kt = 0; kt < KT; kt += NS) {
@@ -400,6 +431,9 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
     if (kt + 1 < KT) slice(kt + 1, std::integral_constant<int, 1>{});
     if constexpr (NS == 3)
       if (kt + 2 < KT) slice(kt + 2, std::integral_constant<int, 2>{});
+  }
+  if constexpr (XB) {
+    if (KT > 0) held_step();
   }
 
   // lane holds C[m_l][n_l + 8q + e], e = 0..3, in accumulator registers 4q + e of each 32x32 block
@@ -570,11 +604,11 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLIT, int QKD = 0,
-          int KSG = 1, int ALN = 0>
+          int KSG = 1, int ALN = 0, int XBO = 1>
 void run_gemm(const GemmArgs &a, hipStream_t s) {
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD, KSG, ALN>;
+  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, NS, EPI, OUT_F32, SPLIT, QKD, KSG, ALN, XBO>;
   kern<<<tiles * SPLIT, Cfg::NT * KSG, 0, s>>>(a);
 }
 
@@ -616,9 +650,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 
 // One product: the tiled GEMM, then (split-K) the ordered reduction with the epilogue.
 // split-K products run with two K-step groups (two waves per SIMD)
-template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int S>
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int S, int XBO = 1>
 void run_product(const GemmArgs &a, hipStream_t s) {
-  run_gemm<BM, BN, WM, WN, NS, EPI, OUT_F32, S, 0, (S > 1 ? 2 : 1)>(a, s);
+  run_gemm<BM, BN, WM, WN, NS, EPI, OUT_F32, S, 0, (S > 1 ? 2 : 1), 0, XBO>(a, s);
   if constexpr (S > 1) {
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
     splitk_reduce_kernel<EPI, OUT_F32, S><<<static_cast<int>((total / 4 + 255) / 256), 256, 0, s>>>(
@@ -629,8 +663,8 @@ void run_product(const GemmArgs &a, hipStream_t s) {
 template <int EPI, int OUT_F32>
 void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
   switch (p.cfg * 8 + p.split) {
-    case 4 * 8 + 1: run_product<384, 192, 4, 2, 2, EPI, OUT_F32, 1>(a, s); break;
-    case 2 * 8 + 1: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 1>(a, s); break;
+    case 4 * 8 + 1: run_product<384, 192, 4, 2, 2, EPI, OUT_F32, 1, 2>(a, s); break;
+    case 2 * 8 + 1: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 1, 2>(a, s); break;
     case 1 * 8 + 1: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
     case 1 * 8 + 2: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s); break;
     case 1 * 8 + 4: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 4>(a, s); break;
@@ -701,8 +735,8 @@ namespace {
 template <int QKD>
 void qkv_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
   switch (p.cfg) {
-    case 4: run_gemm<384, 192, 4, 2, 2, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
-    case 2: run_gemm<256, 256, 2, 4, 2, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
+    case 4: run_gemm<384, 192, 4, 2, 2, H3_EPI_NONE, 0, 1, QKD, 1, 0, 2>(a, s); break;
+    case 2: run_gemm<256, 256, 2, 4, 2, H3_EPI_NONE, 0, 1, QKD, 1, 0, 2>(a, s); break;
     case 1: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
     default: run_gemm<128, 128, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
   }
