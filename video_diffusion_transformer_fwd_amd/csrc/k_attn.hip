@@ -41,6 +41,7 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 constexpr int kBlockN = 64;   // keys per tile
 constexpr float kLazy = 8.0f; // log2 headroom of the lazily moved softmax reference
+constexpr float kLazyBound = 256.0f;  // 2^kLazy
 
 // LDS layout of a staged K or V tile: 64 key rows of D bf16, unpadded (2D bytes a row, so one
 // 256-byte bank line holds 256 / 2D rows).  The 16-byte unit u of bank line `line` sits in
@@ -279,6 +280,11 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
     // score s, c = log2(e) / sqrt(D) and m a running reference maximum in raw units.  The
     // reference only moves up when some lane's tile maximum exceeds it by more than
     // kLazy / c (p stays <= 2^kLazy); O and l are rescaled then, which leaves O / l exact.
+    // A tile is first exponentiated against the current reference: if every lane's sum of p
+    // stays within 2^kLazy, no p exceeds it, so the reference would not move and the tile
+    // needs no maximum.  Otherwise (the first tile of a wave, a score far above the
+    // reference, or many near it) the maximum is taken and the reference moved as above, and
+    // the exponentials are redone if it moved.
     if (kv0 + kBlockN > nk) {  // keys beyond n_k (last tile only)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -288,36 +294,45 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attention_kern
           if (key >= nk) s[kb][i] = -INFINITY;
         }
     }
-    float mt = -INFINITY;
+    f32x16_t p[2];
+    float psum;
+    auto exponentiate = [&](float mc) __attribute__((always_inline)) {
+      psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool raise = mt * scale_log2 > m_ref * scale_log2 + kLazy;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform: rare after the first tiles
-      const float m_new = raise ? mt : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
-      l_run *= alpha;
+        for (int i = 0; i < 16; ++i) {
+          p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], scale_log2, -mc));
+          psum += p[kb][i];
+        }
+    };
+    // (m_ref = -inf makes every p +inf or NaN here, so a wave's first tile takes the slow path)
+    exponentiate(m_ref * scale_log2);
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kLazyBound)) != 0) {  // wave-uniform, rare
+      float mt = -INFINITY;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m_ref = m_new;
-    }
-    // (with two key groups a wave may have seen no key yet (n_k <= 64): then every score and the
-    // reference are -inf, and P must come out 0 rather than 2^(-inf + inf))
-    const float mc = KG == 1 || m_ref != -INFINITY ? m_ref * scale_log2 : 0.f;
-    float psum = 0.f;
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const bool raise = mt * scale_log2 > m_ref * scale_log2 + kLazy;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? mt : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * scale_log2);
+        l_run *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], scale_log2, -mc));
-        s[kb][i] = p;
-        psum += p;
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        m_ref = m_new;
       }
+      // (with two key groups a wave may have seen no key yet (n_k <= 64): then every score and
+      // the reference are -inf, and P must come out 0 rather than 2^(-inf + inf))
+      exponentiate(KG == 1 || m_ref != -INFINITY ? m_ref * scale_log2 : 0.f);
+    }
     l_run += psum;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = p[kb];
 
     // O^T += V^T P^T over 4 steps of 16 keys; the V^T fragments of step st + 1 are read while
     // step st's MFMAs run
