@@ -35,6 +35,10 @@ def sync():
     (4100, 2304, 256, 0, 0, 0),     # 256x256 tiles, ragged M
     (4100, 2100, 128, 1, 0, 0),     # 256x256 tiles, ragged M and N, GELU
     (1601, 8300, 256, 1, 0, 1),     # 384x192 tiles, ragged M and N, GELU, two biases
+    (1536, 8192, 64, 1, 0, 0),      # 384x192 tiles, one K slice (its held last step only)
+    (1700, 8448, 192, 0, 1, 0),     # 384x192 tiles, odd slice count, float32 out
+    (4100, 2048, 64, 0, 0, 0),      # 256x256 tiles, one K slice
+    (900, 640, 320, 1, 0, 0),       # 192x192 tiles (three stages), five slices
 ])
 def test_gemm_bf16(M, N, K, epi, f32, two_bias):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
