@@ -3,22 +3,27 @@ shape (1536 tokens, d = 3072, 50 blocks):
 
   * 512sq_22f       --steps 4 --reuse 1, all 50 blocks, bf16 FC2 (P2 §2: the four-pass run);
   * 512sq_22f_int8  the same loop with the per-row int8 FC2 (P2 §4, P4 §4);
+  * 512sq_22f_int8g the same loop with the grouped int8 FC2 (one activation scale per 1024
+                    channels);
+  * 512sq_22f_int8_all  the same loop with int8 QKV and FC1 as well (P3 "the int8 path");
   * 512sq_22f_tr    --steps 20 --layers 45 --reuse 2 with token pairing (P2 §4, P3
                     "aggressive levers"): 11 fresh evaluations, 1536 -> 768 tokens.
 
 The oracle's loops are stored by ``tests/golden/make_full_depth.py`` (float64 oracle on the same
 seeded model; minutes of CPU per loop).  Bars: the latent after the loop and the part the loop
 changed, x_N - x_0, within rel-L2 5e-2; the velocity of every fresh evaluation within 2e-2 of
-the oracle's on its own trajectory (5e-2 with the int8 FC2, below).  So that the bars are known
+the oracle's on its own trajectory (5e-2 with int8 products, below).  So that the bars are known
 to resolve the blocks, the oracle's loop without any block (patch -> head on every evaluation:
 what zero gates give) must lie at least 5 times the GPU's error away from the oracle's loop.
 
-The int8 FC2's quantiser is discontinuous in its input: the GPU quantises the bf16 FC2 input it
+The int8 quantisers are discontinuous in their input: the GPU quantises the bf16 operand it
 stores, the oracle its float64 one, and bf16 rounding moves h / s by up to ~127 * 2^-9 ~ 0.25 of
 a step, so a share of the codes differ by one step.  Over 50 blocks that leaves the velocities
-2.7-3.0e-2 apart -- as far as the oracle's own int8 loop is from its bf16 loop (2.4-2.6e-2) --
-so there the per-evaluation velocity takes the loop's 5e-2 bar.  The int8 arithmetic itself is
-checked bit for bit on identical inputs and per block at 2e-2 elsewhere.
+2.7-3.0e-2 from the oracle's with the per-row int8 FC2, 2.4-2.7e-2 with the grouped one and
+3.9-4.2e-2 with int8 QKV, FC1 and FC2 -- the same order as the oracle's own int8 loops are
+from its bf16 loop (2.4-2.6e-2, 2.2-2.3e-2 and 3.5-3.7e-2) -- so there the per-evaluation
+velocity takes the loop's 5e-2 bar.  The int8 arithmetic itself is checked bit for bit on
+identical inputs and per block at 2e-2 elsewhere.
 """
 import numpy as np
 import pytest
@@ -34,15 +39,16 @@ from video_diffusion_transformer_fwd_amd.runtime import DiTModel
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ("512sq_22f", "512sq_22f_int8", "512sq_22f_tr")
-VELOCITY_BAR = {"512sq_22f": 2e-2, "512sq_22f_int8": 5e-2, "512sq_22f_tr": 2e-2}
+NAMES = ("512sq_22f", "512sq_22f_int8", "512sq_22f_int8g", "512sq_22f_int8_all", "512sq_22f_tr")
+VELOCITY_BAR = {"512sq_22f": 2e-2, "512sq_22f_int8": 5e-2, "512sq_22f_int8g": 5e-2,
+                "512sq_22f_int8_all": 5e-2, "512sq_22f_tr": 2e-2}
 
 
 @pytest.fixture(scope="module")
 def model():
-    # one resident model serves the three loops: they share the shape, the seed and so every
-    # weight; the int8 FC2 copies are made once
-    m = DiTModel(S.WORKLOADS["512sq_22f"], with_int8=True)
+    # one resident model serves every loop: they share the shape, the seed and so every
+    # weight; the int8 copies of FC2, QKV and FC1 are made once
+    m = DiTModel(S.WORKLOADS["512sq_22f"], with_int8=True, with_int8_linear=True)
     yield m
     m.close()
 
@@ -82,7 +88,8 @@ def test_full_depth_loop(model, oracle_globals, name):
     assert (model.geo.f_lat, model.geo.grid_h, model.geo.grid_w, model.geo.n_tokens) == \
         (geo["f_lat"], geo["grid_h"], geo["grid_w"], geo["n"])
     assert model.active(w.n_active) == active
-    opts = model.opts(fc2_mode=w.fc2_mode, token_reduction=w.token_reduction)
+    opts = model.opts(fc2_mode=w.fc2_mode, token_reduction=w.token_reduction,
+                      int8_linear=w.int8_linear)
     lat0, x, vel = run_loop(model, w, active, opts)
     assert len(vel) == len(vel_ref)
     assert np.isfinite(x).all()

@@ -95,6 +95,9 @@ WORKLOADS = {
     # same shape, 50 blocks, per-row int8 FC2
     "512sq_22f_int8": Workload("512sq_22f_int8", 512, 512, 22, 3072, 24, 12288, 256, 50,
                                steps=4, fc2_mode="row"),
+    # same shape, 50 blocks, int8 FC2 with one activation scale per 1024-channel group
+    "512sq_22f_int8g": Workload("512sq_22f_int8g", 512, 512, 22, 3072, 24, 12288, 256, 50,
+                                steps=4, fc2_mode="grouped"),
     # same shape with the whole int8 path: int8 QKV and FC1 (quantisation fused into the gated
     # AdaLN) and the per-row int8 FC2
     "512sq_22f_int8_all": Workload("512sq_22f_int8_all", 512, 512, 22, 3072, 24, 12288, 256, 50,
