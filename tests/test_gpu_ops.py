@@ -34,9 +34,11 @@ def sync():
     (1000, 700, 256, 1, 0, 1),      # 192x192 tiles with ragged M and N
     (4100, 2304, 256, 0, 0, 0),     # 256x256 tiles, ragged M
     (4100, 2100, 128, 1, 0, 0),     # 256x256 tiles, ragged M and N, GELU
-    (1601, 8300, 256, 1, 0, 1),     # 384x192 tiles, ragged M and N, GELU, two biases
-    (1536, 8192, 64, 1, 0, 0),      # 384x192 tiles, one K slice (its held last step only)
-    (1700, 8448, 192, 0, 1, 0),     # 384x192 tiles, odd slice count, float32 out
+    (1500, 12200, 256, 1, 0, 1),    # 384x192 tiles, ragged M and N, GELU, two biases
+    (1536, 12288, 64, 1, 0, 0),     # 384x192 tiles, one K slice (its held last step only)
+    (1536, 12288, 192, 0, 1, 0),    # 384x192 tiles, odd slice count, float32 out
+    (1260, 12288, 512, 1, 0, 0),    # wide product on 256x256 tiles (one wave of them)
+    (1601, 8300, 256, 1, 0, 1),     # wide product on 256x256 tiles, ragged M and N
     (4100, 2048, 64, 0, 0, 0),      # 256x256 tiles, one K slice
     (900, 640, 320, 1, 0, 0),       # 192x192 tiles (three stages), five slices
 ])

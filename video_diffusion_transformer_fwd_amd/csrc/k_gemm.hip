@@ -674,10 +674,29 @@ void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
 
 }  // namespace
 
+// The wide products (QKV, FC1: N >= 8192) take whichever of the 384x192, 256x256 and 192x192
+// tiles needs the least time by a simple model: waves of tiles over the 256 CUs (a partly
+// filled last wave costs a whole one) times the outputs per tile, 192x192 tiles weighted
+// 1.15 for their lower per-output rate.  Measured (FC1-shaped, K = 3072): at 1536 rows the
+// 384x192 tiles make exactly one wave (110 us; 256x256 165 us); at 2430 rows (864x480) the
+// 384-row tiles leave a last row block a third full and 1.75 waves, 256x256 tiles 1.88 waves
+// of smaller tiles (183-200 against 209-220 us); at 1260 rows (864x480 paired) 256x256 tiles
+// make one wave (94 us against 110 for 384x192 and 126 for 192x192); at 768 rows 192x192
+// (70 us); at 61,488 rows the model ties and 384x192 is 2% faster.
+int wide_tile_cfg(int M, int N) {
+  auto cost = [&](int bm, int bn, double w) {
+    const int64_t tiles = static_cast<int64_t>((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+    return static_cast<double>((tiles + 255) / 256) * bm * bn * w;
+  };
+  const double c4 = cost(384, 192, 1.0), c2 = cost(256, 256, 1.0), c1 = cost(192, 192, 1.15);
+  // ties (within 2%) go to 384x192, then to 256x256
+  if (c4 <= 1.02 * c2 && c4 <= 1.02 * c1) return 4;
+  return c2 <= c1 ? 2 : 1;
+}
+
 // Tile choice measured on the MI355X with random bf16 operands:
-//   N >= 8192, M >= 1536            384x192, 8 waves                 (QKV, FC1)
+//   N >= 8192, M >= 192             wide_tile_cfg above               (QKV, FC1)
 //   M >= 4096, N >= 2048            256x256, 8 waves                 (narrow products, 768x1344)
-//   N >= 8192, M >= 192             192x192                          (QKV, FC1 at 768 tokens)
 //   1024 <= M < 4096, N < 8192      192x192, K split in 2            (out-proj, FC2 at 1536)
 //   192 <= M < 1024, N < 8192       192x192, K split in 4            (out-proj, FC2 at 768)
 //   otherwise                       128x128
@@ -686,12 +705,10 @@ GemmPlan plan_gemm(int M, int N, int K) {
   GemmPlan p{};
   p.cfg = 0;
   p.split = 1;
-  if (N >= 8192 && M >= 1536) {
-    p.cfg = 4;
+  if (N >= 8192 && M >= 192) {
+    p.cfg = wide_tile_cfg(M, N);
   } else if (M >= 4096 && N >= 2048) {
     p.cfg = 2;
-  } else if (N >= 8192 && M >= 192) {
-    p.cfg = 1;
   } else if (M >= 1024 && N >= 256) {
     p.cfg = 1;
     p.split = 2;
