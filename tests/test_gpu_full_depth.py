@@ -7,7 +7,9 @@ shape (1536 tokens, d = 3072, 50 blocks):
                     channels);
   * 512sq_22f_int8_all  the same loop with int8 QKV and FC1 as well (P3 "the int8 path");
   * 512sq_22f_tr    --steps 20 --layers 45 --reuse 2 with token pairing (P2 §4, P3
-                    "aggressive levers"): 11 fresh evaluations, 1536 -> 768 tokens.
+                    "aggressive levers"): 11 fresh evaluations, 1536 -> 768 tokens;
+and at the 864x480x22-frame shape (15 x 27 token grid, 2430 tokens), --steps 4 --reuse 1:
+  * 864x480_22f     all 50 blocks, bf16 FC2.
 
 The oracle's loops are stored by ``tests/golden/make_full_depth.py`` (float64 oracle on the same
 seeded model; minutes of CPU per loop).  Bars: the latent after the loop and the part the loop
@@ -39,23 +41,41 @@ from video_diffusion_transformer_fwd_amd.runtime import DiTModel
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ("512sq_22f", "512sq_22f_int8", "512sq_22f_int8g", "512sq_22f_int8_all", "512sq_22f_tr")
+NAMES = ("512sq_22f", "512sq_22f_int8", "512sq_22f_int8g", "512sq_22f_int8_all", "512sq_22f_tr",
+         "864x480_22f")
 VELOCITY_BAR = {"512sq_22f": 2e-2, "512sq_22f_int8": 5e-2, "512sq_22f_int8g": 5e-2,
-                "512sq_22f_int8_all": 5e-2, "512sq_22f_tr": 2e-2}
+                "512sq_22f_int8_all": 5e-2, "512sq_22f_tr": 2e-2, "864x480_22f": 2e-2}
+# the workload whose shape and weights each loop runs on (one resident model per shape)
+SHAPE_OF = {n: ("864x480_22f" if n.startswith("864x480") else "512sq_22f") for n in NAMES}
 
 
 @pytest.fixture(scope="module")
-def model():
-    # one resident model serves every loop: they share the shape, the seed and so every
-    # weight; the int8 copies of FC2, QKV and FC1 are made once
-    m = DiTModel(S.WORKLOADS["512sq_22f"], with_int8=True, with_int8_linear=True)
-    yield m
-    m.close()
+def models():
+    # one resident model per shape serves every loop of that shape: they share the seed and so
+    # every weight; the int8 copies of FC2, QKV and FC1 are made once
+    made = {}
+
+    def get(shape):
+        if shape not in made:
+            int8 = shape == "512sq_22f"
+            made[shape] = DiTModel(S.WORKLOADS[shape], with_int8=int8, with_int8_linear=int8)
+        return made[shape]
+
+    yield get
+    for m in made.values():
+        m.close()
 
 
 @pytest.fixture(scope="module")
 def oracle_globals():
-    return oracle_model(S.WORKLOADS["512sq_22f"], blocks=[])
+    made = {}
+
+    def get(shape):
+        if shape not in made:
+            made[shape] = oracle_model(S.WORKLOADS[shape], blocks=[])
+        return made[shape]
+
+    return get
 
 
 def run_loop(model, w, active, opts):
@@ -76,14 +96,15 @@ def run_loop(model, w, active, opts):
 
 
 @pytest.mark.parametrize("name", NAMES)
-def test_full_depth_loop(model, oracle_globals, name):
+def test_full_depth_loop(models, oracle_globals, name):
     rec = golden.load(name)
     if rec is None:
         pytest.fail(f"tests/golden/full_depth_{name}.npz is missing: run tests/golden/make_full_depth.py")
     vel_ref, x_ref, meta = rec
     w = S.WORKLOADS[name]
+    model, og = models(SHAPE_OF[name]), oracle_globals(SHAPE_OF[name])
     geo = oracle_geom(w)
-    active = oracle_active(w, oracle_globals)
+    active = oracle_active(w, og)
     assert meta["active"] == active and meta["n_fresh"] == len(vel_ref)
     assert (model.geo.f_lat, model.geo.grid_h, model.geo.grid_w, model.geo.n_tokens) == \
         (geo["f_lat"], geo["grid_h"], geo["grid_w"], geo["n"])
@@ -104,7 +125,7 @@ def test_full_depth_loop(model, oracle_globals, name):
     # outside the GPU's error
     lat_o = oracle_latent(w)
     assert np.array_equal(lat_o, lat0)
-    x0_ref, _ = dit.denoise(lat_o, oracle_globals, w.steps, w.reuse, [], geo, w.n_heads)
+    x0_ref, _ = dit.denoise(lat_o, og, w.steps, w.reuse, [], geo, w.n_heads)
     d_lat, d_delta = rel_l2(x0_ref, x_ref), rel_l2(x0_ref - lat0, x_ref - lat0)
     print(f"{name}: no-block loop vs oracle: latent {d_lat:.2e}, x_N - x_0 {d_delta:.2e}")
     assert d_lat >= 5 * e_lat and d_delta >= 5 * e_delta, (d_lat, e_lat, d_delta, e_delta)
