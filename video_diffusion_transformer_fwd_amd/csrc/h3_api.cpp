@@ -308,9 +308,22 @@ int32_t run_block(const h3_model *m, int32_t b, const h3_geom &geom, int32_t row
       launch_quant_rows(h, hq, hs, rows, F, group, s);
     }
     ProfScope ps(H3_ST_FC2_I8_GEMM, s);
-    launch_gemm_i8(hq, hs, reinterpret_cast<const int8_t *>(w.fc2_q),
-                   reinterpret_cast<const float *>(w.fc2_s),
-                   reinterpret_cast<const bf16_t *>(w.fc2_b), mo, d, rows, d, F, group, s, sk);
+    // row mode with K split: the int32 partials go to the gate kernel, which sums and
+    // dequantises them exactly as the int8 split-K reduction would
+    if (o.fc2_mode == H3_FC2_INT8_ROW && d <= 4096) {
+      mp.S = launch_gemm_i8_partials(hq, hs, reinterpret_cast<const int8_t *>(w.fc2_q),
+                                     reinterpret_cast<const float *>(w.fc2_s), rows, d, F, s, sk);
+      if (mp.S) {
+        mp.part = nullptr;
+        mp.ipart = reinterpret_cast<const int32_t *>(sk.part);
+        mp.sa = hs;
+        mp.sw = reinterpret_cast<const float *>(w.fc2_s);
+      }
+    }
+    if (!mp.S)
+      launch_gemm_i8(hq, hs, reinterpret_cast<const int8_t *>(w.fc2_q),
+                     reinterpret_cast<const float *>(w.fc2_s),
+                     reinterpret_cast<const bf16_t *>(w.fc2_b), mo, d, rows, d, F, group, s, sk);
   }
   // x <- x + g2 m ; optionally n1_next = AdaLN(x; next shift, scale)
   {

@@ -312,6 +312,11 @@ GemmPlan plan_gemm_i8(int M, int N, int K, int group);
 // launched then).
 int launch_gemm_bf16_partials(const bf16_t *A, int64_t lda, const bf16_t *B, int64_t ldb, int M,
                               int N, int K, hipStream_t s, const SplitScratch &scratch);
+// The same for a row-mode int8 product: its int32 partials [S][M][N] stay in the scratch for
+// the gate kernel (GateY with ipart, sa, sw), which sums and dequantises them as the int8
+// split-K reduction would.  Returns S, or 0 (nothing launched).
+int launch_gemm_i8_partials(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
+                            int M, int N, int K, hipStream_t s, const SplitScratch &scratch);
 void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
                     const bf16_t *bias, bf16_t *C, int64_t ldc, int M, int N, int K, int group,
                     hipStream_t s, const SplitScratch &scratch = SplitScratch(),
@@ -369,6 +374,11 @@ struct GateY {
   int64_t stride;
   const bf16_t *b1, *b2;
   bf16_t *y_out;
+  // int8 FC2 (row mode): the partials are int32 (ipart instead of part) and y is dequantised
+  // with the activation scale sa [rows] and the weight scale sw [d], as the int8 split-K
+  // reduction does
+  const int32_t *ipart = nullptr;
+  const float *sa = nullptr, *sw = nullptr;
 };
 void launch_gate_adaln_part(const bf16_t *x, const GateY &ysrc, const float *gate, bf16_t *x_out,
                             const float *shift, const float *scale, bf16_t *n_out, int rows, int d,

@@ -463,13 +463,14 @@ __global__ __launch_bounds__(256) void splitk_i8_reduce_kernel(const int32_t *__
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT, int EPI, int QKD = 0>
+template <int BM, int BN, int WM, int WN, int NS, bool GROUPED, int SPLIT, int EPI, int QKD = 0,
+          bool REDUCE = true>
 void run_gemm_i8(const GemmI8Args &a, hipStream_t s) {
   using Cfg = GemmI8Cfg<BM, BN, WM, WN, NS>;
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   auto kern = gemm_i8_kernel<BM, BN, WM, WN, NS, GROUPED, SPLIT, EPI, QKD>;
   kern<<<tiles * SPLIT, Cfg::NT, 0, s>>>(a);
-  if constexpr (SPLIT > 1) {
+  if constexpr (SPLIT > 1 && REDUCE) {
     const int64_t total4 = static_cast<int64_t>(a.M) * a.N / 4;
     splitk_i8_reduce_kernel<SPLIT, EPI><<<static_cast<int>((total4 + 255) / 256), 256, 0, s>>>(
         a.part, a.M, a.N, a.SA, a.SW, a.bias, a.C, a.ldc);
@@ -548,6 +549,18 @@ void launch_gemm_i8(const int8_t *QA, const float *SA, const int8_t *QW, const f
     dispatch_i8<H3_EPI_GELU>(p, a, group != K, s);
   else
     dispatch_i8<H3_EPI_NONE>(p, a, group != K, s);
+}
+
+int launch_gemm_i8_partials(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,
+                            int M, int N, int K, hipStream_t s, const SplitScratch &sc) {
+  const GemmPlan p = plan_gemm_i8(M, N, K, K);
+  if (p.split <= 1 || !sc.part || p.part_bytes > sc.part_bytes) return 0;
+  GemmI8Args a{QA, SA, QW, SW, nullptr, nullptr, 0, M, N, K, K, reinterpret_cast<int32_t *>(sc.part)};
+  switch (p.cfg * 8 + p.split) {
+    case 4 * 8 + 4: run_gemm_i8<384, 192, 4, 2, 2, false, 4, H3_EPI_NONE, 0, false>(a, s); return 4;
+    case 1 * 8 + 4: run_gemm_i8<192, 192, 2, 2, 3, false, 4, H3_EPI_NONE, 0, false>(a, s); return 4;
+    default: return 0;
+  }
 }
 
 int launch_gemm_i8_qkv(const int8_t *QA, const float *SA, const int8_t *QW, const float *SW,

@@ -79,6 +79,9 @@ __device__ __forceinline__ float quant_rcp(float s) { return s > 0.f ? __builtin
 // partials summed in piece order plus the bias sum, rounded to bf16 -- the reduction kernel's
 // arithmetic -- and optionally stored to ysrc.y_out.  An absent second bias adds +0, which
 // leaves every sum's bits unchanged, so the bias loads need no branch.
+// YI8 (with YS): the partials are the int32 sums of the row-mode int8 FC2 (ysrc.ipart), added
+// in piece order and dequantised as the int8 split-K reduction does:
+// y = bf16((float(sum) * sa[row]) * sw[col] + b1[col]), without contraction.
 // All loads of a chunk are issued before its values are used (no branches, no runtime loops),
 // and the AdaLN shift / scale are loaded before the row reductions.
 // WPR waves per row: 1 (four rows per 256-thread block) or 2 (one row per 128-thread block,
@@ -105,7 +108,7 @@ __device__ __forceinline__ float row_max(float v, float *red, int t) {
   return v;
 }
 
-template <int VPL, int WPR, bool GATE, bool NORM, bool QUANT, int YS>
+template <int VPL, int WPR, bool GATE, bool NORM, bool QUANT, int YS, bool YI8 = false>
 __global__ __launch_bounds__(256) void gate_adaln_kernel(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ y, GateY ysrc,
     const float *__restrict__ gate, bf16_t *x_out, const float *__restrict__ shift,
@@ -131,7 +134,33 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
     unpack8(xv, v[i]);
     if constexpr (GATE) {
       float yv[8], gv[8];
-      if constexpr (YS > 0) {
+      if constexpr (YS > 0 && YI8) {
+        int32_t t[8];
+        float sw[8], b1[8];
+        {
+          const int4 *pp = reinterpret_cast<const int4 *>(ysrc.ipart + base + e);
+          const int4 p0 = pp[0], p1 = pp[1];
+          t[0] = p0.x; t[1] = p0.y; t[2] = p0.z; t[3] = p0.w;
+          t[4] = p1.x; t[5] = p1.y; t[6] = p1.z; t[7] = p1.w;
+        }
+#pragma unroll
+        for (int q = 1; q < YS; ++q) {
+          const int4 *pp = reinterpret_cast<const int4 *>(ysrc.ipart + q * ysrc.stride + base + e);
+          const int4 p0 = pp[0], p1 = pp[1];
+          t[0] += p0.x; t[1] += p0.y; t[2] += p0.z; t[3] += p0.w;
+          t[4] += p1.x; t[5] += p1.y; t[6] += p1.z; t[7] += p1.w;
+        }
+        load8f(ysrc.sw + e, sw);
+        unpack8(*reinterpret_cast<const uint4 *>(ysrc.b1 + e), b1);
+        const float sa = ysrc.sa[row];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float v = static_cast<float>(t[k]) * sa;
+          const float w = v * sw[k];
+          yv[k] = bf2f(f2bf(w + b1[k]));
+          yk[i][k] = yv[k];
+        }
+      } else if constexpr (YS > 0) {
         float t[8], u[8], b1[8], b2[8];
         load8f(ysrc.part + base + e, t);
         unpack8(*reinterpret_cast<const uint4 *>(ysrc.b1 + e), b1);
@@ -236,7 +265,7 @@ __global__ __launch_bounds__(256) void gate_adaln_kernel(
   }
 }
 
-template <bool GATE, bool NORM, bool QUANT, int YS = 0>
+template <bool GATE, bool NORM, bool QUANT, int YS = 0, bool YI8 = false>
 void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf16_t *x_out,
                          const float *shift, const float *scale, bf16_t *n_out, int8_t *q_out,
                          float *s_out, int rows, int d, hipStream_t s, const GateY &ysrc = GateY{}) {
@@ -249,7 +278,7 @@ void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf
     switch (v512) {
 #define H3_CASE1(V)                                                                         \
   case V:                                                                                   \
-    gate_adaln_kernel<V, 1, GATE, NORM, QUANT, YS><<<grid1, block1, 0, s>>>(                \
+    gate_adaln_kernel<V, 1, GATE, NORM, QUANT, YS, YI8><<<grid1, block1, 0, s>>>(           \
         x, y, ysrc, gate, x_out, shift, scale, n_out, q_out, s_out, rows, d);               \
     break;
       H3_CASE1(1) H3_CASE1(2) H3_CASE1(3) H3_CASE1(4) H3_CASE1(5) H3_CASE1(6) H3_CASE1(8)
@@ -262,7 +291,7 @@ void dispatch_gate_adaln(const bf16_t *x, const bf16_t *y, const float *gate, bf
   switch (v512) {
 #define H3_CASE2(V)                                                                         \
   case 2 * V:                                                                               \
-    gate_adaln_kernel<V, 2, GATE, NORM, QUANT, YS><<<grid2, block2, 0, s>>>(                \
+    gate_adaln_kernel<V, 2, GATE, NORM, QUANT, YS, YI8><<<grid2, block2, 0, s>>>(           \
         x, y, ysrc, gate, x_out, shift, scale, n_out, q_out, s_out, rows, d);               \
     break;
     H3_CASE2(1) H3_CASE2(2) H3_CASE2(3) H3_CASE2(4) H3_CASE2(5) H3_CASE2(6) H3_CASE2(8)
@@ -616,22 +645,26 @@ void launch_gate_adaln_part(const bf16_t *x, const GateY &ysrc, const float *gat
                             const float *shift, const float *scale, bf16_t *n_out, int rows, int d,
                             hipStream_t s, int8_t *q_out, float *s_out) {
   if (rows <= 0) return;
-  const auto go = [&](auto ys) {
+  const auto go = [&](auto ys, auto yi8) {
     constexpr int YS = decltype(ys)::value;
+    constexpr bool YI8 = decltype(yi8)::value;
     if (q_out)
-      dispatch_gate_adaln<true, true, true, YS>(x, nullptr, gate, x_out, shift, scale, nullptr,
-                                                q_out, s_out, rows, d, s, ysrc);
+      dispatch_gate_adaln<true, true, true, YS, YI8>(x, nullptr, gate, x_out, shift, scale, nullptr,
+                                                     q_out, s_out, rows, d, s, ysrc);
     else if (n_out)
-      dispatch_gate_adaln<true, true, false, YS>(x, nullptr, gate, x_out, shift, scale, n_out,
-                                                 nullptr, nullptr, rows, d, s, ysrc);
+      dispatch_gate_adaln<true, true, false, YS, YI8>(x, nullptr, gate, x_out, shift, scale, n_out,
+                                                      nullptr, nullptr, rows, d, s, ysrc);
     else
-      dispatch_gate_adaln<true, false, false, YS>(x, nullptr, gate, x_out, shift, scale, nullptr,
-                                                  nullptr, nullptr, rows, d, s, ysrc);
+      dispatch_gate_adaln<true, false, false, YS, YI8>(x, nullptr, gate, x_out, shift, scale,
+                                                       nullptr, nullptr, nullptr, rows, d, s, ysrc);
   };
-  if (ysrc.S == 4)
-    go(std::integral_constant<int, 4>());
+  // the int8 FC2's partials are always four pieces (its row-mode plan splits K in 4)
+  if (ysrc.ipart)
+    go(std::integral_constant<int, 4>(), std::true_type());
+  else if (ysrc.S == 4)
+    go(std::integral_constant<int, 4>(), std::false_type());
   else
-    go(std::integral_constant<int, 2>());
+    go(std::integral_constant<int, 2>(), std::false_type());
 }
 
 void launch_rope_table(float2 *table, const h3_geom &geom, int n_tokens, int head_dim,
