@@ -7,6 +7,7 @@
 // are K-contiguous, so A and B tiles are staged identically, straight from global memory into
 // LDS (global_load_lds_dwordx4: 8 consecutive lanes cover one 128-byte row slice), NS slices
 // in flight; a slice is consumed once its loads have landed (explicit vmcnt wait + barrier).
+// The MFMAs of each slice's last K step are held across that barrier (XBO below).
 //
 // LDS rows are 64 bf16 = 128 bytes = 8 chunks of 16 bytes, stored without padding: chunk c of
 // row r sits at slot c ^ ((r >> 1) & 7).  The MFMA-operand reads (16 bytes per lane, 32 rows at
@@ -19,8 +20,9 @@
 // 8(i/4) + 4(l/32) + 0..3: the epilogue writes 8-byte (bf16) or 16-byte (float32) vectors.
 //
 // Tile shapes are chosen per problem by plan_gemm (measured on random bf16 operands): 384x192
-// tiles (8 waves of 96x96, two per SIMD, two LDS stages) for the wide QKV / FC1 products,
-// 256x256 tiles with 8 waves of 128x64 for the narrow products at large M, and 192x192 tiles
+// tiles (8 waves of 96x96, two per SIMD, two LDS stages), 256x256 or 192x192 tiles for the wide
+// QKV / FC1 products by a wave-count model, 256x256 tiles with 8 waves of 128x64 for the narrow
+// products at large M, and 192x192 tiles
 // (three LDS stages) with K split in two for the narrow (N = d) products of the 1536-token
 // workload and in four at 768 tokens, run by 8 waves in two K-step groups (KSG below).
 //
