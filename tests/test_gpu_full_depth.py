@@ -8,8 +8,10 @@ shape (1536 tokens, d = 3072, 50 blocks):
   * 512sq_22f_int8_all  the same loop with int8 QKV and FC1 as well (P3 "the int8 path");
   * 512sq_22f_tr    --steps 20 --layers 45 --reuse 2 with token pairing (P2 §4, P3
                     "aggressive levers"): 11 fresh evaluations, 1536 -> 768 tokens;
-and at the 864x480x22-frame shape (15 x 27 token grid, 2430 tokens), --steps 4 --reuse 1:
-  * 864x480_22f     all 50 blocks, bf16 FC2.
+and at the 864x480x22-frame shape (15 x 27 token grid, 2430 tokens):
+  * 864x480_22f     --steps 4 --reuse 1, all 50 blocks, bf16 FC2;
+  * 864x480_22f_tr  --steps 20 --layers 45 --reuse 2 with token pairing along the odd width
+                    (2430 -> 1260 tokens, the 27th column alone).
 
 The oracle's loops are stored by ``tests/golden/make_full_depth.py`` (float64 oracle on the same
 seeded model; minutes of CPU per loop).  Bars: the latent after the loop and the part the loop
@@ -42,9 +44,10 @@ from video_diffusion_transformer_fwd_amd.runtime import DiTModel
 pytestmark = pytest.mark.gpu
 
 NAMES = ("512sq_22f", "512sq_22f_int8", "512sq_22f_int8g", "512sq_22f_int8_all", "512sq_22f_tr",
-         "864x480_22f")
+         "864x480_22f", "864x480_22f_tr")
 VELOCITY_BAR = {"512sq_22f": 2e-2, "512sq_22f_int8": 5e-2, "512sq_22f_int8g": 5e-2,
-                "512sq_22f_int8_all": 5e-2, "512sq_22f_tr": 2e-2, "864x480_22f": 2e-2}
+                "512sq_22f_int8_all": 5e-2, "512sq_22f_tr": 2e-2, "864x480_22f": 2e-2,
+                "864x480_22f_tr": 2e-2}
 # the workload whose shape and weights each loop runs on (one resident model per shape)
 SHAPE_OF = {n: ("864x480_22f" if n.startswith("864x480") else "512sq_22f") for n in NAMES}
 
