@@ -84,9 +84,11 @@ def test_gemm_strided_operands():
     (1536, 256, 2, 128),   # cross-attention length
     (5, 1, 1, 64),         # one key: output is that value
     (64, 600, 2, 64),      # keys span several tiles with a ragged tail
-    # more than 256 (query tile, head) pairs: four-wave workgroups; the cases above (fewer)
-    # take the eight-wave workgroups that split the key tiles between two wave groups
+    # more than 256 (128-query tile, head) pairs: eight-wave workgroups of 256 queries while
+    # their grid takes at most 192 CUs, else four-wave workgroups; the cases above (fewer
+    # pairs) take the eight-wave workgroups that split the key tiles between two wave groups
     (1040, 300, 32, 128),
+    (1040, 300, 48, 128),
     (700, 100, 48, 64),
 ])
 def test_attention(nq, nk, H, D):
@@ -159,8 +161,9 @@ def planted_scores(nq, nk, H, D, tiles, seed):
     (600, 700, 2, 128, (4,)),      # ... in the first group's tile
     (600, 700, 2, 128, (2, 6)),    # two jumps, one in each group
     (600, 256, 2, 128, (3,)),      # cross-attention length, two key groups
-    (1040, 700, 32, 128, (5,)),    # four-wave workgroups
-    (1040, 256, 32, 128, (1, 3)),  # four-wave, cross-attention length, two jumps
+    (1040, 700, 48, 128, (5,)),    # four-wave workgroups
+    (1040, 256, 48, 128, (1, 3)),  # four-wave, cross-attention length, two jumps
+    (1040, 700, 32, 128, (2, 6)),  # eight-wave workgroups of 256 queries below 8192 queries
     (600, 600, 2, 64, (5,)),       # head dim 64, two key groups
     (600, 600, 2, 64, (4,)),
     (700, 600, 48, 64, (2, 5)),    # head dim 64, four-wave workgroups

@@ -433,16 +433,21 @@ void launch_cfg(const AttnProblems &pr, int n_problems, int heads, float scale_l
   attention_kernel<D, WAVES, KG><<<grid, block, 0, s>>>(pr, scale_log2);
 }
 
-// 8192+ queries: 8-wave workgroups of 256 queries.  Fewer: 128 queries per workgroup, with 4
-// waves (two workgroups per CU) when the (query tile, head) grid of the longest problem covers
-// the 256 CUs, else with 8 waves in two key groups (two waves per SIMD on each occupied CU,
-// every wave half the key tiles).
+// 8192+ queries: 8-wave workgroups of 256 queries.  Fewer: 128 queries per workgroup, with 8
+// waves in two key groups when the (128-query tile, head) grid of the longest problem leaves
+// CUs idle (at most 256 workgroups: two waves per SIMD on each occupied CU, every wave half the
+// key tiles); otherwise 8-wave workgroups of 256 queries again when their grid takes at most
+// three quarters of the CUs, leaving the rest to the short cross-attention of the same launch
+// (1536 tokens, 24 heads: 144 workgroups; -0.8% per 512x512x22f step against the next form),
+// else 4 waves (two workgroups per CU; 2430 tokens: 240 workgroups of 256 queries would take
+// a second round with the cross-attention's, +0.6% per step).
 void launch_problems(const AttnProblems &pr, int n_problems, int heads, int head_dim, hipStream_t s) {
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
   int nq = 0;
   for (int i = 0; i < n_problems; ++i) nq = std::max(nq, pr.p[i].nq);
   const bool sparse = static_cast<int64_t>((nq + 127) / 128) * heads <= 256;
-  if (head_dim == 128 && nq >= 8192)
+  const bool wide8 = static_cast<int64_t>((nq + 255) / 256) * heads <= 192;
+  if (head_dim == 128 && (nq >= 8192 || (!sparse && wide8)))
     launch_cfg<128, 8, 1>(pr, n_problems, heads, scale_log2, s);
   else if (head_dim == 128)
     sparse ? launch_cfg<128, 8, 2>(pr, n_problems, heads, scale_log2, s)
