@@ -171,7 +171,7 @@ template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int SPLI
 __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(QKD == 0 || (EPI == H3_EPI_NONE && !OUT_F32 && SPLIT == 1), "QKV epilogue form");
   static_assert(ALN == 0 || (QKD == 0 && KSG == 1 && SPLIT == 1 && NS == 3), "AdaLN A operand form");
-  static_assert(KSG == 1 || (KSG == 2 && SPLIT > 1), "two K-step groups: split-K partial tiles only");
+  static_assert(KSG == 1 || KSG == 2, "one or two K-step groups");
   static_assert(XBO == 1 || XBO == 2, "cross-barrier order");
   using Cfg = GemmCfg<BM, BN, WM, WN, NS>;
   constexpr int NT = Cfg::NT * KSG, BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN;
@@ -455,7 +455,20 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
           for (int r = 0; r < 16; ++r) xw[((i * TN + j) * 16 + r) * 64 + lane] = acc[i][j][r];
     }
     __syncthreads();
-    if (kg == 1) return;  // no barrier follows; the first group adds them as it stores
+    if constexpr (SPLIT > 1) {
+      if (kg == 1) return;  // no barrier follows; the first group adds them as it stores
+    } else {
+      // the first group takes the sums; both groups then run the epilogue, whose opening
+      // barrier also orders these LDS reads before the band overwrites them
+      if (kg == 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = acc[i][j][r] + xch[((i * TN + j) * 16 + r) * 64 + lane];
+      }
+    }
   }
   if constexpr (SPLIT > 1) {
     // split-K: store this K piece's float32 partial tile, row-major [piece][M][N] (N % 4 == 0);
@@ -528,12 +541,14 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i > 0) __syncthreads();
+      if (KSG == 1 || kg == 0) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4 *>(band + (wm * 32 + m_l) * LD + (wn * TN + j) * 32 + q * 8 + n_l) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4 *>(band + (wm * 32 + m_l) * LD + (wn * TN + j) * 32 + q * 8 + n_l) =
+                make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
       __syncthreads();
       hp.run(i, [&](int row, int col, float *a) {
         const float4 *bp = reinterpret_cast<const float4 *>(band + row * LD + col);
@@ -563,12 +578,14 @@ __global__ __launch_bounds__(64 * WM * WN * KSG) void gemm_bf16_kernel(GemmArgs 
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (i > 0) __syncthreads();  // previous band fully read
+    if (KSG == 1 || kg == 0) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4 *>(band + (wm * 32 + m_l) * LD + (wn * TN + j) * 32 + q * 8 + n_l) =
-            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4 *>(band + (wm * 32 + m_l) * LD + (wn * TN + j) * 32 + q * 8 + n_l) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    }
     __syncthreads();
 #pragma unroll 2
     for (int c4 = tid; c4 < BAND_CHUNKS; c4 += NT) {
@@ -651,10 +668,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 }
 
 // One product: the tiled GEMM, then (split-K) the ordered reduction with the epilogue.
-// split-K products run with two K-step groups (two waves per SIMD)
-template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int S, int XBO = 1>
+// split-K products and the unsplit 192x192 tiles run with two K-step groups (two waves per
+// SIMD)
+template <int BM, int BN, int WM, int WN, int NS, int EPI, int OUT_F32, int S, int XBO = 1,
+          int KSG = (S > 1 ? 2 : 1)>
 void run_product(const GemmArgs &a, hipStream_t s) {
-  run_gemm<BM, BN, WM, WN, NS, EPI, OUT_F32, S, 0, (S > 1 ? 2 : 1), 0, XBO>(a, s);
+  run_gemm<BM, BN, WM, WN, NS, EPI, OUT_F32, S, 0, KSG, 0, XBO>(a, s);
   if constexpr (S > 1) {
     const int64_t total = static_cast<int64_t>(a.M) * a.N;
     splitk_reduce_kernel<EPI, OUT_F32, S><<<static_cast<int>((total / 4 + 255) / 256), 256, 0, s>>>(
@@ -667,7 +686,7 @@ void gemm_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
   switch (p.cfg * 8 + p.split) {
     case 4 * 8 + 1: run_product<384, 192, 4, 2, 2, EPI, OUT_F32, 1, 2>(a, s); break;
     case 2 * 8 + 1: run_product<256, 256, 2, 4, 2, EPI, OUT_F32, 1, 2>(a, s); break;
-    case 1 * 8 + 1: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
+    case 1 * 8 + 1: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 1, 1, 2>(a, s); break;
     case 1 * 8 + 2: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 2>(a, s); break;
     case 1 * 8 + 4: run_product<192, 192, 2, 2, 3, EPI, OUT_F32, 4>(a, s); break;
     default: run_product<128, 128, 2, 2, 3, EPI, OUT_F32, 1>(a, s); break;
@@ -756,7 +775,7 @@ void qkv_dispatch(const GemmPlan &p, const GemmArgs &a, hipStream_t s) {
   switch (p.cfg) {
     case 4: run_gemm<384, 192, 4, 2, 2, H3_EPI_NONE, 0, 1, QKD, 1, 0, 2>(a, s); break;
     case 2: run_gemm<256, 256, 2, 4, 2, H3_EPI_NONE, 0, 1, QKD, 1, 0, 2>(a, s); break;
-    case 1: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
+    case 1: run_gemm<192, 192, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD, 2>(a, s); break;
     default: run_gemm<128, 128, 2, 2, 3, H3_EPI_NONE, 0, 1, QKD>(a, s); break;
   }
 }
