@@ -41,6 +41,8 @@ def sync():
     (1601, 8300, 256, 1, 0, 1),     # wide product on 256x256 tiles, ragged M and N
     (4100, 2048, 64, 0, 0, 0),      # 256x256 tiles, one K slice
     (900, 640, 320, 1, 0, 0),       # 192x192 tiles (three stages), five slices
+    (300, 640, 64, 1, 0, 1),        # 192x192 tiles, two K-step groups over a single slice
+    (768, 12288, 3072, 1, 0, 0),    # FC1 at 768 rows: 192x192 tiles, two K-step groups
 ])
 def test_gemm_bf16(M, N, K, epi, f32, two_bias):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
