@@ -22,9 +22,9 @@
 // Tile shapes are chosen per problem by plan_gemm (measured on random bf16 operands): 384x192
 // tiles (8 waves of 96x96, two per SIMD, two LDS stages), 256x256 or 192x192 tiles for the wide
 // QKV / FC1 products by a wave-count model, 256x256 tiles with 8 waves of 128x64 for the narrow
-// products at large M, and 192x192 tiles
-// (three LDS stages) with K split in two for the narrow (N = d) products of the 1536-token
-// workload and in four at 768 tokens, run by 8 waves in two K-step groups (KSG below).
+// products at large M, and 192x192 tiles (three LDS stages) with K split in two for the narrow
+// (N = d) products of the 1536-token workload and in four at 768 tokens.  192x192 tiles, split or
+// not, are run by 8 waves in two K-step groups (KSG below).
 //
 // Split-K (S pieces of K per tile in separate workgroups): each piece stores its float32 partial
 // tile with plain stores; a second launch sums the S partials in piece order 0..S-1 and applies
@@ -155,10 +155,11 @@ __device__ __forceinline__ uint4 aln_chunk(const uint4 &xv, float mean, float rs
 
 // QKD > 0: the QKV product with heads of QKD channels; columns follow QkMap<BN, QKD> and the
 // epilogue applies the Q/K RMSNorm + RoPE to the q/k heads (bias, no GELU, bf16, unsplit).
-// KSG = 2 (split-K products only): twice the waves, in two groups over the same WM x WN layout;
-// each group takes half of the 16-wide K steps of every staged slice (two waves per SIMD where
-// one group alone has one), and the second group hands its accumulators to the first through
-// LDS before the partial tile is stored.
+// KSG = 2: twice the waves, in two groups over the same WM x WN layout; each group takes half of
+// the 16-wide K steps of every staged slice (two waves per SIMD where one group alone has one),
+// and the second group hands its accumulators to the first through LDS: with split K the first
+// adds them as it stores the partial tile, unsplit it adds them in registers and both groups run
+// the epilogue (only the first writes the LDS band).
 // XBO (the K loop without ALN): the MFMAs of every slice's last K step are issued after the
 // slice's barrier, from fragments already in registers, so the matrix cores stay busy while
 // the next slice's first fragments are read.  XBO = 1 issues them before the next slice's
