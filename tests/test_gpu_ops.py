@@ -187,6 +187,25 @@ def test_attention_softmax_rescale(nq, nk, H, D, tiles):
     assert_close(f64(O)[rows], ref.reshape(-1, H * D), rel=1e-2, elem=3e-2, what="rescaled attention")
 
 
+@pytest.mark.parametrize("nq,nk,D,h_a,h_b", [
+    (1040, 300, 128, 32, 48),   # 8-wave workgroups of 256 queries (32 heads) / 4-wave (48 heads)
+    (1536, 256, 128, 24, 48),   # the 512x512x22f cross-attention shape: 8-wave / 4-wave
+])
+def test_attention_workgroup_form_keeps_the_bits(nq, nk, D, h_a, h_b):
+    # which workgroup form runs (and the XCD order of its (tile, head) pairs) depends on the
+    # head count; a query's arithmetic does not (the forms with two key groups excepted: each
+    # group rounds its P to bf16 against its own softmax reference, so they are only checked
+    # against the oracle).  The first h_a heads are computed by both launches.
+    rng = np.random.default_rng(nq + nk + D)
+    Q, K, V = (randn_bf16(rng, (n, h_b * D)) for n in (nq, nk, nk))
+    Oa = torch.empty((nq, h_a * D), dtype=torch.bfloat16, device=DEV)
+    Ob = torch.empty((nq, h_b * D), dtype=torch.bfloat16, device=DEV)
+    B.h3_attention(Q[:, :h_a * D], K[:, :h_a * D], V[:, :h_a * D], Oa, nq, nk, h_a, D)
+    B.h3_attention(Q, K, V, Ob, nq, nk, h_b, D)
+    sync()
+    assert torch.equal(Oa.view(torch.int16), Ob[:, :h_a * D].contiguous().view(torch.int16))
+
+
 def test_attention_strided_views_of_qkvq():
     # the block's layout: q, k, v, qc as column slices of one [N, 4d] buffer, output into [N, 2d]
     rng = np.random.default_rng(11)
