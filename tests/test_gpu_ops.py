@@ -63,6 +63,26 @@ def test_gemm_bf16(M, N, K, epi, f32, two_bias):
         assert_close(f64(C), ref, rel=6e-3, elem=1.5e-2, what="gemm bf16")
 
 
+def test_gemm_tile_shape_keeps_the_bits():
+    # the tile shape follows M (1536 rows: 384x192, 1260: 256x256, 129: 128x128); every shape
+    # with one K-step group adds each output's K steps in the same order with the same MFMA and
+    # applies the same epilogue, so the rows they share have the same bits
+    rng = np.random.default_rng(77)
+    N, K = 12288, 512
+    A = randn_bf16(rng, (1536, K))
+    W = randn_bf16(rng, (N, K), 0.02)
+    b = randn_bf16(rng, (N,), 0.02)
+    outs = {}
+    for M in (1536, 1260, 129):
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        B.h3_gemm_bf16(A[:M], W, C, bias=b, epilogue=1)
+        outs[M] = C
+    sync()
+    i16 = lambda t: t.contiguous().view(torch.int16)
+    assert torch.equal(i16(outs[1536][:1260]), i16(outs[1260]))
+    assert torch.equal(i16(outs[1536][:129]), i16(outs[129]))
+
+
 def test_gemm_strided_operands():
     # operands that are column slices of wider rows (as the block's [O | Oc] and qkvq are)
     rng = np.random.default_rng(5)
